@@ -1,0 +1,123 @@
+"""Step-sequence drivers shared by the oracle pins and the GPU parity tests.
+
+A scenario owns the synthetic generator, the per-item total lengths and a
+per-position ``version`` table (a rejected draft position that is appended
+again gets a new version, hence new contents).  Backends hold their own
+cache buffers; the oracle backend's state never comes from the GPU.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import oracle
+import synth
+
+NAN16 = {synth.F16: 0x7E00, synth.BF16: 0x7FC0}
+
+
+@dataclasses.dataclass
+class Cfg:
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    C: int
+    W: int
+    dtype: int = synth.F32
+    scale: float = 0.0
+    softcap: float = 0.0
+    seed: int = 1
+    v_pos: bool = False
+    zero_q: bool = False
+
+    def synth(self) -> synth.Synth:
+        return synth.Synth(self.seed, self.Hq, self.Hkv, self.D, self.dtype,
+                           v_pos_in_elem0=self.v_pos, zero_query=self.zero_q)
+
+    def params(self, S: int, total: int, B: int | None = None):
+        return oracle.make_params(self.B if B is None else B, S, self.Hq,
+                                  self.Hkv, self.D, self.C, self.W, total,
+                                  self.dtype, self.scale, self.softcap)
+
+
+def nan_array(shape, dtype):
+    if dtype == synth.F32:
+        return np.full(shape, np.nan, dtype=np.float32)
+    return np.full(shape, NAN16[dtype], dtype=np.uint16)
+
+
+def as_f64(a, dtype):
+    return synth.from_storage(np.asarray(a), dtype)
+
+
+class Versions:
+    """version[b][pos]: how many times position pos of item b was re-drawn."""
+
+    def __init__(self, B: int, n: int = 1 << 16):
+        self.v = np.zeros((B, n), dtype=np.int64)
+
+    def of(self, b: int, pos):
+        return self.v[b, np.asarray(pos)]
+
+    def bump(self, b: int, pos):
+        self.v[b, np.asarray(pos)] += 1
+
+
+def layout_rows(cfg: Cfg, syn: synth.Synth, b: int, T: int, vers: Versions,
+                item_key: int | None = None):
+    """Rows the contract puts in [0, L(T)) of item b: (Hkv, L, D) K and V."""
+    L = oracle.resident_length(T, cfg.C, cfg.W)
+    pos = np.arange(T - L, T)
+    ver = vers.of(b, pos)[None, :]
+    heads = np.arange(cfg.Hkv)[:, None]
+    key = b if item_key is None else item_key
+    k = syn.kv_rows(synth.K, key, heads, pos[None, :], ver)
+    v = syn.kv_rows(synth.V, key, heads, pos[None, :], ver)
+    return L, k, v
+
+
+def seeded_cache(cfg: Cfg, syn: synth.Synth, Ts, vers: Versions):
+    """(B, Hkv, C, D) caches holding the contract layout for lengths Ts and
+    NaN in every unspecified row."""
+    shape = (len(Ts), cfg.Hkv, cfg.C, cfg.D)
+    K = nan_array(shape, cfg.dtype)
+    V = nan_array(shape, cfg.dtype)
+    for b, T in enumerate(Ts):
+        L, k, v = layout_rows(cfg, syn, b, int(T), vers)
+        K[b, :, :L] = k
+        V[b, :, :L] = v
+    return K, V
+
+
+def step_inputs(cfg: Cfg, syn: synth.Synth, P, S: int, vers: Versions):
+    P = np.asarray(P, dtype=np.int64)
+    ver = np.stack([vers.of(b, P[b] + np.arange(S)) for b in range(len(P))])
+    return syn.step_inputs(P, S, ver)
+
+
+class OracleBackend:
+    """Cache state advanced by the oracle alone (in place: present == past)."""
+
+    def __init__(self, cfg: Cfg, K=None, V=None, B: int | None = None):
+        B = cfg.B if B is None else B
+        shape = (B, cfg.Hkv, cfg.C, cfg.D)
+        self.cfg = cfg
+        self.K = nan_array(shape, cfg.dtype) if K is None else K.copy()
+        self.V = nan_array(shape, cfg.dtype) if V is None else V.copy()
+
+    def step(self, S, seqlens, q, k, v, bias=None, total=None, bias_bcast=(1, 1)):
+        seqlens = np.asarray(seqlens, dtype=np.int32)
+        total = int(seqlens.max()) + 1 if total is None else total
+        p = self.cfg.params(S, total, B=len(seqlens))
+        p.bias_dim0_is_batch, p.bias_dim1_is_heads = bias_bcast
+        st, out, plan = oracle.forward(p, q, k, v, self.K, self.V, seqlens, bias)
+        return st, out, plan
+
+    def snapshot(self):
+        return self.K.copy(), self.V.copy()
+
+    def restore(self, snap):
+        self.K[...] = snap[0]
+        self.V[...] = snap[1]

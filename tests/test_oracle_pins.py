@@ -1,0 +1,622 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test names the passage it pins (page title, section).  None of these
+re-types the oracle's own formula: they compare it with an independent
+recurrence, brute force, closed forms, printed values, or invariants.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.scenario import (Cfg, OracleBackend, Versions, as_f64, layout_rows,
+                            nan_array, step_inputs)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# P1. Resident length vs the one-token recurrence.
+# "Specify GroupQueryAttention windowed KV cache layout contract",
+# Description: L(T) closed form and min(T, W) <= L(T) <= min(T, C).
+# "[CPU] Add windowed kv cache for GQA", drifting layout: the append point
+# grows by one per token and a whole gap of G rows is reclaimed when the
+# buffer would overflow.
+def _recurrence(Tmax, C, W):
+    G = C - W + 1
+    out = np.zeros(Tmax + 1, dtype=np.int64)
+    l = 0
+    for t in range(1, Tmax + 1):
+        l += 1
+        if l > C:
+            l -= G
+        out[t] = l
+    return out
+
+
+def test_p1_resident_length_small_all_pairs():
+    Tmax = 10_000
+    T = np.arange(Tmax + 1)
+    for C in range(1, 65):
+        # vectorised recurrence over all W for this C
+        Ws = np.arange(1, C + 1)
+        G = C - Ws + 1
+        ref = np.zeros((Tmax + 1, C), dtype=np.int64)
+        l = np.zeros(C, dtype=np.int64)
+        for t in range(1, Tmax + 1):
+            l += 1
+            l = np.where(l > C, l - G, l)
+            ref[t] = l
+        for wi, W in enumerate(Ws):
+            got = oracle.resident_lengths(T, C, int(W))
+            assert np.array_equal(got, ref[:, wi]), (C, W)
+            assert np.all(got >= np.minimum(T, W)) and np.all(got <= np.minimum(T, C))
+
+
+@pytest.mark.parametrize("C,W", [(6, 4), (384, 128), (136, 128), (1032, 1024),
+                                 (1055, 1024), (4608, 4096), (128, 128)])
+def test_p1_resident_length_config_pairs(C, W):
+    Tmax = 40_000
+    T = np.arange(Tmax + 1)
+    got = oracle.resident_lengths(T, C, W)
+    assert np.array_equal(got, _recurrence(Tmax, C, W))
+    assert np.all(got >= np.minimum(T, W)) and np.all(got <= np.minimum(T, C))
+    assert np.all(np.diff(got) <= 1)
+    # second closed form for T > C: L = W + ((T - C - 1) mod G)
+    G = C - W + 1
+    big = T[T > C]
+    assert np.array_equal(got[T > C], W + ((big - C - 1) % G))
+
+
+def test_p1_int64_range():
+    # the planner works in int64 (PR #31142 review thread): no wrap near 2^31
+    T = np.array([2**31 - 1, 2**31 + 5, 2**40 + 3], dtype=np.int64)
+    C, W = 4608, 4096
+    G = C - W + 1
+    got = oracle.resident_lengths(T, C, W)
+    assert np.array_equal(got, W + ((T - C - 1) % G))
+
+
+# ---------------------------------------------------------------------------
+# Element conversions used for outputs: pinned against numpy's IEEE binary16
+# cast and against a brute-force nearest-even search for bf16.
+def test_conversions_fp16_against_numpy():
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([rng.normal(0, 1, 3000), rng.normal(0, 1e-5, 1000),
+                         rng.normal(0, 3e4, 1000), [0.0, -0.0, 65504.0, 65520.0,
+                                                     65519.99, 6e-8, 2.98e-8,
+                                                     2.99e-8, 1e-9]])
+    for x in xs:
+        with np.errstate(over="ignore"):
+            want = int(np.array([x], dtype=np.float64).astype(np.float16).view(np.uint16)[0])
+        assert oracle.encode(synth.F16, float(x)) == want, x
+        assert oracle.decode(synth.F16, want) == float(np.uint16(want).view(np.float16))
+
+
+def test_conversions_bf16_nearest_even():
+    rng = np.random.default_rng(8)
+    xs = np.concatenate([rng.normal(0, 1, 2000), rng.normal(0, 1e-38, 200),
+                         rng.normal(0, 1e30, 200)])
+    allbits = np.arange(1 << 16, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):
+        vals = (allbits << 16).view(np.float32).astype(np.float64)
+    finite = np.isfinite(vals)
+    for x in xs:
+        bits = oracle.encode(synth.BF16, float(x))
+        got = oracle.decode(synth.BF16, bits)
+        err = abs(got - x)
+        best = np.min(np.abs(vals[finite] - x))
+        assert err == best, x
+        if err != 0:  # ties go to the even significand
+            cands = allbits[finite][np.abs(vals[finite] - x) == best]
+            if len(cands) == 2:
+                assert bits % 2 == 0
+    assert oracle.encode(synth.BF16, 1.0 + 2**-8) == 0x3F80      # tie -> even
+    assert oracle.encode(synth.BF16, 1.0 + 3 * 2**-8) == 0x3F82  # tie -> even
+
+
+# ---------------------------------------------------------------------------
+# Brute force: a full-length cache that never evicts, with an explicit
+# causal-and-window mask.  "[CPU] Add windowed kv cache for GQA", intro:
+# windowed results equal those of a full-length cache; causal rule of
+# "Fix CPU Attention causal mask ..." (j <= i + past); window of W keys.
+def brute_force(cfg: Cfg, syn, b, P, S, vers, q_storage, bias=None):
+    T = P + S
+    pos = np.arange(T)
+    ver = vers.of(b, pos)[None, :]
+    heads = np.arange(cfg.Hkv)[:, None]
+    Kall = as_f64(syn.kv_rows(synth.K, b, heads, pos[None, :], ver), cfg.dtype)
+    Vall = as_f64(syn.kv_rows(synth.V, b, heads, pos[None, :], ver), cfg.dtype)
+    q = as_f64(q_storage, cfg.dtype).reshape(S, cfg.Hq, cfg.D)
+    scale = cfg.scale if cfg.scale > 0 else 1.0 / np.sqrt(cfg.D)
+    i = np.arange(S)[:, None]
+    j = np.arange(T)[None, :]
+    mask = (j <= P + i) & (j > P + i - cfg.W)
+    out = np.zeros((S, cfg.Hq, cfg.D))
+    grp = cfg.Hq // cfg.Hkv
+    for h in range(cfg.Hq):
+        g = h // grp
+        s = scale * (q[:, h, :] @ Kall[g].T)
+        if cfg.softcap > 0:
+            s = cfg.softcap * np.tanh(s / cfg.softcap)
+        if bias is not None:
+            s = s + bias[h, :, :T]
+        s = np.where(mask, s, -np.inf)
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (w @ Vall[g]) / w.sum(axis=1, keepdims=True)
+    return out.reshape(S, cfg.Hq * cfg.D)
+
+
+def _close_to_rounded(got_storage, ref, dtype):
+    got = as_f64(got_storage, dtype)
+    # half an ulp of the format plus fp64 noise, with the subnormal quantum
+    # as the absolute floor
+    rel = {synth.F32: 2.0**-23, synth.F16: 2.0**-10, synth.BF16: 2.0**-7}[dtype]
+    floor = {synth.F32: 2.0**-149, synth.F16: 2.0**-24, synth.BF16: 2.0**-133}[dtype]
+    return np.all(np.abs(got - ref) <= rel * np.abs(ref) + floor)
+
+
+def run_sequence(cfg: Cfg, steps, check=None, vers=None, bias_fn=None):
+    """Drive the oracle through `steps` (list of S) for every item in lock
+    step from T=0.  Returns per-position outputs {(b, pos): row}."""
+    syn = cfg.synth()
+    vers = vers or Versions(cfg.B)
+    be = OracleBackend(cfg)
+    T = np.zeros(cfg.B, dtype=np.int64)
+    outs = {}
+    for S in steps:
+        P = T.copy()
+        T = T + S
+        q, k, v = step_inputs(cfg, syn, P, S, vers)
+        bias = None
+        if bias_fn is not None:
+            bias = bias_fn(syn, P, S, int(T.max()))
+        st, out, plan = be.step(S, T - 1, q, k, v, bias=bias)
+        assert st == 0
+        for b in range(cfg.B):
+            for i in range(S):
+                outs[(b, int(P[b]) + i)] = out[b, i].copy()
+        if check is not None:
+            check(be, syn, P, S, T, q, out, plan, vers, bias)
+    return outs, be
+
+
+def _check_layout(cfg):
+    def check(be, syn, P, S, T, q, out, plan, vers, bias):
+        for b in range(cfg.B):
+            L, k, v = layout_rows(cfg, syn, b, int(T[b]), vers)
+            assert plan[b, 3] == L
+            assert np.array_equal(be.K[b, :, :L].view(np.uint8), k.view(np.uint8))
+            assert np.array_equal(be.V[b, :, :L].view(np.uint8), v.view(np.uint8))
+    return check
+
+
+# ---------------------------------------------------------------------------
+# P2 + P5: layout by regeneration after every step, and outputs equal to the
+# full-cache brute force, over many small shapes and step splits.
+SMALL = [
+    Cfg(B=1, Hq=4, Hkv=2, D=8, C=6, W=4, seed=1001, v_pos=True),
+    Cfg(B=2, Hq=2, Hkv=2, D=4, C=5, W=5, seed=11),
+    Cfg(B=1, Hq=3, Hkv=1, D=2, C=7, W=1, seed=12),
+    Cfg(B=2, Hq=4, Hkv=1, D=8, C=9, W=3, seed=13, dtype=synth.F16),
+    Cfg(B=1, Hq=2, Hkv=1, D=8, C=8, W=6, seed=14, dtype=synth.BF16, softcap=2.0),
+    Cfg(B=1, Hq=4, Hkv=4, D=1, C=1, W=1, seed=15),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"C{c.C}W{c.W}D{c.D}t{c.dtype}")
+def test_p2_p5_layout_and_brute_force(cfg):
+    rng = np.random.default_rng(cfg.seed)
+    steps = [int(s) for s in rng.integers(1, 2 * cfg.C + 2, size=12)]
+    vers = Versions(cfg.B)
+    layout = _check_layout(cfg)
+
+    def check(be, syn, P, S, T, q, out, plan, vers_, bias):
+        layout(be, syn, P, S, T, q, out, plan, vers_, bias)
+        for b in range(cfg.B):
+            ref = brute_force(cfg, syn, b, int(P[b]), S, vers_, q[b])
+            assert _close_to_rounded(out[b], ref, cfg.dtype)
+
+    run_sequence(cfg, steps, check=check, vers=vers)
+
+
+def test_p5_brute_force_catches_a_planted_window_error():
+    """The brute-force pin is sensitive: a window one key wider than the
+    contract's changes the outputs (the oracle is checked against W, and a
+    copy of the reference with W+1 disagrees)."""
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=4, C=6, W=3, seed=3)
+    outs, _ = run_sequence(cfg, [8, 1, 1])
+    syn = cfg.synth()
+    vers = Versions(1)
+    wide = Cfg(**{**cfg.__dict__, "W": 4, "C": 6})
+    q, _, _ = step_inputs(cfg, syn, np.array([9]), 1, vers)
+    ref_ok = brute_force(cfg, syn, 0, 9, 1, vers, q[0])
+    ref_wide = brute_force(wide, syn, 0, 9, 1, vers, q[0])
+    assert _close_to_rounded(outs[(0, 9)][None], ref_ok, cfg.dtype)
+    assert not _close_to_rounded(outs[(0, 9)][None], ref_wide, cfg.dtype)
+
+
+# ---------------------------------------------------------------------------
+# P3. Step-split invariance: "Specify ... layout contract", Description (the
+# layout depends only on T; a multi-token step leaves the layout the same
+# tokens leave one at a time) and Summary of Changes (8-token prefill then a
+# 4-token step vs four 1-token steps, byte-identical presents and outputs).
+def test_p3_prefill8_then_4_vs_four_single_steps():
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=8, C=6, W=4, seed=1001, v_pos=True)
+    outs_a, be_a = run_sequence(cfg, [8, 4], check=_check_layout(cfg))
+    outs_b, be_b = run_sequence(cfg, [8, 1, 1, 1, 1], check=_check_layout(cfg))
+    L = oracle.resident_length(12, cfg.C, cfg.W)
+    assert np.array_equal(be_a.K[:, :, :L].view(np.uint8), be_b.K[:, :, :L].view(np.uint8))
+    assert np.array_equal(be_a.V[:, :, :L].view(np.uint8), be_b.V[:, :, :L].view(np.uint8))
+    for pos in range(12):
+        assert np.array_equal(outs_a[(0, pos)].view(np.uint8), outs_b[(0, pos)].view(np.uint8))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_p3_random_partitions(seed):
+    rng = np.random.default_rng(100 + seed)
+    C = int(rng.integers(1, 10))
+    W = int(rng.integers(1, C + 1))
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=4, C=C, W=W, seed=200 + seed)
+    total = 40
+    parts = []
+    for _ in range(3):
+        steps, t = [], 0
+        while t < total:
+            s = int(min(total - t, rng.integers(1, 2 * C + 2)))
+            steps.append(s)
+            t += s
+        parts.append(steps)
+    parts.append([1] * total)
+    runs = [run_sequence(cfg, st, check=_check_layout(cfg)) for st in parts]
+    for o, be in runs[1:]:
+        for pos in range(total):
+            assert np.array_equal(o[(0, pos)].view(np.uint8), runs[0][0][(0, pos)].view(np.uint8))
+        L = oracle.resident_length(total, C, W)
+        assert np.array_equal(be.K[:, :, :L], runs[0][1].K[:, :, :L])
+
+
+# ---------------------------------------------------------------------------
+# P4. Rollback: "Specify ... layout contract", Description: rejecting k drafts
+# needs no cache edit and is exact iff L(T-k) == L(T) - k; Summary of Changes:
+# verify 4 drafts, accept 2, resume from the untouched buffer and match the
+# path that only ever appended the accepted tokens.
+def test_p4_rollback_rule_both_directions():
+    checked_exact = checked_inexact = 0
+    for C, W in [(6, 4), (5, 5), (8, 3), (9, 6)]:
+        cfg = Cfg(B=1, Hq=2, Hkv=1, D=4, C=C, W=W, seed=31, v_pos=True)
+        for P in range(0, 3 * C):
+            for S in range(1, C + 2):
+                T = P + S
+                for k in range(0, S):
+                    exact = oracle.rollback_exact(T, k, C, W)
+                    vers_a = Versions(1)
+                    # path A: reach P, verify S drafts
+                    _, be_a = run_sequence(cfg, ([P] if P else []) + [S], vers=vers_a)
+                    # path B: reach P, append only the accepted S - k
+                    vers_b = Versions(1)
+                    steps_b = ([P] if P else []) + ([S - k] if S - k else [])
+                    _, be_b = run_sequence(cfg, steps_b, vers=vers_b)
+                    Lk = oracle.resident_length(T - k, C, W)
+                    same = np.array_equal(be_a.V[:, :, :Lk], be_b.V[:, :, :Lk]) and \
+                        np.array_equal(be_a.K[:, :, :Lk], be_b.K[:, :, :Lk])
+                    assert same == exact, (C, W, P, S, k)
+                    if exact:
+                        checked_exact += 1
+                        # resume both with the same next token (re-drawn)
+                        syn = cfg.synth()
+                        vers_a.bump(0, np.arange(T - k, T))
+                        vers_b.bump(0, np.arange(T - k, T))
+                        q, kk, vv = step_inputs(cfg, syn, np.array([T - k]), 1, vers_a)
+                        _, oa, _ = be_a.step(1, [T - k], q, kk, vv)
+                        _, ob, _ = be_b.step(1, [T - k], q, kk, vv)
+                        assert np.array_equal(oa, ob)
+                        L1 = oracle.resident_length(T - k + 1, C, W)
+                        assert np.array_equal(be_a.V[:, :, :L1], be_b.V[:, :, :L1])
+                    else:
+                        checked_inexact += 1
+                if P > 2 * C:
+                    break
+    assert checked_exact > 100 and checked_inexact > 50
+
+
+def test_p4_tiny_contract_run_a_vs_b():
+    """The tiny contract run: prefill 8 (S > C), 12 decodes, a 4-token verify
+    step at P=20, reject k=2, one decode resumed at T=22 on the untouched
+    buffer; versus the accepted-only path."""
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=8, C=6, W=4, seed=1001, v_pos=True)
+    assert oracle.rollback_exact(24, 2, 6, 4)
+    syn = cfg.synth()
+    va, vb = Versions(1), Versions(1)
+    _, be_a = run_sequence(cfg, [8] + [1] * 12 + [4], vers=va)
+    _, be_b = run_sequence(cfg, [8] + [1] * 12 + [2], vers=vb)
+    va.bump(0, [22, 23])
+    vb.bump(0, [22, 23])
+    q, k, v = step_inputs(cfg, syn, np.array([22]), 1, va)
+    _, oa, _ = be_a.step(1, [22], q, k, v)
+    _, ob, _ = be_b.step(1, [22], q, k, v)
+    assert np.array_equal(oa, ob)
+    L = oracle.resident_length(23, 6, 4)
+    assert np.array_equal(be_a.K[:, :, :L], be_b.K[:, :, :L])
+    # and the inexact case P=19, S=4, k=2: L(21)=6 != L(23)-2=3
+    assert oracle.resident_length(21, 6, 4) == 6 and oracle.resident_length(23, 6, 4) == 5
+    assert not oracle.rollback_exact(23, 2, 6, 4)
+
+
+# ---------------------------------------------------------------------------
+# P6. Zero query: every visible score is equal, so each output is the mean of
+# the visible V rows; with V[..., 0] = absolute position that mean is
+# (lo + p) / 2 with lo = max(0, p - W + 1).
+@pytest.mark.parametrize("C,W", [(6, 4), (7, 7), (9, 2)])
+def test_p6_zero_query_closed_form(C, W):
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=8, C=C, W=W, seed=61, v_pos=True, zero_q=True)
+    outs, _ = run_sequence(cfg, [C + 2, 1, 3, 1, 2 * C + 1, 1])
+    for (b, p), row in outs.items():
+        lo = max(0, p - W + 1)
+        got = row.reshape(cfg.Hq, cfg.D)[:, 0]
+        assert np.all(got == np.float32((lo + p) / 2.0)), (p, got)
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split("=", 1)
+            vals[k.strip()] = np.array([float(x) for x in v.split()], dtype=np.float32)
+    return vals
+
+
+def _onehot_step(W):
+    """Two cached positions and a two-token step; V rows one-hot at their
+    position, K and Q zero (the printed example's inputs)."""
+    D = 4
+    p = oracle.make_params(1, 2, 1, 1, D, 6, W, 4, synth.F32)
+    eye = np.eye(4, D, dtype=np.float32)
+    past_k = np.zeros((1, 1, 6, D), np.float32)
+    past_v = np.full((1, 1, 6, D), np.nan, np.float32)
+    past_v[0, 0, :2] = eye[:2]
+    q = np.zeros((1, 2, D), np.float32)
+    k = np.zeros((1, 2, D), np.float32)
+    v = eye[2:].reshape(1, 2, D).copy()
+    st, out, _ = oracle.forward(p, q, k, v, past_k, past_v, np.array([3], np.int32))
+    assert st == 0
+    return out[0]
+
+
+def test_p6_printed_causal_example():
+    """"Fix CPU Attention causal mask for q_len=1 with past_key and
+    kv_len > 1", Description / repro: the query at position 2 attends keys
+    0, 1, 2 equally -> [1/3, 1/3, 1/3, 0]; the bug gave [0.25]*4."""
+    g = _read_golden("p4_causal_onehot.txt")
+    out = _onehot_step(W=4)
+    assert np.array_equal(out[0], g["reference"])
+    assert not np.array_equal(out[0], g["buggy"])
+    assert np.array_equal(out[1], np.full(4, 0.25, np.float32))
+    out2 = _onehot_step(W=2)  # window of two keys: positions 1 and 2
+    assert np.array_equal(out2[0], np.array([0, 0.5, 0.5, 0], np.float32))
+
+
+# ---------------------------------------------------------------------------
+# P7. attention_bias in absolute key coordinates: "Specify ... layout
+# contract", Description (last dimension stays total_sequence_length; the
+# kernel selects the resident columns).
+def test_p7_bias_spike_selects_absolute_column():
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=4, C=6, W=5, seed=71, v_pos=True)
+    syn = cfg.synth()
+    vers = Versions(1)
+    _, be = run_sequence(cfg, [13], vers=vers)   # T=13, L=5 rows: pos 8..12
+    P, S = 13, 2
+    total = P + S
+    q, k, v = step_inputs(cfg, syn, np.array([P]), S, vers)
+    for jstar in (10, 11, 13):
+        bias = np.zeros((1, cfg.Hq, S, total), np.float32)
+        bias[..., jstar] = 1000.0
+        be2 = OracleBackend(cfg, be.K, be.V)
+        st, out, _ = be2.step(S, [P + S - 1], q, k, v, bias=bias, total=total)
+        assert st == 0
+        vrow = as_f64(syn.kv_rows(synth.V, 0, 0, jstar, 0), cfg.dtype)
+        for i in range(S):
+            if jstar <= P + i and jstar > P + i - cfg.W:
+                for h in range(cfg.Hq):
+                    assert np.array_equal(out[0, i, h * 4:(h + 1) * 4].astype(np.float64), vrow)
+
+
+def test_p7_bias_row_constant_and_weighted_mean():
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=4, C=6, W=4, seed=72, v_pos=True, zero_q=True)
+    syn = cfg.synth()
+    vers = Versions(1)
+    _, be = run_sequence(cfg, [9], vers=vers)
+    P, S, total = 9, 3, 12
+    q, k, v = step_inputs(cfg, syn, np.array([P]), S, vers)
+    rng = np.random.default_rng(0)
+    w = rng.uniform(0.5, 2.0, size=(cfg.Hq, S, total))
+    bias = np.log(w).astype(np.float32)[None]
+    st, out, _ = OracleBackend(cfg, be.K, be.V).step(S, [P + S - 1], q, k, v, bias=bias, total=total)
+    for i in range(S):
+        p = P + i
+        js = np.arange(max(0, p - cfg.W + 1), p + 1)
+        for h in range(cfg.Hq):
+            ww = np.exp(bias[0, h, i, js].astype(np.float64))
+            want = np.sum(ww * js) / np.sum(ww)      # V[...,0] = position
+            assert abs(out[0, i, h * 4] - want) <= 2**-22 * abs(want)
+    # a per-row constant leaves the output unchanged
+    bias2 = bias + np.float32(3.0)
+    _, out2, _ = OracleBackend(cfg, be.K, be.V).step(S, [P + S - 1], q, k, v, bias=bias2, total=total)
+    assert np.allclose(out2, out, rtol=2**-21, atol=0)
+
+
+def test_p7_bias_broadcast_dims():
+    cfg = Cfg(B=2, Hq=2, Hkv=1, D=4, C=6, W=4, seed=73)
+    syn = cfg.synth()
+    vers = Versions(2)
+    _, be = run_sequence(cfg, [7], vers=vers)
+    P, S, total = 7, 2, 9
+    q, k, v = step_inputs(cfg, syn, np.array([P, P]), S, vers)
+    small = np.random.default_rng(1).normal(0, 0.1, (1, 1, S, total)).astype(np.float32)
+    full = np.broadcast_to(small, (2, 2, S, total)).copy()
+    _, o1, _ = OracleBackend(cfg, be.K, be.V).step(S, [8, 8], q, k, v, bias=small, total=total, bias_bcast=(0, 0))
+    _, o2, _ = OracleBackend(cfg, be.K, be.V).step(S, [8, 8], q, k, v, bias=full, total=total)
+    assert np.array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# P8. softcap (Investigation Report 1.3: logit soft-capping, 0 = disabled):
+# zero query unchanged; saturation closed form; a huge cap equals none.
+def test_p8_softcap_saturation_closed_form():
+    D, c = 4, 1.5
+    p = oracle.make_params(1, 1, 1, 1, D, 4, 4, 2, synth.F32, scale=1.0, softcap=c)
+    past_k = np.zeros((1, 1, 4, D), np.float32)
+    past_v = np.zeros((1, 1, 4, D), np.float32)
+    past_k[0, 0, 0] = [1, 0, 0, 0]
+    past_v[0, 0, 0] = [1, 0, 0, 0]
+    q = np.array([[[100.0, 0, 0, 0]]], np.float32)
+    k = np.array([[[-1.0, 0, 0, 0]]], np.float32)     # score -100 -> -c
+    v = np.array([[[0, 1.0, 0, 0]]], np.float32)
+    _, out, _ = oracle.forward(p, q, k, v, past_k, past_v, np.array([1], np.int32))
+    e1, e2 = np.exp(c), np.exp(-c)
+    want = np.array([e1 / (e1 + e2), e2 / (e1 + e2), 0, 0])
+    assert np.all(np.abs(out[0, 0] - want) <= 2**-23 * np.abs(want) + 1e-30)
+
+
+def test_p8_softcap_limits():
+    base = Cfg(B=1, Hq=2, Hkv=1, D=8, C=6, W=4, seed=81)
+    o_none, _ = run_sequence(base, [7, 1, 2])
+    o_huge, _ = run_sequence(Cfg(**{**base.__dict__, "softcap": 1e30}), [7, 1, 2])
+    for key in o_none:
+        assert np.allclose(o_none[key], o_huge[key], rtol=2**-22, atol=0)
+    o_small, _ = run_sequence(Cfg(**{**base.__dict__, "softcap": 0.05}), [7, 1, 2])
+    assert any(not np.allclose(o_none[k], o_small[k], rtol=1e-3) for k in o_none)
+    z = Cfg(**{**base.__dict__, "zero_q": True, "v_pos": True})
+    o_z, _ = run_sequence(z, [7, 1])
+    o_zc, _ = run_sequence(Cfg(**{**z.__dict__, "softcap": 0.7}), [7, 1])
+    for key in o_z:
+        assert np.array_equal(o_z[key], o_zc[key])
+
+
+# ---------------------------------------------------------------------------
+# P9. GQA grouping (Investigation Report 1.3: num_heads Q heads share
+# kv_num_heads K/V heads): with a zero query each Q head averages its KV
+# head's V rows; MHA (Hq == Hkv) is the identity grouping.
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 3), (4, 4), (5, 1)])
+def test_p9_grouping(Hq, Hkv):
+    D, C, W = 4, 5, 3
+    p = oracle.make_params(1, 2, Hq, Hkv, D, C, W, 7, synth.F32)
+    past_k = np.zeros((1, Hkv, C, D), np.float32)
+    past_v = np.zeros((1, Hkv, C, D), np.float32)
+    for g in range(Hkv):
+        past_v[0, g] = g + 1.0
+    q = np.zeros((1, 2, Hq * D), np.float32)
+    k = np.zeros((1, 2, Hkv * D), np.float32)
+    v = np.repeat(np.arange(1, Hkv + 1, dtype=np.float32), D)[None, None, :].repeat(2, 1).copy()
+    _, out, _ = oracle.forward(p, q, k, v, past_k, past_v, np.array([6], np.int32))
+    for h in range(Hq):
+        assert np.all(out[0, :, h * D:(h + 1) * D] == h // (Hq // Hkv) + 1.0)
+
+
+# ---------------------------------------------------------------------------
+# P10. Staging criterion: "[CPU] Add windowed kv cache for GQA", staging for
+# hazardous steps.  Where the plan says "no hazard", compacting first and
+# attending over the cache alone gives byte-identical outputs and caches;
+# where it says "hazard", compacting first loses a key some query reads.
+def test_p10_hazard_criterion_is_tight():
+    n_h = n_ok = 0
+    for C in range(1, 11):
+        for W in range(1, C + 1):
+            cfg = Cfg(B=1, Hq=2, Hkv=1, D=2, C=C, W=W, seed=C * 16 + W)
+            syn = cfg.synth()
+            vers = Versions(1)
+            for P in range(0, 2 * C + 3):
+                _, be = run_sequence(cfg, [P] if P else [], vers=vers)
+                for S in range(1, 2 * C + 2):
+                    q, k, v = step_inputs(cfg, syn, np.array([P]), S, vers)
+                    p = cfg.params(S, P + S)
+                    _, plan = oracle.plan(p, np.array([P + S - 1]))
+                    hazard = plan[0, 7]
+                    a = OracleBackend(cfg, be.K, be.V)
+                    _, oa, _ = a.step(S, [P + S - 1], q, k, v)
+                    bk, bv = be.K.copy(), be.V.copy()
+                    st, ob = oracle.forward_compact_first(p, q, k, v, bk, bv,
+                                                          np.array([P + S - 1], np.int32))
+                    if hazard:
+                        n_h += 1
+                        assert st == 5, (C, W, P, S)
+                    else:
+                        n_ok += 1
+                        assert st == 0, (C, W, P, S)
+                        La = plan[0, 3]
+                        assert np.array_equal(oa, ob)
+                        assert np.array_equal(a.K[:, :, :La], bk[:, :, :La])
+                        assert np.array_equal(a.V[:, :, :La], bv[:, :, :La])
+    assert n_h > 100 and n_ok > 100
+
+
+def test_p10_decode_never_hazardous():
+    for C in range(1, 40):
+        for W in range(1, C + 1):
+            T = np.arange(1, 400)
+            p = oracle.make_params(len(T), 1, 1, 1, 1, C, W, 400)
+            st, plan = oracle.plan(p, T - 1)
+            assert st == 0 and not plan[:, 7].any()
+
+
+# ---------------------------------------------------------------------------
+# P11. Printed facts of "[CPU] Add windowed kv cache for GQA": C = W + 8 with
+# 400 decode steps gives about 44 compactions (Tests table); at C = W = 128
+# every decode moves C - 1 rows, 0.50 MiB per token for 8 KV heads x 64 fp32
+# (key design decisions); the C = 384 cache is 1.50 MiB (Performance).
+def test_p11_printed_facts():
+    W, C = 128, 136
+    T = 512 + np.arange(1, 401)
+    p = oracle.make_params(len(T), 1, 64, 8, 64, C, W, 2000)
+    _, plan = oracle.plan(p, T - 1)
+    events = int(np.count_nonzero(plan[:, 5] > 0))
+    assert 44 <= events <= 45
+    assert list(T[plan[:, 5] > 0][:3]) == [515, 524, 533]
+    p = oracle.make_params(3, 1, 64, 8, 64, 128, 128, 2000)
+    _, plan = oracle.plan(p, np.array([300, 700, 1500]))
+    moved = plan[:, 4] * 8 * 2 * 64 * 4          # kept rows x heads x (K,V) x row
+    assert np.all(plan[:, 4] == 127)
+    assert round(moved[0] / 2**20, 2) == 0.50
+    assert 8 * 2 * 384 * 64 * 4 / 2**20 == 1.5
+
+
+def test_invalid_items_zero_output_untouched_cache():
+    cfg = Cfg(B=3, Hq=2, Hkv=1, D=4, C=6, W=4, seed=91)
+    syn = cfg.synth()
+    vers = Versions(3)
+    _, be = run_sequence(cfg, [5], vers=vers)
+    q, k, v = step_inputs(cfg, syn, np.array([5, 5, 5]), 2, vers)
+    before = be.snapshot()
+    seq = np.array([6, 0, 6], np.int32)      # item 1: T=1 < S=2
+    st, out, plan = be.step(2, seq, q, k, v, total=7)
+    assert st == 4
+    assert np.all(out[1] == 0) and np.all(plan[1] == -1)
+    assert np.array_equal(be.K[1].view(np.uint8), before[0][1].view(np.uint8))
+    seq = np.array([6, 6, 9], np.int32)      # item 2: T=10 > total=7
+    st, out, plan = OracleBackend(cfg, *before).step(2, seq, q, k, v, total=7)
+    assert st == 4 and np.all(out[2] == 0)
+
+
+def test_argument_errors():
+    p = oracle.make_params(1, 1, 3, 2, 4, 6, 4, 8)
+    z = np.zeros(64, np.float32)
+    assert oracle.forward(p, z, z, z, z, z, np.array([0], np.int32))[0] == 1
+    p = oracle.make_params(1, 1, 2, 2, 4, 6, 7, 8)   # W > C
+    assert oracle.forward(p, z, z, z, z, z, np.array([0], np.int32))[0] == 1
+    p = oracle.make_params(1, 1, 2, 2, 4, 6, 0, 8)   # W < 1
+    assert oracle.forward(p, z, z, z, z, z, np.array([0], np.int32))[0] == 1
+    p = oracle.make_params(1, 1, 1, 1, 4, 2, 2, 8)
+    big = np.zeros(16, np.float32)
+    part = big[4:]                                   # partial overlap
+    st = oracle.lib().swgqa_oracle_forward(
+        p, z.ctypes.data, z.ctypes.data, z.ctypes.data, big.ctypes.data,
+        big.ctypes.data, np.array([0], np.int32).ctypes.data, None,
+        z.ctypes.data, part.ctypes.data, part.ctypes.data, None)
+    assert st == 3
