@@ -1,0 +1,235 @@
+// swgqa_api.hip -- the C ABI of libswgqa (declared in include/swgqa.h):
+// host-side validation, launch planning and kernel dispatch.  No allocation,
+// no synchronisation on the forward path.
+#include "swgqa.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "swgqa_common.hpp"
+#include "swgqa_internal.hpp"
+
+namespace {
+
+using namespace swgqa;
+
+constexpr size_t kHeaderBytes = 256;  // status word + reserved
+constexpr int kTargetWorkgroups = 2048;
+constexpr int kMinKeysPerSplit = 32;
+
+size_t elem_bytes(int dt) { return dt == SWGQA_F32 ? 4 : 2; }
+
+swgqa_status validate(const swgqa_params* p) {
+  if (!p) return SWGQA_ERR_ARG;
+  if (p->batch_size < 0 || p->sequence_length < 1 || p->num_heads < 1 ||
+      p->kv_num_heads < 1 || p->head_size < 1 || p->capacity < 1)
+    return SWGQA_ERR_ARG;
+  if (p->num_heads % p->kv_num_heads != 0) return SWGQA_ERR_ARG;
+  if (p->local_window_size < 1 || p->local_window_size > p->capacity) return SWGQA_ERR_ARG;
+  if (p->total_sequence_length < 1) return SWGQA_ERR_ARG;
+  if (!(p->scale >= 0.0f) || !(p->softcap >= 0.0f)) return SWGQA_ERR_ARG;
+  if (p->dtype < SWGQA_F32 || p->dtype > SWGQA_BF16) return SWGQA_ERR_UNSUPPORTED;
+  if (!head_size_supported(p->head_size)) return SWGQA_ERR_UNSUPPORTED;
+  return SWGQA_OK;
+}
+
+// Launch geometry of the split-K kernel, a pure function of the parameters.
+struct SplitPlan {
+  int nq;      // query tile width ((position, head) pairs)
+  int ntiles;  // tiles per (item, KV head)
+  int nsplit;  // key splits per tile
+};
+
+SplitPlan plan_split(const swgqa_params* p) {
+  SplitPlan s;
+  const int group = p->num_heads / p->kv_num_heads;
+  const int per_kv = p->sequence_length * group;  // queries per (item, KV head)
+  int nq = 2;
+  while (nq < per_kv && nq < 16) nq *= 2;
+  while (nq > 2 && nq * p->head_size > kSplitMaxTileElems) nq /= 2;
+  s.nq = nq;
+  s.ntiles = (per_kv + nq - 1) / nq;
+  // key rows a tile can touch: the window of its first position plus the
+  // positions it spans
+  const int64_t span = (nq + group - 1) / group + 1;
+  int64_t nkeys = (int64_t)p->local_window_size + span - 1;
+  if (nkeys > p->total_sequence_length) nkeys = p->total_sequence_length;
+  const int64_t base = (int64_t)p->batch_size * p->kv_num_heads * s.ntiles;
+  int64_t ns = base > 0 ? (kTargetWorkgroups + base - 1) / base : 1;
+  const int64_t ns_max = (nkeys + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
+  if (ns > ns_max) ns = ns_max;
+  if (ns < 1) ns = 1;
+  s.nsplit = (int)ns;
+  return s;
+}
+
+size_t partial_bytes(const swgqa_params* p, const SplitPlan& s) {
+  if (s.nsplit <= 1) return 0;
+  const size_t rows = (size_t)p->batch_size * p->sequence_length * p->num_heads * s.nsplit;
+  return rows * (size_t)p->head_size * 4 + rows * 2 * 4;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool ranges_partially_overlap(const void* a, const void* b, size_t n) {
+  const char* x = (const char*)a;
+  const char* y = (const char*)b;
+  if (x == y) return false;
+  return x < y + n && y < x + n;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t swgqa_workspace_size(const swgqa_params* p) {
+  if (validate(p) != SWGQA_OK) return 0;
+  const SplitPlan s = plan_split(p);
+  return kHeaderBytes + align256(partial_bytes(p, s));
+}
+
+swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < kHeaderBytes) return SWGQA_ERR_ARG;
+  if (launch_clear_status((uint32_t*)workspace, (hipStream_t)stream) != hipSuccess)
+    return SWGQA_ERR_HIP;
+  return SWGQA_OK;
+}
+
+swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void* key,
+                           const void* value, const void* past_key,
+                           const void* past_value, const int32_t* seqlens_k,
+                           const void* attention_bias, void* output,
+                           void* present_key, void* present_value, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const swgqa_status v = validate(p);
+  if (v != SWGQA_OK) return v;
+  if (p->batch_size == 0) return SWGQA_OK;
+  if (!query || !key || !value || !past_key || !past_value || !seqlens_k || !output ||
+      !present_key || !present_value || !workspace)
+    return SWGQA_ERR_ARG;
+  const size_t e = elem_bytes(p->dtype);
+  const size_t cache_bytes =
+      (size_t)p->batch_size * p->kv_num_heads * p->capacity * p->head_size * e;
+  if (ranges_partially_overlap(past_key, present_key, cache_bytes) ||
+      ranges_partially_overlap(past_value, present_value, cache_bytes))
+    return SWGQA_ERR_ALIAS;
+  if (((uintptr_t)workspace & 255u) != 0) return SWGQA_ERR_ARG;
+  // every 16-byte row access below needs 16-byte aligned rows
+  const uintptr_t align_or = (uintptr_t)query | (uintptr_t)key | (uintptr_t)value |
+                             (uintptr_t)past_key | (uintptr_t)past_value |
+                             (uintptr_t)present_key | (uintptr_t)present_value |
+                             (uintptr_t)output;
+  if (align_or & 15u) return SWGQA_ERR_ARG;
+
+  const SplitPlan s = plan_split(p);
+  if (workspace_bytes < kHeaderBytes + partial_bytes(p, s)) return SWGQA_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const bool shared = present_key == past_key && present_value == past_value;
+
+  AttnArgs a;
+  a.q = query;
+  a.k = key;
+  a.v = value;
+  a.past_k = past_key;
+  a.past_v = past_value;
+  a.seqlens = seqlens_k;
+  a.bias = attention_bias;
+  a.out = output;
+  a.status = (uint32_t*)workspace;
+  float* part = (float*)((char*)workspace + kHeaderBytes);
+  a.opart = part;
+  a.ml = part + (size_t)p->batch_size * p->sequence_length * p->num_heads * s.nsplit *
+                    p->head_size;
+  a.present_k = shared ? present_key : nullptr;
+  a.present_v = shared ? present_value : nullptr;
+  a.B = p->batch_size;
+  a.S = p->sequence_length;
+  a.Hq = p->num_heads;
+  a.Hkv = p->kv_num_heads;
+  a.C = p->capacity;
+  a.W = p->local_window_size;
+  a.total = p->total_sequence_length;
+  a.group = p->num_heads / p->kv_num_heads;
+  a.ntiles = s.ntiles;
+  a.nsplit = s.nsplit;
+  a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_size);
+  a.softcap = p->softcap;
+  a.bias_b = p->bias_dim0_is_batch ? 1 : 0;
+  a.bias_h = p->bias_dim1_is_heads ? 1 : 0;
+
+  if (launch_attn_split(p->dtype, p->head_size, s.nq, a, st) != hipSuccess) return SWGQA_ERR_HIP;
+  if (s.nsplit > 1 && launch_combine(p->dtype, p->head_size, a, st) != hipSuccess)
+    return SWGQA_ERR_HIP;
+
+  CopyArgs c;
+  c.past_k = past_key;
+  c.past_v = past_value;
+  c.k = key;
+  c.v = value;
+  c.present_k = present_key;
+  c.present_v = present_value;
+  c.seqlens = seqlens_k;
+  c.B = p->batch_size;
+  c.S = p->sequence_length;
+  c.Hkv = p->kv_num_heads;
+  c.C = p->capacity;
+  c.W = p->local_window_size;
+  c.total = p->total_sequence_length;
+  c.D = p->head_size;
+  c.elem_bytes = (int32_t)e;
+  c.skip_drifting = shared ? 1 : 0;
+  if (launch_writeback(c, st) != hipSuccess) return SWGQA_ERR_HIP;
+  return SWGQA_OK;
+}
+
+swgqa_status swgqa_plan(const swgqa_params* p, const int32_t* seqlens_k,
+                        swgqa_plan_entry* plan_out, void* stream) {
+  const swgqa_status v = validate(p);
+  if (v != SWGQA_OK) return v;
+  if (p->batch_size == 0) return SWGQA_OK;
+  if (!seqlens_k || !plan_out) return SWGQA_ERR_ARG;
+  if (launch_plan(seqlens_k, p->batch_size, p->sequence_length, p->capacity,
+                  p->local_window_size, p->total_sequence_length, (int64_t*)plan_out,
+                  (hipStream_t)stream) != hipSuccess)
+    return SWGQA_ERR_HIP;
+  return SWGQA_OK;
+}
+
+int64_t swgqa_resident_length(int64_t T, int64_t C, int64_t W) {
+  if (W < 1 || C < W || T < 0) return -1;
+  return resident_len(T, C, W);
+}
+
+int swgqa_rollback_exact(int64_t T, int64_t k, int64_t C, int64_t W) {
+  if (W < 1 || C < W || T < 0 || k < 0 || k > T) return 0;
+  return resident_len(T - k, C, W) == resident_len(T, C, W) - k ? 1 : 0;
+}
+
+swgqa_status swgqa_device_status(const void* workspace, int clear, void* stream) {
+  if (!workspace) return SWGQA_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, st) != hipSuccess)
+    return SWGQA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return SWGQA_ERR_HIP;
+  if (clear) {
+    if (launch_clear_status((uint32_t*)workspace, st) != hipSuccess) return SWGQA_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return SWGQA_ERR_HIP;
+  }
+  return (word & kStatusBadItem) ? SWGQA_ERR_DEVICE_INPUT : SWGQA_OK;
+}
+
+const char* swgqa_status_string(swgqa_status s) {
+  switch (s) {
+    case SWGQA_OK: return "ok";
+    case SWGQA_ERR_ARG: return "invalid argument";
+    case SWGQA_ERR_UNSUPPORTED: return "unsupported head size or element type";
+    case SWGQA_ERR_ALIAS: return "past and present buffers overlap partially";
+    case SWGQA_ERR_DEVICE_INPUT: return "seqlens_k out of range for some item";
+    case SWGQA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

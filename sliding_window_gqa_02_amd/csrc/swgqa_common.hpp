@@ -1,0 +1,158 @@
+// swgqa_common.hpp -- device-side pieces shared by the libswgqa kernels:
+// the resident-range planner, element loads/stores and small wave helpers.
+//
+// Target: AMD CDNA4 (gfx950), wave64.  Nothing here is shared with the CPU
+// oracle under oracle/.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swgqa {
+
+// Element type tags (match swgqa_dtype).
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Status word bits, stored at workspace offset 0.
+enum : uint32_t { kStatusBadItem = 1u };
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Resident-range planner.  "Specify GroupQueryAttention windowed KV cache
+// layout contract" (onnxruntime PR #32419), Description: G = C - W + 1,
+// L(T) = T for T <= C, else T - G * ceil((T - C) / G).  "[CPU] Add windowed
+// kv cache for GQA" (PR #31142), review thread: per-item plan computed in
+// int64 from seqlens_k.
+struct ItemPlan {
+  int64_t T;      // total length after the step
+  int64_t P;      // past length (absolute position of the first new token)
+  int64_t Lb;     // resident rows before the step
+  int64_t La;     // resident rows after the step
+  int64_t kept;   // La - S: old rows that survive (may be negative)
+  int64_t shift;  // Lb + S - La: rows evicted by this step
+  bool ok;        // seqlens_k[b] consistent with S and total length
+};
+
+__host__ __device__ __forceinline__ int64_t resident_len(int64_t T, int64_t C,
+                                                         int64_t W) {
+  if (T <= C) return T;
+  const int64_t G = C - W + 1;
+  return T - G * ((T - C + G - 1) / G);
+}
+
+__device__ __forceinline__ ItemPlan plan_item(int32_t seqlen_k, int64_t S,
+                                              int64_t C, int64_t W,
+                                              int64_t total) {
+  ItemPlan pl;
+  pl.T = (int64_t)seqlen_k + 1;
+  pl.P = pl.T - S;
+  pl.ok = pl.P >= 0 && pl.T <= total;
+  if (!pl.ok) {
+    pl.T = pl.P = pl.Lb = pl.La = pl.kept = pl.shift = -1;
+    return pl;
+  }
+  pl.Lb = resident_len(pl.P, C, W);
+  pl.La = resident_len(pl.T, C, W);
+  pl.kept = pl.La - S;
+  pl.shift = pl.Lb + S - pl.La;
+  return pl;
+}
+
+// ---------------------------------------------------------------------------
+// Element access.  fp32 = float, fp16 = _Float16, bf16 = upper half of a
+// binary32 (kept as uint16_t).  Conversions to the narrow types round to
+// nearest-even.
+template <int DT> struct Elem;
+template <> struct Elem<kF32> { using T = float; static constexpr int bytes = 4; };
+template <> struct Elem<kF16> { using T = _Float16; static constexpr int bytes = 2; };
+template <> struct Elem<kBF16> { using T = uint16_t; static constexpr int bytes = 2; };
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // NaN
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Unpacks one 32-bit word holding 1 (fp32) or 2 (fp16/bf16) elements.
+template <int DT> __device__ __forceinline__ void unpack_word(uint32_t w, float* out);
+template <> __device__ __forceinline__ void unpack_word<kF32>(uint32_t w, float* out) {
+  out[0] = __uint_as_float(w);
+}
+template <> __device__ __forceinline__ void unpack_word<kF16>(uint32_t w, float* out) {
+  union { uint32_t u; _Float16 h[2]; } c;
+  c.u = w;
+  out[0] = (float)c.h[0];
+  out[1] = (float)c.h[1];
+}
+template <> __device__ __forceinline__ void unpack_word<kBF16>(uint32_t w, float* out) {
+  out[0] = bf16_lo(w);
+  out[1] = bf16_hi(w);
+}
+
+template <int DT> __device__ __forceinline__ uint32_t pack_word(const float* in);
+template <> __device__ __forceinline__ uint32_t pack_word<kF32>(const float* in) {
+  return __float_as_uint(in[0]);
+}
+template <> __device__ __forceinline__ uint32_t pack_word<kF16>(const float* in) {
+  union { uint32_t u; _Float16 h[2]; } c;
+  c.h[0] = (_Float16)in[0];
+  c.h[1] = (_Float16)in[1];
+  return c.u;
+}
+template <> __device__ __forceinline__ uint32_t pack_word<kBF16>(const float* in) {
+  return (uint32_t)f32_to_bf16(in[0]) | ((uint32_t)f32_to_bf16(in[1]) << 16);
+}
+
+template <int DT> __device__ __forceinline__ float load_one(const void* base, int64_t idx) {
+  if constexpr (DT == kF32) {
+    return ((const float*)base)[idx];
+  } else if constexpr (DT == kF16) {
+    return (float)((const _Float16*)base)[idx];
+  } else {
+    return __uint_as_float((uint32_t)((const uint16_t*)base)[idx] << 16);
+  }
+}
+
+// Loads NW consecutive 32-bit words (NW*4 bytes, 4-byte aligned at least;
+// 16-byte aligned when NW % 4 == 0) with the widest vector accesses.
+template <int NW>
+__device__ __forceinline__ void load_words(const void* p, uint32_t* w) {
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 v = ((const uint4*)p)[i];
+      w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NW == 2) {
+    const uint2 v = *(const uint2*)p;
+    w[0] = v.x; w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = ((const uint32_t*)p)[i];
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void store_words(void* p, const uint32_t* w) {
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i)
+      ((uint4*)p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else if constexpr (NW == 2) {
+    *(uint2*)p = make_uint2(w[0], w[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) ((uint32_t*)p)[i] = w[i];
+  }
+}
+
+// Marks the workspace status word (sticky).
+__device__ __forceinline__ void flag_status(uint32_t* status, uint32_t bits) {
+  atomicOr(status, bits);
+}
+
+}  // namespace swgqa

@@ -1,0 +1,137 @@
+// swgqa_copy.hip -- cache write-back (append + block compaction), the
+// planner kernel and the status-word reset.
+//
+// After a step, rows [0, La) of present hold the newest La rows of the
+// logical concatenation [resident rows | S new rows] ("Specify
+// GroupQueryAttention windowed KV cache layout contract", Description).  In
+// cache terms ("[CPU] Add windowed kv cache for GQA", key design decisions):
+// the old rows [shift, Lb) move to [0, kept) -- only when a gap-sized block is
+// reclaimed (shift > 0); on drifting steps nothing moves -- and the new rows
+// land after them.  Rows a step of S > C never keeps are dropped.
+//
+// This kernel runs after attention on the same stream, so in the shared
+// buffer mode (present == past) no row a query reads is overwritten early.
+// In place, the move [shift, Lb) -> [0, kept) overlaps itself whenever
+// kept > shift; it is done by one workgroup per (item, KV head, K|V) in
+// passes of at most `shift` rows with a barrier between passes: a pass's
+// destination rows were sources only of earlier passes, whose loads have
+// completed.  The append waits for the whole move, since new rows may land on
+// rows the move still reads.
+#include "swgqa_common.hpp"
+#include "swgqa_internal.hpp"
+
+namespace swgqa {
+
+namespace {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;   // 16-byte words per thread per pass
+
+__global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int which = blockIdx.z;  // 0: key cache, 1: value cache
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  if (!pl.ok) return;
+
+  const void* past = which ? a.past_v : a.past_k;
+  void* present = which ? a.present_v : a.present_k;
+  const char* fresh = (const char*)(which ? a.v : a.k);
+  const bool shared = present == past;
+  if (shared && pl.shift == 0 && a.skip_drifting) return;  // appended by attention
+
+  const int64_t rowb = (int64_t)a.D * a.elem_bytes;
+  const int64_t w16 = rowb / 16;  // 16-byte words per row
+  const int64_t slice = ((int64_t)b * a.Hkv + kvh) * a.C * rowb;
+  const uint4* src = (const uint4*)((const char*)past + slice);
+  uint4* dst = (uint4*)((char*)present + slice);
+  const int tid = threadIdx.x;
+
+  // 1. Surviving old rows: [shift, shift + kept) -> [0, kept).
+  if (pl.kept > 0 && (!shared || pl.shift > 0)) {
+    if (shared) {
+      const int64_t cap_rows = (int64_t)kCopyThreads * kCopyUnroll / w16;
+      const int64_t pass = pl.shift < cap_rows ? pl.shift : (cap_rows > 0 ? cap_rows : 1);
+      for (int64_t r0 = 0; r0 < pl.kept; r0 += pass) {
+        const int64_t nr = pl.kept - r0 < pass ? pl.kept - r0 : pass;
+        const int64_t nw = nr * w16;
+        uint4 buf[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int64_t idx = tid + (int64_t)u * kCopyThreads;
+          if (idx < nw) buf[u] = src[(pl.shift + r0) * w16 + idx];
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int64_t idx = tid + (int64_t)u * kCopyThreads;
+          if (idx < nw) dst[r0 * w16 + idx] = buf[u];
+        }
+        // every load of this pass completes before the next pass stores
+        __syncthreads();
+      }
+    } else {
+      const int64_t nw = pl.kept * w16;
+      for (int64_t idx = tid; idx < nw; idx += kCopyThreads)
+        dst[idx] = src[pl.shift * w16 + idx];
+    }
+  }
+  __syncthreads();
+
+  // 2. New rows i in [max(0, -kept), S) -> row kept + i.
+  const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
+  const int64_t nw = (a.S - i0) * w16;
+  for (int64_t idx = tid; idx < nw; idx += kCopyThreads) {
+    const int64_t i = i0 + idx / w16;
+    const int64_t w = idx % w16;
+    const uint4* s = (const uint4*)(fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb);
+    dst[(pl.kept + i) * w16 + w] = s[w];
+  }
+}
+
+__global__ void plan_kernel(const int32_t* seqlens, int32_t B, int32_t S,
+                            int32_t C, int32_t W, int32_t total, int64_t* out) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const ItemPlan pl = plan_item(seqlens[b], S, C, W, total);
+  int64_t* o = out + 8 * (int64_t)b;
+  if (!pl.ok) {
+    for (int f = 0; f < 8; ++f) o[f] = -1;
+    return;
+  }
+  // hazard: compacting before attention would drop history query 0 reads
+  const int64_t need = pl.P < W - 1 ? pl.P : (int64_t)W - 1;
+  o[0] = pl.T;
+  o[1] = pl.P;
+  o[2] = pl.Lb;
+  o[3] = pl.La;
+  o[4] = pl.kept;
+  o[5] = pl.shift;
+  o[6] = pl.T - pl.La;
+  o[7] = pl.kept < need ? 1 : 0;
+}
+
+__global__ void clear_status_kernel(uint32_t* status) {
+  status[threadIdx.x] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_writeback(const CopyArgs& a, hipStream_t st) {
+  const dim3 grid(a.Hkv, a.B, 2);
+  writeback_kernel<<<grid, kCopyThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
+                       int32_t W, int32_t total, int64_t* out, hipStream_t st) {
+  const int threads = 64;
+  plan_kernel<<<(B + threads - 1) / threads, threads, 0, st>>>(seqlens, B, S, C, W, total, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_status(uint32_t* status, hipStream_t st) {
+  clear_status_kernel<<<1, 64, 0, st>>>(status);
+  return hipGetLastError();
+}
+
+}  // namespace swgqa

@@ -1,0 +1,62 @@
+// swgqa_internal.hpp -- launch interface between the C ABI (swgqa_api.hip)
+// and the kernels.  Internal to libswgqa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swgqa {
+
+// Arguments shared by the attention kernels.  Pointers are device pointers;
+// layouts as in include/swgqa.h.
+struct AttnArgs {
+  const void* q;
+  const void* k;        // new rows (B, S, Hkv*D)
+  const void* v;
+  const void* past_k;   // (B, Hkv, C, D)
+  const void* past_v;
+  const int32_t* seqlens;
+  const void* bias;     // NULL or (B|1, Hq|1, S, total)
+  void* out;            // (B, S, Hq*D)
+  float* opart;         // split partial accumulators (rows of D floats)
+  float* ml;            // split partial (max, sum) pairs, log2 domain
+  uint32_t* status;
+  // fused append on drifting steps (shared buffer only; may be NULL)
+  void* present_k;
+  void* present_v;
+  int32_t B, S, Hq, Hkv, C, W, total, group;
+  int32_t ntiles, nsplit;
+  float scale, softcap;
+  int32_t bias_b, bias_h;
+};
+
+struct CopyArgs {
+  const void* past_k;
+  const void* past_v;
+  const void* k;
+  const void* v;
+  void* present_k;
+  void* present_v;
+  const int32_t* seqlens;
+  int32_t B, S, Hkv, C, W, total, D;
+  int32_t elem_bytes;
+  int32_t skip_drifting;  // shared buffer and the append already fused
+};
+
+// Split-K attention for short steps; returns hipSuccess or the launch error.
+hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
+                             hipStream_t stream);
+hipError_t launch_combine(int dtype, int D, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_writeback(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
+                       int32_t W, int32_t total, int64_t* out, hipStream_t stream);
+hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
+
+// Supported head sizes of every kernel.
+bool head_size_supported(int D);
+
+// The split kernel's query tile holds NQ (position, head) pairs, NQ in
+// {2, 4, 8, 16}, with NQ * D <= kSplitMaxTileElems.
+constexpr int kSplitMaxTileElems = 2048;
+
+}  // namespace swgqa

@@ -1,0 +1,156 @@
+"""GPU side of the parity tests: device buffers (torch) + calls through the
+C ABI of libswgqa via the thin binding.
+
+Storage is raw: float32 for fp32, int16 bit patterns for fp16/bf16, so the
+bytes the oracle and the GPU see are identical.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sliding_window_gqa_02_amd as sw
+import synth
+from tests.scenario import NAN16, Cfg
+
+DEV = "cuda:0"
+GUARD = 4096  # elements of canary before and after every cache buffer
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def to_host(t: torch.Tensor, dtype: int) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if dtype != synth.F32 else a
+
+
+def nan_value(dtype):
+    return float("nan") if dtype == synth.F32 else int(np.uint16(NAN16[dtype]).view(np.int16))
+
+
+def torch_storage(dtype):
+    return torch.float32 if dtype == synth.F32 else torch.int16
+
+
+class GuardedCache:
+    """A (B, Hkv, C, D) cache inside a larger allocation whose margins hold a
+    canary pattern; `intact()` checks nothing was written outside."""
+
+    CANARY32 = 0x5A5AA5A5
+
+    def __init__(self, shape, dtype):
+        n = int(np.prod(shape))
+        st = torch_storage(dtype)
+        self.flat = torch.empty(n + 2 * GUARD, dtype=st, device=DEV)
+        if dtype == synth.F32:
+            self.flat.view(torch.int32).fill_(self.CANARY32)
+        else:
+            self.flat.fill_(0x2BCD)
+        self.t = self.flat[GUARD:GUARD + n].view(*shape)
+        self.t.fill_(nan_value(dtype))
+        self.dtype = dtype
+
+    def intact(self) -> bool:
+        g = torch.cat([self.flat[:GUARD], self.flat[-GUARD:]])
+        if self.dtype == synth.F32:
+            return bool((g.view(torch.int32) == self.CANARY32).all())
+        return bool((g == 0x2BCD).all())
+
+
+class GpuBackend:
+    """Cache state advanced by libswgqa.  mode 'shared': present == past (in
+    place); mode 'separate': ping-pong between two buffers."""
+
+    def __init__(self, cfg: Cfg, K=None, V=None, B=None, mode="shared"):
+        B = cfg.B if B is None else B
+        self.cfg = cfg
+        self.B = B
+        self.mode = mode
+        shape = (B, cfg.Hkv, cfg.C, cfg.D)
+        self.bufs = [(GuardedCache(shape, cfg.dtype), GuardedCache(shape, cfg.dtype))]
+        if mode == "separate":
+            self.bufs.append((GuardedCache(shape, cfg.dtype), GuardedCache(shape, cfg.dtype)))
+        if K is not None:
+            self.bufs[0][0].t.copy_(to_dev(K))
+            self.bufs[0][1].t.copy_(to_dev(V))
+        self.cur = 0
+        self.ws = None
+        self.ws_bytes = 0
+        self.T = None  # per-item lengths, tracked by the caller via step()
+
+    @property
+    def K(self):
+        return self.bufs[self.cur][0].t
+
+    @property
+    def V(self):
+        return self.bufs[self.cur][1].t
+
+    def intact(self) -> bool:
+        return all(c.intact() for pair in self.bufs for c in pair)
+
+    def _workspace(self, p):
+        need = sw.workspace_size(p)
+        assert need > 0
+        if self.ws is None or need > self.ws_bytes:
+            self.ws = torch.zeros(need // 4 + 64, dtype=torch.int32, device=DEV)
+            self.ws_bytes = need
+            sw.workspace_init(self.ws)
+        return self.ws
+
+    def poison_unspecified(self, P):
+        """Rows [L(P_b), C) of the current cache are unspecified: NaN them so
+        that a kernel reading one shows up in the outputs."""
+        nv = nan_value(self.cfg.dtype)
+        for b, Pb in enumerate(np.asarray(P)):
+            if Pb < 0:
+                continue
+            L = oracle.resident_length(int(Pb), self.cfg.C, self.cfg.W)
+            self.K[b, :, L:].fill_(nv)
+            self.V[b, :, L:].fill_(nv)
+
+    def step(self, S, seqlens, q, k, v, bias=None, total=None, bias_bcast=(1, 1),
+             poison=True):
+        cfg = self.cfg
+        seqlens = np.asarray(seqlens, dtype=np.int32)
+        B = len(seqlens)
+        total = int(seqlens.max()) + 1 if total is None else total
+        p = sw.make_params(B, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, total,
+                           cfg.dtype, cfg.scale, cfg.softcap, *bias_bcast)
+        if poison:
+            self.poison_unspecified(seqlens.astype(np.int64) + 1 - S)
+        dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+        dbias = None if bias is None else to_dev(bias)
+        dseq = to_dev(seqlens)
+        out = torch.full(dq.shape, nan_value(cfg.dtype), dtype=torch_storage(cfg.dtype), device=DEV)
+        ws = self._workspace(p)
+        pk, pv = self.K, self.V
+        if self.mode == "separate":
+            nxt = 1 - self.cur
+            prk, prv = self.bufs[nxt][0].t, self.bufs[nxt][1].t
+            prk.fill_(nan_value(cfg.dtype))
+            prv.fill_(nan_value(cfg.dtype))
+        else:
+            nxt = self.cur
+            prk, prv = pk, pv
+        sw.forward(p, dq, dk, dv, pk, pv, dseq, dbias, out, prk, prv, ws)
+        torch.cuda.synchronize()
+        self.cur = nxt
+        status = sw.device_status(ws, clear=True)
+        return status, to_host(out, cfg.dtype)
+
+    def present_host(self):
+        return to_host(self.K, self.cfg.dtype), to_host(self.V, self.cfg.dtype)
+
+    def snapshot(self):
+        return self.K.clone(), self.V.clone()
+
+    def restore(self, snap):
+        self.K.copy_(snap[0])
+        self.V.copy_(snap[1])
