@@ -1,0 +1,416 @@
+#!/usr/bin/env python3
+"""Benchmark of the windowed-GQA decode step on one MI355X.
+
+Headline workload (the pages' decode shape): B=1, 64 Q / 8 KV heads x 64,
+fp32 cache, W=128, C=384; an 8192-token prompt prefilled in one step, then
+decode steps of one token.  A "step" is one decode step of the whole path
+(planner, split-K attention, split combine, append / block compaction);
+`--steps` of them are timed (default 256, which crosses the compaction at
+T=8352).  Inputs are synthetic (seeded, N(0,1)) and resident in HBM before the
+timed region.  The decode loop is replayed from a HIP graph (value) and also
+run eagerly with per-step HIP events (kernel time for the roofline).
+
+Also reported: prefill times, the batched-serving decode (B=32, 32 Q / 8 KV
+heads x 128, bf16, W=4096, C=4608, softcap 50, 128 steps) with its own
+roofline, and the CPU oracle timed on a bounded sample of the headline
+workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+class Workload:
+    def __init__(self, name, B, Hq, Hkv, D, C, W, dtype, scale=0.0, softcap=0.0, seed=0):
+        self.name, self.B, self.Hq, self.Hkv, self.D = name, B, Hq, Hkv, D
+        self.C, self.W, self.dtype, self.scale, self.softcap, self.seed = C, W, dtype, scale, softcap, seed
+        self.e = 4 if dtype == 0 else 2
+
+    def step_bytes(self, T: np.ndarray, S: int, sw) -> dict:
+        """Algorithmic HBM bytes of one step for items with lengths T (after
+        the step): distinct K/V rows the queries read, Q read, output write,
+        appended rows, and rows moved by block compaction (read + write)."""
+        row = self.D * self.e
+        P = T - S
+        n_kv = np.minimum(T, self.W + S - 1)
+        kv_read = int(np.sum(self.Hkv * 2 * n_kv * row))
+        qo = 2 * len(T) * S * self.Hq * row
+        La = np.array([sw.resident_length(int(t), self.C, self.W) for t in T])
+        Lb = np.array([sw.resident_length(int(p), self.C, self.W) for p in P])
+        shift = Lb + S - La
+        kept = La - S
+        append = int(np.sum(self.Hkv * 2 * np.minimum(S, La) * row))
+        moved = int(np.sum(np.where((shift > 0) & (kept > 0), self.Hkv * 2 * 2 * kept * row, 0)))
+        return {"kv_read": kv_read, "qo": qo, "append": append, "compaction": moved,
+                "total": kv_read + qo + append + moved}
+
+
+def storage_torch_dtype(torch, dtype):
+    return torch.float32 if dtype == 0 else torch.int16
+
+
+def to_dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+class DecodeLoop:
+    """Device-resident decode loop: inputs for every step staged in HBM, one
+    C-ABI call per step with precomputed arguments."""
+
+    def __init__(self, torch, sw, wl: Workload, P0: np.ndarray, nsteps: int, K, V):
+        import synth
+        self.torch, self.sw, self.wl = torch, sw, wl
+        self.nsteps = nsteps
+        syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
+        B = wl.B
+        qs, ks, vs = [], [], []
+        for s in range(nsteps):
+            q, k, v = syn.step_inputs(P0 + s, 1)
+            qs.append(q), ks.append(k), vs.append(v)
+        self.q = to_dev(torch, np.stack(qs))        # (n, B, 1, Hq*D)
+        self.k = to_dev(torch, np.stack(ks))
+        self.v = to_dev(torch, np.stack(vs))
+        self.seq = to_dev(torch, (P0[None, :] + np.arange(nsteps)[:, None]).astype(np.int32))
+        self.out = torch.empty_like(self.q)
+        self.K, self.V = K, V
+        self.T = P0[None, :] + np.arange(nsteps)[:, None] + 1
+        total = int(self.T.max())
+        self.p = sw.make_params(B, 1, wl.Hq, wl.Hkv, wl.D, wl.C, wl.W, total, wl.dtype,
+                                wl.scale, wl.softcap)
+        nbytes = sw.workspace_size(self.p)
+        self.ws = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda:0")
+        sw.workspace_init(self.ws)
+        lib = sw.load()
+        self.fn = lib.swgqa_forward
+        vp = ctypes.c_void_p
+        self.args = []
+        for s in range(nsteps):
+            self.args.append((ctypes.byref(self.p), vp(self.q[s].data_ptr()),
+                              vp(self.k[s].data_ptr()), vp(self.v[s].data_ptr()),
+                              vp(K.data_ptr()), vp(V.data_ptr()), vp(self.seq[s].data_ptr()),
+                              None, vp(self.out[s].data_ptr()), vp(K.data_ptr()),
+                              vp(V.data_ptr()), vp(self.ws.data_ptr()),
+                              ctypes.c_size_t(nbytes)))
+
+    def run(self, stream, events=None):
+        st = ctypes.c_void_p(stream.cuda_stream)
+        fn = self.fn
+        for s, a in enumerate(self.args):
+            if events is not None:
+                events[s][0].record(stream)
+            rc = fn(*a, st)
+            if events is not None:
+                events[s][1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"swgqa_forward failed at step {s}: {self.sw.status_string(rc)}")
+
+    def bytes_per_step(self):
+        return [self.wl.step_bytes(self.T[s], 1, self.sw) for s in range(self.nsteps)]
+
+
+def time_decode(torch, loop: DecodeLoop, snapshot, use_graph: bool):
+    """Returns dict with eager per-step event times and graph/eager wall times."""
+    K, V = loop.K, loop.V
+    stream = torch.cuda.current_stream()
+
+    def restore():
+        K.copy_(snapshot[0])
+        V.copy_(snapshot[1])
+
+    res = {}
+    # eager, with per-step events (kernel time of the step)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(loop.nsteps)]
+    restore()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop.run(stream, ev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    res["eager_s"] = t1 - t0
+    res["step_ms"] = np.array([a.elapsed_time(b) for a, b in ev])
+    eager_out = loop.out.clone()
+    eager_K = K.clone()
+    # graph: all steps captured once, replayed from the restored snapshot
+    res["graph_s"] = None
+    res["graph_ok"] = None
+    if use_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            restore()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    loop.run(side)
+            torch.cuda.synchronize()
+            ok = True
+            for rep in range(3):
+                restore()
+                loop.out.zero_()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                g.replay()
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                ok = ok and bool(torch.equal(loop.out, eager_out)) and bool(torch.equal(K, eager_K))
+            res["graph_s"] = t1 - t0
+            res["graph_ok"] = ok
+            del g
+        except Exception as exc:  # report, fall back to the eager number
+            res["graph_error"] = repr(exc)
+    return res
+
+
+# ---------------------------------------------------------------------------
+def seeded_cache(torch, sw, wl: Workload, P0: np.ndarray):
+    """Caches holding the contract layout for past lengths P0 (rows
+    [0, L(P_b)) = regenerated positions P_b - L + r); the layout depends only
+    on the length, so this equals the state a prefill + decodes would leave."""
+    import synth
+    syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
+    shape = (wl.B, wl.Hkv, wl.C, wl.D)
+    st = storage_torch_dtype(torch, wl.dtype)
+    K = torch.zeros(shape, dtype=st, device="cuda:0")
+    V = torch.zeros(shape, dtype=st, device="cuda:0")
+    for b, P in enumerate(P0):
+        L = sw.resident_length(int(P), wl.C, wl.W)
+        pos = np.arange(P - L, P)[None, :]
+        heads = np.arange(wl.Hkv)[:, None]
+        K[b, :, :L] = to_dev(torch, syn.kv_rows(synth.K, b, heads, pos))
+        V[b, :, :L] = to_dev(torch, syn.kv_rows(synth.V, b, heads, pos))
+    return K, V
+
+
+def roofline(bytes_list, step_ms):
+    algo = float(sum(b["total"] for b in bytes_list))
+    dur_s = float(np.sum(step_ms)) / 1e3
+    per_launch = algo / len(bytes_list)
+    achieved = algo / dur_s / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 5), "traffic": None,
+            "algorithmic_bytes_per_launch": int(per_launch),
+            "avg_launch_us": round(float(np.mean(step_ms)) * 1e3, 3)}
+
+
+def prefill_times(torch, sw, wl: Workload, prompts):
+    import synth
+    syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
+    out = {}
+    shape = (wl.B, wl.Hkv, wl.C, wl.D)
+    st = storage_torch_dtype(torch, wl.dtype)
+    K = torch.zeros(shape, dtype=st, device="cuda:0")
+    V = torch.zeros(shape, dtype=st, device="cuda:0")
+    for S in prompts:
+        q, k, v = syn.step_inputs(np.zeros(wl.B, np.int64), S)
+        dq, dk, dv = to_dev(torch, q), to_dev(torch, k), to_dev(torch, v)
+        seq = to_dev(torch, np.full(wl.B, S - 1, np.int32))
+        p = sw.make_params(wl.B, S, wl.Hq, wl.Hkv, wl.D, wl.C, wl.W, S, wl.dtype, wl.scale, wl.softcap)
+        ws = torch.zeros(sw.workspace_size(p) // 4 + 64, dtype=torch.int32, device="cuda:0")
+        sw.workspace_init(ws)
+        o = torch.empty_like(dq)
+        times = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            sw.forward(p, dq, dk, dv, K, V, seq, None, o, K, V, ws)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        out[str(S)] = round(min(times[1:]), 4)
+        del dq, dk, dv, o, ws
+    return out, (K, V)
+
+
+def cpu_baseline(wl: Workload, P: int, max_steps: int, seconds: float):
+    """The oracle (fp64, OpenMP over (item, head)) on decode steps of the
+    headline workload, from a cache holding the contract layout at length P."""
+    import oracle
+    import synth
+    from tests.scenario import Cfg, OracleBackend, Versions, seeded_cache as seed_host
+
+    cfg = Cfg(B=wl.B, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, C=wl.C, W=wl.W, dtype=wl.dtype,
+              scale=wl.scale, softcap=wl.softcap, seed=wl.seed)
+    syn = cfg.synth()
+    vers = Versions(wl.B, n=P + max_steps + 8)
+    K, V = seed_host(cfg, syn, [P] * wl.B, vers)
+    be = OracleBackend(cfg, K, V)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = oracle.set_threads(cores)
+    n = 0
+    t_used = 0.0
+    while n < max_steps and t_used < seconds:
+        q, k, v = syn.step_inputs(np.full(wl.B, P + n), 1)
+        t0 = time.perf_counter()
+        st, _, _ = be.step(1, np.full(wl.B, P + n, np.int32), q, k, v)
+        t_used += time.perf_counter() - t0
+        assert st == 0
+        n += 1
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(wl.B * n / t_used, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} decode steps T={P + 1}..{P + n} of the headline workload from a "
+                      f"cache holding the contract layout, fp64 oracle, {threads} OpenMP threads "
+                      f"on {cpu} ({platform.machine()}), {t_used:.1f} s of CPU time",
+            "ms_per_step": round(t_used / n * 1e3, 3)}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--prompt", type=int, default=8192)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-serving", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the windowed GQA step needs no exchange "
+              "between GPUs and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import sliding_window_gqa_02_amd as sw
+    sw.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.init()
+
+    headline = Workload("pages_decode_w128_c384", B=1, Hq=64, Hkv=8, D=64, C=384, W=128,
+                        dtype=0, scale=0.125, seed=1002)
+    result = {}
+
+    # prefill (also leaves the cache at T = prompt, used by the decode loop)
+    prefill = {}
+    if not args.no_prefill:
+        log("prefill ...")
+        prompts = sorted({512, 2048, args.prompt})
+        prefill, _ = prefill_times(torch, sw, headline, prompts)
+        log(f"  prefill ms {prefill}")
+
+    P0 = np.array([args.prompt])
+    K, V = seeded_cache(torch, sw, headline, P0)
+    snap = (K.clone(), V.clone())
+    nsteps = max(args.steps, 1)
+    loop = DecodeLoop(torch, sw, headline, P0, nsteps, K, V)
+    # warm-up: W steps from the snapshot (the loop restores it before timing)
+    warm = DecodeLoop(torch, sw, headline, P0, max(args.warmup, 1), K, V) if args.warmup else None
+    if warm is not None:
+        K.copy_(snap[0]), V.copy_(snap[1])
+        warm.run(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+    log("decode ...")
+    r = time_decode(torch, loop, snap, not args.no_graph)
+    bytes_list = loop.bytes_per_step()
+    wall_s = r["graph_s"] if (r.get("graph_ok") and r["graph_s"]) else r["eager_s"]
+    mode = "hip_graph" if (r.get("graph_ok") and r["graph_s"]) else "eager"
+    K_steps = nsteps
+    value = headline.B * K_steps / wall_s
+    step_us = r["step_ms"] * 1e3
+    rl = roofline(bytes_list, r["step_ms"])
+    kv_gbps = sum(b["kv_read"] for b in bytes_list) / (float(np.sum(r["step_ms"])) / 1e3) / 1e9
+
+    result = {
+        "metric": "decode tokens/s + KV-read HBM GB/s (% peak), windowed GQA W=128 C=384",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_s / K_steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode after a {args.prompt}-token prompt, B=1, 64 Q / 8 KV heads "
+                               f"x 64, fp32 cache, W=128, C=384 (pages' decode shape)",
+                   "global_batch": 1, "seq_len": args.prompt, "capacity": 384, "window": 128},
+        "roofline": rl,
+        "timing": {"mode": mode, "eager_tokens_per_s": round(headline.B * K_steps / r["eager_s"], 2),
+                   "graph_ok": r.get("graph_ok"), "graph_error": r.get("graph_error"),
+                   "step_us_p10": round(float(np.percentile(step_us, 10)), 3),
+                   "step_us_p50": round(float(np.percentile(step_us, 50)), 3),
+                   "step_us_p90": round(float(np.percentile(step_us, 90)), 3),
+                   "kv_read_GBps": round(kv_gbps, 2),
+                   "kv_read_frac_of_peak": round(kv_gbps / PEAK_HBM_GBPS, 5)},
+        "prefill_ms": prefill,
+        "pages_cpu_reference": {"decode_p10_ms_prompt_8192": 0.155,
+                                "hardware": "AMD EPYC 7V12, 8 intra-op threads (context only)"},
+    }
+
+    if not args.no_serving:
+        log("serving decode ...")
+        srv = Workload("batched_serving", B=32, Hq=32, Hkv=8, D=128, C=4608, W=4096, dtype=2,
+                       softcap=50.0, seed=1005)
+        rng = np.random.default_rng(1005)
+        Ps = rng.integers(4096, 32769, size=32)
+        Ks, Vs = seeded_cache(torch, sw, srv, Ps)
+        ssnap = (Ks.clone(), Vs.clone())
+        sloop = DecodeLoop(torch, sw, srv, Ps, 128, Ks, Vs)
+        sloop.run(torch.cuda.current_stream())  # warm-up
+        torch.cuda.synchronize()
+        sr = time_decode(torch, sloop, ssnap, not args.no_graph)
+        sbytes = sloop.bytes_per_step()
+        swall = sr["graph_s"] if (sr.get("graph_ok") and sr["graph_s"]) else sr["eager_s"]
+        srl = roofline(sbytes, sr["step_ms"])
+        skv = sum(b["kv_read"] for b in sbytes) / (float(np.sum(sr["step_ms"])) / 1e3) / 1e9
+        result["serving"] = {
+            "workload": "B=32 decode, 32 Q / 8 KV heads x 128, bf16 cache, W=4096, C=4608, "
+                        "softcap 50, past lengths U[4096, 32768], 128 steps",
+            "tokens_per_s": round(32 * 128 / swall, 1),
+            "ms_per_step": round(swall / 128 * 1e3, 5),
+            "mode": "hip_graph" if (sr.get("graph_ok") and sr["graph_s"]) else "eager",
+            "kv_read_GBps": round(skv, 1),
+            "roofline": srl,
+        }
+        del Ks, Vs, ssnap, sloop
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(headline, args.prompt, 400_000, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
