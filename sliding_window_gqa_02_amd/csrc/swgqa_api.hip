@@ -34,11 +34,13 @@ swgqa_status validate(const swgqa_params* p) {
   return SWGQA_OK;
 }
 
-// Launch geometry of the split-K kernel, a pure function of the parameters.
+// Launch geometry of the attention kernels, a pure function of the
+// parameters.
 struct SplitPlan {
-  int nq;      // query tile width ((position, head) pairs)
-  int ntiles;  // tiles per (item, KV head)
-  int nsplit;  // key splits per tile
+  bool staged;  // the staged decode kernel (else the generic split kernel)
+  int nq;       // query tile width ((position, head) pairs)
+  int ntiles;   // tiles per (item, KV head)
+  int nsplit;   // key splits per tile
 };
 
 SplitPlan plan_split(const swgqa_params* p) {
@@ -47,7 +49,15 @@ SplitPlan plan_split(const swgqa_params* p) {
   const int per_kv = p->sequence_length * group;  // queries per (item, KV head)
   int nq = 2;
   while (nq < per_kv && nq < 16) nq *= 2;
-  while (nq > 2 && nq * p->head_size > kSplitMaxTileElems) nq /= 2;
+  // the staged kernel keeps NQ x (elements per 16 bytes) accumulators per lane
+  int nq_staged = nq;
+  while (nq_staged > 2 && nq_staged * (p->dtype == SWGQA_F32 ? 4 : 8) > 64) nq_staged /= 2;
+  s.staged = decode_kernel_supports(p->dtype, p->head_size, nq_staged);
+  if (s.staged) {
+    nq = nq_staged;
+  } else {
+    while (nq > 2 && nq * p->head_size > kSplitMaxTileElems) nq /= 2;
+  }
   s.nq = nq;
   s.ntiles = (per_kv + nq - 1) / nq;
   // key rows a tile can touch: the window of its first position plus the
@@ -158,7 +168,9 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.bias_b = p->bias_dim0_is_batch ? 1 : 0;
   a.bias_h = p->bias_dim1_is_heads ? 1 : 0;
 
-  if (launch_attn_split(p->dtype, p->head_size, s.nq, a, st) != hipSuccess) return SWGQA_ERR_HIP;
+  const hipError_t ea = s.staged ? launch_attn_decode(p->dtype, p->head_size, s.nq, a, st)
+                                 : launch_attn_split(p->dtype, p->head_size, s.nq, a, st);
+  if (ea != hipSuccess) return SWGQA_ERR_HIP;
   if (s.nsplit > 1 && launch_combine(p->dtype, p->head_size, a, st) != hipSuccess)
     return SWGQA_ERR_HIP;
 

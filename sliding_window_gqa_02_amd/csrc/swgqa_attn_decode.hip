@@ -1,0 +1,486 @@
+// swgqa_attn_decode.hip -- split-K grouped-query attention for short steps
+// (decode and small verify steps) over a windowed KV cache, tuned for
+// CDNA4's wave64 / LDS / HBM balance.
+//
+// Same contract as the generic split kernel (swgqa_attn_split.hip): query i
+// of item b at absolute position p = P + i attends to keys p - W < j <= p of
+// [resident rows | S new rows], keys below P read from cache row
+// j - (P - Lb), the rest from the new rows (no staging copy).
+//
+// Work of one wave is organised in stages of SR consecutive key rows:
+//  A. K rows arrive as 16-byte chunks, LPR lanes per row (coalesced: one load
+//     instruction covers RPW whole rows).  Each lane forms partial dot
+//     products of its chunk with the NQ queries of the tile (packed dot2 for
+//     fp16/bf16) and stores them to LDS -- no cross-lane shuffles.
+//  B. One lane per (row, query) pair sums the LPR partials, applies scale,
+//     softcap, bias and the causal/window mask once (no redundant
+//     transcendental work), takes the stage maximum per query across lanes,
+//     and writes p = 2^(s - m) and the rescale factor to LDS.
+//  C. The V rows (same lane layout as K) are accumulated with p read back
+//     from LDS as a broadcast.
+// K and V of the next stage are loaded into a second register set before
+// stage n is computed, so each wave keeps two stages of loads in flight.
+// LDS traffic is private to the wave and in program order, so phases only
+// need compiler ordering fences, not barriers.
+#include "swgqa_common.hpp"
+#include "swgqa_internal.hpp"
+
+#include <math.h>
+
+namespace swgqa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int DT, int D, int NQ>
+struct DecShape {
+  static constexpr int e = Elem<DT>::bytes;
+  static constexpr int EPL = 16 / e;                    // elements per lane per row
+  static constexpr int LPR = D / EPL;                   // lanes per row
+  static constexpr int RPW = kWave / (LPR > 0 ? LPR : 1);  // rows per load instruction
+  static constexpr int U = (LPR / NQ) >= 1 ? (LPR / NQ) : 1;  // loads per stage
+  static constexpr int SR = RPW * U;                    // rows per wave stage
+  static constexpr int PAIRS = SR * NQ;                 // (row, query) pairs per stage
+  static constexpr int PPL = PAIRS / kWave;             // pairs per lane
+  static constexpr int NW = 4;                          // 32-bit words per chunk
+  static constexpr bool ok = D % EPL == 0 && LPR >= 1 && LPR <= 16 &&
+                             NQ * EPL <= 64 && PAIRS % kWave == 0 && NQ <= kWave;
+};
+
+// Wave-private ordering point for LDS traffic between the phases: LDS
+// instructions of one wave execute in order, so only the compiler must not
+// move accesses across this point.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Max / sum over the lanes that share (lane % NQ): xor offsets NQ..32.
+// Offsets below 16 use DPP inside a 16-lane row (quad_perm for 1 and 2,
+// row rotations by 4 and 8, which cover the same lane classes), the rest
+// cross-row shuffles.
+template <int NQ, bool MAX>
+__device__ __forceinline__ float allreduce_q(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  if constexpr (NQ <= 1) x = op(x, dpp_f<0xB1>(x));    // quad_perm [1,0,3,2]
+  if constexpr (NQ <= 2) x = op(x, dpp_f<0x4E>(x));    // quad_perm [2,3,0,1]
+  if constexpr (NQ <= 4) x = op(x, dpp_f<0x124>(x));   // row_ror:4
+  if constexpr (NQ <= 8) x = op(x, dpp_f<0x128>(x));   // row_ror:8
+  if constexpr (NQ <= 16) x = op(x, __shfl_xor(x, 16, kWave));
+  if constexpr (NQ <= 32) x = op(x, __shfl_xor(x, 32, kWave));
+  return x;
+}
+
+// dot of one 16-byte chunk of Q (held as words) with one chunk of K
+template <int DT>
+__device__ __forceinline__ float chunk_dot(const uint32_t* q, const uint32_t* k, float acc) {
+  if constexpr (DT == kF32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(q[i]), __uint_as_float(k[i]), acc);
+  } else if constexpr (DT == kBF16) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, q[i]),
+                                            __builtin_bit_cast(bf2, k[i]), acc, false);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, q[i]), __builtin_bit_cast(h2, k[i]),
+                                   acc, false);
+  }
+  return acc;
+}
+
+template <int DT, int D, int NQ>
+__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
+  using Sh = DecShape<DT, D, NQ>;
+  constexpr int e = Sh::e, EPL = Sh::EPL, LPR = Sh::LPR, RPW = Sh::RPW, U = Sh::U;
+  constexpr int SR = Sh::SR, PAIRS = Sh::PAIRS, PPL = Sh::PPL;
+  static_assert(Sh::ok, "unsupported decode shape");
+
+  const int b = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int tile = blockIdx.x / a.nsplit;
+  const int split = blockIdx.x % a.nsplit;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int rslot = lane / LPR;
+  const int sub = lane % LPR;
+
+  __shared__ float s_part[kWaves][NQ * SR * LPR];   // [q][row][sub]
+  __shared__ float s_p[kWaves][PAIRS];              // [row][q]
+  __shared__ float s_corr[kWaves][NQ];
+  __shared__ float s_m[kWaves][NQ];
+  __shared__ float s_l[kWaves][NQ];
+  __shared__ float s_acc[kWaves][NQ][D];
+
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  const int nq_item = a.S * a.group;
+  const int q0 = tile * NQ;
+
+  if (!pl.ok) {
+    if (tid == 0 && tile == 0 && split == 0 && kvh == 0) flag_status(a.status, kStatusBadItem);
+    for (int idx = tid; idx < NQ * D; idx += kThreads) {
+      const int t = idx / D, d = idx % D;
+      const int qi = q0 + t;
+      if (qi >= nq_item) continue;
+      const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+      const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
+      if (a.nsplit == 1) {
+        if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = 0.0f;
+        else ((uint16_t*)a.out)[row * D + d] = 0;
+      } else {
+        a.opart[(row * a.nsplit + split) * D + d] = 0.0f;
+        if (d == 0) {
+          a.ml[(row * a.nsplit + split) * 2 + 0] = -INFINITY;
+          a.ml[(row * a.nsplit + split) * 2 + 1] = 0.0f;
+        }
+      }
+    }
+    return;
+  }
+
+  // Appends on drifting steps with a shared buffer (rows [Lb, Lb + S) are
+  // beyond every row attention reads).
+  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
+    constexpr int W16 = D * e / 16;
+    char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    for (int idx = tid; idx < a.S * W16; idx += kThreads) {
+      const int i = idx / W16, w = idx % W16;
+      const int64_t src = ((int64_t)(b * a.S + i) * a.Hkv + kvh) * D * e + w * 16;
+      const int64_t dst = (pl.Lb + i) * (int64_t)D * e + w * 16;
+      *(uint4*)(pk + dst) = *(const uint4*)((const char*)a.k + src);
+      *(uint4*)(pv + dst) = *(const uint4*)((const char*)a.v + src);
+    }
+  }
+
+  // Query tile: (position, head) pairs q0 .. q0 + NQ - 1, position-major.
+  const int i_first = q0 / a.group;
+  const int i_last = (min(q0 + NQ, nq_item) - 1) / a.group;
+  uint32_t qw[NQ][4];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    const int qi = min(q0 + t, nq_item - 1);
+    const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+    const uint4 v = *(const uint4*)((const char*)a.q +
+                                    ((((int64_t)b * a.S + i) * a.Hq + h) * D + sub * EPL) * e);
+    qw[t][0] = v.x; qw[t][1] = v.y; qw[t][2] = v.z; qw[t][3] = v.w;
+  }
+  // the query this lane scores in phase B (same for all its pairs)
+  const int my_q = lane % NQ;
+  const int my_qi = q0 + my_q;
+  const bool my_q_ok = my_qi < nq_item;
+  const int my_i = my_q_ok ? my_qi / a.group : i_last;
+  const int my_h = kvh * a.group + (my_q_ok ? my_qi % a.group : 0);
+  const int64_t my_pos = pl.P + my_i;
+
+  // Union key range of the tile, split evenly.
+  const int64_t p_first = pl.P + i_first;
+  const int64_t p_last = pl.P + i_last;
+  const int64_t lo = p_first - a.W + 1 > 0 ? p_first - a.W + 1 : 0;
+  const int64_t n = p_last - lo + 1;
+  const int64_t chunk = (n + a.nsplit - 1) / a.nsplit;
+  const int64_t kb = lo + split * chunk;
+  const int64_t ke = kb + chunk < p_last + 1 ? kb + chunk : p_last + 1;
+  const int nst = ke > kb ? (int)((ke - kb + SR - 1) / SR) : 0;
+
+  const int64_t base = pl.P - pl.Lb;
+  const char* cache_k = (const char*)a.past_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+  const char* cache_v = (const char*)a.past_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+  const int64_t new_stride = (int64_t)a.Hkv * D * e;   // bytes between new rows
+  const char* new_k = (const char*)a.k + (((int64_t)b * a.S) * a.Hkv + kvh) * D * e;
+  const char* new_v = (const char*)a.v + (((int64_t)b * a.S) * a.Hkv + kvh) * D * e;
+
+  const uint64_t ck_addr = (uint64_t)cache_k;
+  const uint64_t nk_addr = (uint64_t)new_k;
+  const uint64_t cv_minus_ck = (uint64_t)cache_v - ck_addr;
+  const uint64_t nv_minus_nk = (uint64_t)new_v - nk_addr;
+
+  const bool has_cap = a.softcap > 0.0f;
+  const float cap = a.softcap;
+  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
+  const bool has_bias = a.bias != nullptr;
+  const int64_t bias_row = has_bias
+      ? ((((a.bias_b ? (int64_t)b : 0) * (a.bias_h ? a.Hq : 1) + (a.bias_h ? my_h : 0)) * a.S + my_i) *
+         (int64_t)a.total)
+      : 0;
+
+  float m_run = -INFINITY;  // running max (log2 units) of query my_q; wave-uniform per query
+  float l_run = 0.0f;       // this lane's share of the running sum
+  float acc[NQ][EPL];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t)
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) acc[t][k] = 0.0f;
+
+  float* part = s_part[wave];
+  float* pbuf = s_p[wave];
+  float* cbuf = s_corr[wave];
+
+  auto load_stage = [&](int st, uint32_t (&kr)[U][4], uint32_t (&vr)[U][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = kb + (int64_t)st * SR + u * RPW + rslot;
+      const bool ok = st < nst && j < ke;
+      const bool in_cache = j < pl.P;
+      // branch-free mask select: a plain select between these uniform bases
+      // is turned into a private-memory lookup table by the compiler
+      const uint64_t msk = 0ull - (uint64_t)in_cache;
+      const uint64_t kaddr =
+          ((ck_addr + (uint64_t)(((j - base) * D + sub * EPL) * e)) & msk) |
+          ((nk_addr + (uint64_t)((j - pl.P) * new_stride + sub * EPL * e)) & ~msk);
+      const uint64_t vaddr = kaddr + ((cv_minus_ck & msk) | (nv_minus_nk & ~msk));
+      const char* kp = (const char*)kaddr;
+      const char* vp = (const char*)vaddr;
+      uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
+      if (ok) {
+        kk = *(const uint4*)kp;
+        vv = *(const uint4*)vp;
+      }
+      kr[u][0] = kk.x; kr[u][1] = kk.y; kr[u][2] = kk.z; kr[u][3] = kk.w;
+      vr[u][0] = vv.x; vr[u][1] = vv.y; vr[u][2] = vv.z; vr[u][3] = vv.w;
+    }
+  };
+
+  auto compute_stage = [&](int st, const uint32_t (&kr)[U][4], const uint32_t (&vr)[U][4]) __attribute__((always_inline)) {
+    // A. partial dots -> LDS [q][row][sub]
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = u * RPW + rslot;
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) part[(t * SR + row) * LPR + sub] = chunk_dot<DT>(qw[t], kr[u], 0.0f);
+    }
+    wave_lds_fence();
+    // B. scores, stage max, probabilities
+    float s[PPL];
+    float smax = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const int pid = lane + k * kWave;
+      const int row = pid / NQ;
+      const float* pp = part + (my_q * SR + row) * LPR;
+      float x = 0.0f;
+      if constexpr (LPR % 4 == 0) {
+#pragma unroll
+        for (int w = 0; w < LPR; w += 4) {
+          const float4 v4 = *(const float4*)(pp + w);
+          x += (v4.x + v4.y) + (v4.z + v4.w);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < LPR; ++w) x += pp[w];
+      }
+      x *= a.scale;
+      const int64_t j = kb + (int64_t)st * SR + row;
+      const bool vis = my_q_ok && j < ke && j <= my_pos && j > my_pos - a.W;
+      if (has_cap) {
+        const float y = x * inv_cap;
+        if constexpr (DT == kF32) {
+          x = cap * tanhf(y);
+        } else {
+          // tanh|y| = 1 - 2 / (e^{2|y|} + 1): one exp and one reciprocal;
+          // its absolute error (~1e-7) is far inside fp16/bf16 outputs
+          const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(
+                                     __builtin_amdgcn_exp2f(2.0f * kLog2e * fabsf(y)) + 1.0f);
+          x = cap * copysignf(t, y);
+        }
+      }
+      if (has_bias && vis) x += load_one<DT>(a.bias, bias_row + j);
+      s[k] = vis ? x * kLog2e : -INFINITY;
+      smax = fmaxf(smax, s[k]);
+    }
+    smax = allreduce_q<NQ, true>(smax);
+    const float m_new = fmaxf(m_run, smax);
+    const float corr = (m_run == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const float p = (s[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[k] - m_new);
+      pbuf[lane + k * kWave] = p;
+      psum += p;
+    }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (lane < NQ) cbuf[lane] = corr;
+    wave_lds_fence();
+    // C. rescale and accumulate V
+    float cr[NQ];
+#pragma unroll
+    for (int t = 0; t < NQ; ++t) cr[t] = cbuf[t];
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) acc[t][k] *= cr[t];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = u * RPW + rslot;
+      float pr[NQ];
+#pragma unroll
+      for (int t = 0; t < NQ; ++t) pr[t] = pbuf[row * NQ + t];
+      float vf[EPL];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) unpack_word<DT>(vr[u][w], &vf[w * (EPL / 4)]);
+#pragma unroll
+      for (int t = 0; t < NQ; ++t)
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) acc[t][k] = fmaf(pr[t], vf[k], acc[t][k]);
+    }
+    wave_lds_fence();
+  };
+
+  // Stages of this wave: wave, wave + 4, ...; two register sets in flight.
+  uint32_t k0[U][4], v0[U][4], k1[U][4], v1[U][4];
+  int st = wave;
+  load_stage(st, k0, v0);
+  while (st < nst) {
+    load_stage(st + kWaves, k1, v1);
+    compute_stage(st, k0, v0);
+    st += kWaves;
+    if (st >= nst) break;
+    load_stage(st + kWaves, k0, v0);
+    compute_stage(st, k1, v1);
+    st += kWaves;
+  }
+
+  // Wave result: acc summed over row slots, l over the lanes of each query.
+  const float l_tot = allreduce_q<NQ, false>(l_run);
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) acc[t][k] += __shfl_xor(acc[t][k], off, kWave);
+  if (rslot == 0) {
+#pragma unroll
+    for (int t = 0; t < NQ; ++t)
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) s_acc[wave][t][sub * EPL + k] = acc[t][k];
+  }
+  if (lane < NQ) {
+    s_m[wave][lane] = m_run;
+    s_l[wave][lane] = l_tot;
+  }
+  __syncthreads();
+
+  // Merge the waves; write the output or this split's partial.
+  for (int idx = tid; idx < NQ * D; idx += kThreads) {
+    const int t = idx / D, d = idx % D;
+    const int qi = q0 + t;
+    if (qi >= nq_item) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][t]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float c = (s_m[w][t] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][t] - M);
+      L += s_l[w][t] * c;
+      A += s_acc[w][t][d] * c;
+    }
+    const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+    const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
+    if (a.nsplit == 1) {
+      const float o = A / L;
+      if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = o;
+      else if constexpr (DT == kF16) ((_Float16*)a.out)[row * D + d] = (_Float16)o;
+      else ((uint16_t*)a.out)[row * D + d] = f32_to_bf16(o);
+    } else {
+      a.opart[(row * a.nsplit + split) * D + d] = A;
+      if (d == 0) {
+        a.ml[(row * a.nsplit + split) * 2 + 0] = M;
+        a.ml[(row * a.nsplit + split) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+template <int DT, int D, int NQ>
+hipError_t launch_nq(const AttnArgs& a, hipStream_t st) {
+  if constexpr (DecShape<DT, D, NQ>::ok) {
+    const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
+    attn_decode_kernel<DT, D, NQ><<<grid, kThreads, 0, st>>>(a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int DT, int D>
+bool shape_ok(int nq) {
+  switch (nq) {
+    case 2: return DecShape<DT, D, 2>::ok;
+    case 4: return DecShape<DT, D, 4>::ok;
+    case 8: return DecShape<DT, D, 8>::ok;
+    case 16: return DecShape<DT, D, 16>::ok;
+    default: return false;
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_d(int nq, const AttnArgs& a, hipStream_t st) {
+  switch (nq) {
+    case 2: return launch_nq<DT, D, 2>(a, st);
+    case 4: return launch_nq<DT, D, 4>(a, st);
+    case 8: return launch_nq<DT, D, 8>(a, st);
+    case 16: return launch_nq<DT, D, 16>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+bool ok_t(int D, int nq) {
+  switch (D) {
+    case 8: return shape_ok<DT, 8>(nq);
+    case 16: return shape_ok<DT, 16>(nq);
+    case 32: return shape_ok<DT, 32>(nq);
+    case 64: return shape_ok<DT, 64>(nq);
+    case 128: return shape_ok<DT, 128>(nq);
+    default: return false;
+  }
+}
+
+template <int DT>
+hipError_t launch_t(int D, int nq, const AttnArgs& a, hipStream_t st) {
+  switch (D) {
+    case 8: return launch_d<DT, 8>(nq, a, st);
+    case 16: return launch_d<DT, 16>(nq, a, st);
+    case 32: return launch_d<DT, 32>(nq, a, st);
+    case 64: return launch_d<DT, 64>(nq, a, st);
+    case 128: return launch_d<DT, 128>(nq, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool decode_kernel_supports(int dtype, int D, int nq) {
+  switch (dtype) {
+    case kF32: return ok_t<kF32>(D, nq);
+    case kF16: return ok_t<kF16>(D, nq);
+    case kBF16: return ok_t<kBF16>(D, nq);
+    default: return false;
+  }
+}
+
+hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a, hipStream_t st) {
+  switch (dtype) {
+    case kF32: return launch_t<kF32>(D, nq, a, st);
+    case kF16: return launch_t<kF16>(D, nq, a, st);
+    case kBF16: return launch_t<kBF16>(D, nq, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swgqa

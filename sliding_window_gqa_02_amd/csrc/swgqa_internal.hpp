@@ -46,6 +46,11 @@ struct CopyArgs {
 // Split-K attention for short steps; returns hipSuccess or the launch error.
 hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
                              hipStream_t stream);
+// Staged decode kernel (swgqa_attn_decode.hip): supports row sizes up to
+// 256 bytes and NQ * (16 / element bytes) <= 64.
+bool decode_kernel_supports(int dtype, int D, int nq);
+hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
+                              hipStream_t stream);
 hipError_t launch_combine(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_writeback(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,

@@ -22,13 +22,30 @@ def say(*a):
     sys.stdout.flush()
 
 
+def format_ulp(x: np.ndarray, dtype) -> np.ndarray:
+    """Spacing of the output format at |x| (one unit in the last place)."""
+    mant = {synth.F32: 23, synth.F16: 10, synth.BF16: 7}[dtype]
+    emin = {synth.F32: -126, synth.F16: -14, synth.BF16: -126}[dtype]
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, emin)
+    return np.ldexp(1.0, (e - mant).astype(np.int64))
+
+
 def assert_outputs_close(got, ref, dtype, what=""):
+    """|gpu - oracle| <= tol * max(1, |oracle|), or the two stored values are
+    neighbours in the output format: each side rounds its own result (fp32 on
+    the GPU, fp64 in the oracle) to nearest-even, and where the exact value
+    sits near a rounding boundary the two land one ulp apart -- for bf16 one
+    ulp is up to 2^-7 relative, more than the 2e-3 bound itself."""
     g = as_f64(got, dtype)
     r = as_f64(ref, dtype)
     assert not np.isnan(g).any(), f"{what}: NaN in GPU output"
-    err = np.abs(g - r) / np.maximum(1.0, np.abs(r))
-    worst = float(err.max()) if err.size else 0.0
-    assert worst <= TOL[dtype], f"{what}: max scaled error {worst:.3g} > {TOL[dtype]}"
+    diff = np.abs(g - r)
+    err = diff / np.maximum(1.0, np.abs(r))
+    ok = (err <= TOL[dtype]) | (diff <= format_ulp(np.maximum(np.abs(g), np.abs(r)), dtype))
+    worst = float(np.where(ok, np.minimum(err, TOL[dtype]), err).max()) if err.size else 0.0
+    assert ok.all(), f"{what}: max scaled error {float(err[~ok].max()):.3g} > {TOL[dtype]} and > 1 ulp"
     return worst
 
 
