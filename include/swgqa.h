@@ -102,13 +102,15 @@ typedef struct {
   int64_t T, P, Lb, La, kept, shift, first, hazard;
 } swgqa_plan_entry;
 
-/* Bytes of device workspace swgqa_forward needs for these parameters (>= 256;
- * the first 256 bytes hold the status word).  0 if the parameters are
- * invalid.  Pure host function. */
+/* Bytes of device workspace swgqa_forward needs for these parameters: the
+ * status word in bytes [0, 256), then key-split partials (scratch).  0 if the
+ * parameters are invalid.  Pure host function.  A workspace of at least this
+ * size serves any parameter set whose own size is not larger. */
 size_t swgqa_workspace_size(const swgqa_params* params);
 
-/* Clears the workspace status word (enqueued on `stream`; a small kernel,
- * no memset node).  Call once on a fresh workspace. */
+/* Zeroes the first workspace_bytes of the workspace, status word included
+ * (enqueued on `stream`; a small kernel, no memset node).  Call once on a
+ * fresh workspace. */
 swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes,
                                   void* stream);
 

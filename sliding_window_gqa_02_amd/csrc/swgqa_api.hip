@@ -15,8 +15,19 @@ namespace {
 using namespace swgqa;
 
 constexpr size_t kHeaderBytes = 256;  // status word + reserved
-constexpr int kTargetWorkgroups = 2048;
+#ifndef SWGQA_TARGET_WORKGROUPS
+#define SWGQA_TARGET_WORKGROUPS 2048
+#endif
+#ifndef SWGQA_WHOLE_SLICE_MIN_TILES
+#define SWGQA_WHOLE_SLICE_MIN_TILES 128
+#endif
+#ifndef SWGQA_WHOLE_SLICE_MAX_KEYS
+#define SWGQA_WHOLE_SLICE_MAX_KEYS 256
+#endif
+constexpr int kTargetWorkgroups = SWGQA_TARGET_WORKGROUPS;
 constexpr int kMinKeysPerSplit = 32;
+constexpr int64_t kWholeSliceMinTiles = SWGQA_WHOLE_SLICE_MIN_TILES;
+constexpr int64_t kWholeSliceMaxKeys = SWGQA_WHOLE_SLICE_MAX_KEYS;
 
 size_t elem_bytes(int dt) { return dt == SWGQA_F32 ? 4 : 2; }
 
@@ -41,6 +52,7 @@ struct SplitPlan {
   int nq;       // query tile width ((position, head) pairs)
   int ntiles;   // tiles per (item, KV head)
   int nsplit;   // key splits per tile
+  int waves;    // waves per workgroup (staged kernel)
 };
 
 SplitPlan plan_split(const swgqa_params* p) {
@@ -66,6 +78,15 @@ SplitPlan plan_split(const swgqa_params* p) {
   int64_t nkeys = (int64_t)p->local_window_size + span - 1;
   if (nkeys > p->total_sequence_length) nkeys = p->total_sequence_length;
   const int64_t base = (int64_t)p->batch_size * p->kv_num_heads * s.ntiles;
+  s.waves = 4;
+  if (s.staged && (base >= kWholeSliceMinTiles || nkeys <= kWholeSliceMaxKeys)) {
+    // enough tiles to fill the chip with one 8-wave workgroup each, or a
+    // window short enough for one workgroup: no split, no merge pass, and
+    // the in-place write-back stays inside the workgroup
+    s.nsplit = 1;
+    s.waves = 8;
+    return s;
+  }
   int64_t ns = base > 0 ? (kTargetWorkgroups + base - 1) / base : 1;
   const int64_t ns_max = (nkeys + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
   if (ns > ns_max) ns = ns_max;
@@ -81,6 +102,7 @@ size_t partial_bytes(const swgqa_params* p, const SplitPlan& s) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 
 bool ranges_partially_overlap(const void* a, const void* b, size_t n) {
   const char* x = (const char*)a;
@@ -101,7 +123,8 @@ size_t swgqa_workspace_size(const swgqa_params* p) {
 
 swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || workspace_bytes < kHeaderBytes) return SWGQA_ERR_ARG;
-  if (launch_clear_status((uint32_t*)workspace, (hipStream_t)stream) != hipSuccess)
+  if (launch_zero_words((uint32_t*)workspace, workspace_bytes / 4, (hipStream_t)stream) !=
+      hipSuccess)
     return SWGQA_ERR_HIP;
   return SWGQA_OK;
 }
@@ -167,12 +190,17 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.softcap = p->softcap;
   a.bias_b = p->bias_dim0_is_batch ? 1 : 0;
   a.bias_h = p->bias_dim1_is_heads ? 1 : 0;
+  a.fuse_writeback = (shared && s.ntiles == 1 && s.nsplit == 1) ? 1 : 0;
+  a.waves = s.waves;
 
   const hipError_t ea = s.staged ? launch_attn_decode(p->dtype, p->head_size, s.nq, a, st)
                                  : launch_attn_split(p->dtype, p->head_size, s.nq, a, st);
   if (ea != hipSuccess) return SWGQA_ERR_HIP;
   if (s.nsplit > 1 && launch_combine(p->dtype, p->head_size, a, st) != hipSuccess)
     return SWGQA_ERR_HIP;
+  // The write-back: done inside the attention kernel when one workgroup owns
+  // each slice in place; otherwise a kernel of its own, after every read.
+  if (a.fuse_writeback) return SWGQA_OK;
 
   CopyArgs c;
   c.past_k = past_key;
@@ -190,7 +218,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   c.total = p->total_sequence_length;
   c.D = p->head_size;
   c.elem_bytes = (int32_t)e;
-  c.skip_drifting = shared ? 1 : 0;
+  c.skip_drifting = shared ? 1 : 0;  // drifting appends were done by attention
   if (launch_writeback(c, st) != hipSuccess) return SWGQA_ERR_HIP;
   return SWGQA_OK;
 }
@@ -226,7 +254,7 @@ swgqa_status swgqa_device_status(const void* workspace, int clear, void* stream)
     return SWGQA_ERR_HIP;
   if (hipStreamSynchronize(st) != hipSuccess) return SWGQA_ERR_HIP;
   if (clear) {
-    if (launch_clear_status((uint32_t*)workspace, st) != hipSuccess) return SWGQA_ERR_HIP;
+    if (launch_zero_words((uint32_t*)workspace, 1, st) != hipSuccess) return SWGQA_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return SWGQA_ERR_HIP;
   }
   return (word & kStatusBadItem) ? SWGQA_ERR_DEVICE_INPUT : SWGQA_OK;

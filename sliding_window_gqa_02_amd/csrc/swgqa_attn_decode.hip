@@ -24,6 +24,7 @@
 // need compiler ordering fences, not barriers.
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
+#include "swgqa_tail.hpp"
 
 #include <math.h>
 
@@ -31,8 +32,6 @@ namespace swgqa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DT, int D, int NQ>
@@ -101,8 +100,9 @@ __device__ __forceinline__ float chunk_dot(const uint32_t* q, const uint32_t* k,
   return acc;
 }
 
-template <int DT, int D, int NQ>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
+template <int DT, int D, int NQ, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a) {
+  constexpr int kThreads = kWaves * kWave;
   using Sh = DecShape<DT, D, NQ>;
   constexpr int e = Sh::e, EPL = Sh::EPL, LPR = Sh::LPR, RPW = Sh::RPW, U = Sh::U;
   constexpr int SR = Sh::SR, PAIRS = Sh::PAIRS, PPL = Sh::PPL;
@@ -404,13 +404,17 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a) {
       }
     }
   }
+  slice_tail<DT>(a, pl, b, kvh, D);
 }
 
 template <int DT, int D, int NQ>
 hipError_t launch_nq(const AttnArgs& a, hipStream_t st) {
   if constexpr (DecShape<DT, D, NQ>::ok) {
     const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
-    attn_decode_kernel<DT, D, NQ><<<grid, kThreads, 0, st>>>(a);
+    if (a.waves == 8)
+      attn_decode_kernel<DT, D, NQ, 8><<<grid, 8 * kWave, 0, st>>>(a);
+    else
+      attn_decode_kernel<DT, D, NQ, 4><<<grid, 4 * kWave, 0, st>>>(a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

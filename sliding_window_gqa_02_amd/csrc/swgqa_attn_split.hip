@@ -20,9 +20,10 @@
 // slot keeps its own online-softmax state (max, sum, accumulator); row slots
 // and waves are merged once at the end.  With one split the workgroup writes
 // the output; otherwise it writes (max, sum, accumulator) partials that
-// swgqa_combine merges.
+// swgqa_combine.hip merges.
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
+#include "swgqa_tail.hpp"
 
 #include <math.h>
 
@@ -295,32 +296,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
       }
     }
   }
-}
-
-// Merges split partials: one workgroup of D threads per (item, position, head).
-template <int DT>
-__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int D) {
-  const int64_t row = blockIdx.x;               // ((b * S + i) * Hq + h)
-  const int b = (int)(row / ((int64_t)a.S * a.Hq));
-  const int d = threadIdx.x;
-  if (d >= D) return;
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
-  float o = 0.0f;
-  if (pl.ok) {
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ml[(row * a.nsplit + s) * 2]);
-    float L = 0.0f, A = 0.0f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.ml[(row * a.nsplit + s) * 2];
-      const float c = (ms == -INFINITY) ? 0.0f : exp2f(ms - M);
-      L += a.ml[(row * a.nsplit + s) * 2 + 1] * c;
-      A += a.opart[(row * a.nsplit + s) * D + d] * c;
-    }
-    o = A / L;
-  }
-  if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = o;
-  else if constexpr (DT == kF16) ((_Float16*)a.out)[row * D + d] = (_Float16)o;
-  else ((uint16_t*)a.out)[row * D + d] = f32_to_bf16(o);
+  slice_tail<DT>(a, pl, b, kvh, D);
 }
 
 template <int DT, int D, int NQ>
@@ -372,18 +348,6 @@ hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
     case kBF16: return launch_split_t<kBF16>(D, nq, a, st);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_combine(int dtype, int D, const AttnArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)a.B * a.S * a.Hq));
-  const dim3 block(D < 64 ? 64 : D);
-  switch (dtype) {
-    case kF32: combine_kernel<kF32><<<grid, block, 0, st>>>(a, D); break;
-    case kF16: combine_kernel<kF16><<<grid, block, 0, st>>>(a, D); break;
-    case kBF16: combine_kernel<kBF16><<<grid, block, 0, st>>>(a, D); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 }  // namespace swgqa

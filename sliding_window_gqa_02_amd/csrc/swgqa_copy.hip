@@ -110,8 +110,10 @@ __global__ void plan_kernel(const int32_t* seqlens, int32_t B, int32_t S,
   o[7] = pl.kept < need ? 1 : 0;
 }
 
-__global__ void clear_status_kernel(uint32_t* status) {
-  status[threadIdx.x] = 0u;
+__global__ void zero_words_kernel(uint32_t* words, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    words[i] = 0u;
 }
 
 }  // namespace
@@ -129,8 +131,11 @@ hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
   return hipGetLastError();
 }
 
-hipError_t launch_clear_status(uint32_t* status, hipStream_t st) {
-  clear_status_kernel<<<1, 64, 0, st>>>(status);
+hipError_t launch_zero_words(uint32_t* words, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  zero_words_kernel<<<(unsigned)blocks, 256, 0, st>>>(words, n);
   return hipGetLastError();
 }
 

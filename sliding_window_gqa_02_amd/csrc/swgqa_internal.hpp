@@ -28,6 +28,8 @@ struct AttnArgs {
   int32_t ntiles, nsplit;
   float scale, softcap;
   int32_t bias_b, bias_h;
+  int32_t fuse_writeback;  // shared buffer and one workgroup per slice
+  int32_t waves;           // waves per workgroup of the staged kernel
 };
 
 struct CopyArgs {
@@ -46,16 +48,16 @@ struct CopyArgs {
 // Split-K attention for short steps; returns hipSuccess or the launch error.
 hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
                              hipStream_t stream);
+hipError_t launch_combine(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 // Staged decode kernel (swgqa_attn_decode.hip): supports row sizes up to
 // 256 bytes and NQ * (16 / element bytes) <= 64.
 bool decode_kernel_supports(int dtype, int D, int nq);
 hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
                               hipStream_t stream);
-hipError_t launch_combine(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_writeback(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
                        int32_t W, int32_t total, int64_t* out, hipStream_t stream);
-hipError_t launch_clear_status(uint32_t* status, hipStream_t stream);
+hipError_t launch_zero_words(uint32_t* words, size_t n, hipStream_t stream);
 
 // Supported head sizes of every kernel.
 bool head_size_supported(int D);
