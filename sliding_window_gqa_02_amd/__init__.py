@@ -64,6 +64,13 @@ def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own HIP runtime under the same soname; importing it
+    # first makes this library bind to that runtime, so that torch's streams
+    # and allocations are valid handles here.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         from . import build as _build
         _build.build()

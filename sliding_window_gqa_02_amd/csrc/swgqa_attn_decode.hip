@@ -34,6 +34,11 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Stages of K/V loads in flight per wave (2: double, 3: triple buffering).
+#ifndef SWGQA_DEC_DEPTH
+#define SWGQA_DEC_DEPTH 3
+#endif
+
 template <int DT, int D, int NQ>
 struct DecShape {
   static constexpr int e = Elem<DT>::bytes;
@@ -100,7 +105,7 @@ __device__ __forceinline__ float chunk_dot(const uint32_t* q, const uint32_t* k,
   return acc;
 }
 
-template <int DT, int D, int NQ, int kWaves>
+template <int DT, int D, int NQ, int kWaves, int DEPTH>
 __global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a) {
   constexpr int kThreads = kWaves * kWave;
   using Sh = DecShape<DT, D, NQ>;
@@ -340,18 +345,37 @@ __global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a)
     wave_lds_fence();
   };
 
-  // Stages of this wave: wave, wave + 4, ...; two register sets in flight.
+  // Stages of this wave: wave, wave + kWaves, ...; the loads of the next
+  // DEPTH - 1 stages are in flight while one stage is computed.
   uint32_t k0[U][4], v0[U][4], k1[U][4], v1[U][4];
   int st = wave;
   load_stage(st, k0, v0);
-  while (st < nst) {
+  if constexpr (DEPTH == 3) {
+    uint32_t k2[U][4], v2[U][4];
     load_stage(st + kWaves, k1, v1);
-    compute_stage(st, k0, v0);
-    st += kWaves;
-    if (st >= nst) break;
-    load_stage(st + kWaves, k0, v0);
-    compute_stage(st, k1, v1);
-    st += kWaves;
+    while (st < nst) {
+      load_stage(st + 2 * kWaves, k2, v2);
+      compute_stage(st, k0, v0);
+      st += kWaves;
+      if (st >= nst) break;
+      load_stage(st + 2 * kWaves, k0, v0);
+      compute_stage(st, k1, v1);
+      st += kWaves;
+      if (st >= nst) break;
+      load_stage(st + 2 * kWaves, k1, v1);
+      compute_stage(st, k2, v2);
+      st += kWaves;
+    }
+  } else {
+    while (st < nst) {
+      load_stage(st + kWaves, k1, v1);
+      compute_stage(st, k0, v0);
+      st += kWaves;
+      if (st >= nst) break;
+      load_stage(st + kWaves, k0, v0);
+      compute_stage(st, k1, v1);
+      st += kWaves;
+    }
   }
 
   // Wave result: acc summed over row slots, l over the lanes of each query.
@@ -412,9 +436,9 @@ hipError_t launch_nq(const AttnArgs& a, hipStream_t st) {
   if constexpr (DecShape<DT, D, NQ>::ok) {
     const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
     if (a.waves == 8)
-      attn_decode_kernel<DT, D, NQ, 8><<<grid, 8 * kWave, 0, st>>>(a);
+      attn_decode_kernel<DT, D, NQ, 8, SWGQA_DEC_DEPTH><<<grid, 8 * kWave, 0, st>>>(a);
     else
-      attn_decode_kernel<DT, D, NQ, 4><<<grid, 4 * kWave, 0, st>>>(a);
+      attn_decode_kernel<DT, D, NQ, 4, SWGQA_DEC_DEPTH><<<grid, 4 * kWave, 0, st>>>(a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

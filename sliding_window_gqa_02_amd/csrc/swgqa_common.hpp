@@ -18,6 +18,10 @@ enum : uint32_t { kStatusBadItem = 1u };
 
 constexpr int kWave = 64;
 
+// Native 16-byte vector (HIP's uint4 is a struct, and arrays of it are not
+// promoted to registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
 // Resident-range planner.  "Specify GroupQueryAttention windowed KV cache
 // layout contract" (onnxruntime PR #32419), Description: G = C - W + 1,

@@ -43,8 +43,8 @@ __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
   const int64_t rowb = (int64_t)a.D * a.elem_bytes;
   const int64_t w16 = rowb / 16;  // 16-byte words per row
   const int64_t slice = ((int64_t)b * a.Hkv + kvh) * a.C * rowb;
-  const uint4* src = (const uint4*)((const char*)past + slice);
-  uint4* dst = (uint4*)((char*)present + slice);
+  const u32x4* src = (const u32x4*)((const char*)past + slice);
+  u32x4* dst = (u32x4*)((char*)present + slice);
   const int tid = threadIdx.x;
 
   // 1. Surviving old rows: [shift, shift + kept) -> [0, kept).
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
       for (int64_t r0 = 0; r0 < pl.kept; r0 += pass) {
         const int64_t nr = pl.kept - r0 < pass ? pl.kept - r0 : pass;
         const int64_t nw = nr * w16;
-        uint4 buf[kCopyUnroll];
+        u32x4 buf[kCopyUnroll];
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
           const int64_t idx = tid + (int64_t)u * kCopyThreads;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
   for (int64_t idx = tid; idx < nw; idx += kCopyThreads) {
     const int64_t i = i0 + idx / w16;
     const int64_t w = idx % w16;
-    const uint4* s = (const uint4*)(fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb);
+    const u32x4* s = (const u32x4*)(fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb);
     dst[(pl.kept + i) * w16 + w] = s[w];
   }
 }

@@ -21,18 +21,19 @@ constexpr int kMoveUnroll = 16;  // 16-byte words per thread per pass
 // In-place move of one cache slice, rows [shift, shift + kept) -> [0, kept),
 // in passes of at most `shift` rows: a pass's destination rows were sources
 // only of earlier passes, whose loads completed before the barrier.
-__device__ __forceinline__ void move_rows_in_place(uint4* slice, int64_t w16, int64_t shift,
+__device__ __forceinline__ void move_rows_in_place(u32x4* slice, int64_t w16, int64_t shift,
                                                    int64_t kept, int tid, int nthr) {
   const int64_t cap_rows = (int64_t)nthr * kMoveUnroll / w16;
   const int64_t pass = shift < cap_rows ? shift : (cap_rows > 0 ? cap_rows : 1);
   for (int64_t r0 = 0; r0 < kept; r0 += pass) {
     const int64_t nr = kept - r0 < pass ? kept - r0 : pass;
     const int64_t nw = nr * w16;
-    uint4 buf[kMoveUnroll];
+    // all loads of the pass first (clamped to a valid word), then the stores
+    u32x4 buf[kMoveUnroll];
 #pragma unroll
     for (int u = 0; u < kMoveUnroll; ++u) {
       const int64_t idx = tid + (int64_t)u * nthr;
-      if (idx < nw) buf[u] = slice[(shift + r0) * w16 + idx];
+      buf[u] = slice[(shift + r0) * w16 + (idx < nw ? idx : nw - 1)];
     }
 #pragma unroll
     for (int u = 0; u < kMoveUnroll; ++u) {
@@ -53,19 +54,19 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
   const int nthr = blockDim.x;
   if (pl.shift > 0) {
     if (pl.kept > 0) {
-      move_rows_in_place((uint4*)((char*)a.present_k + off), w16, pl.shift, pl.kept, tid, nthr);
-      move_rows_in_place((uint4*)((char*)a.present_v + off), w16, pl.shift, pl.kept, tid, nthr);
+      move_rows_in_place((u32x4*)((char*)a.present_k + off), w16, pl.shift, pl.kept, tid, nthr);
+      move_rows_in_place((u32x4*)((char*)a.present_v + off), w16, pl.shift, pl.kept, tid, nthr);
     }
     // new rows after the move (they may land on rows the move read)
     const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
     const int64_t nw = (a.S - i0) * w16;
-    uint4* dk = (uint4*)((char*)a.present_k + off);
-    uint4* dv = (uint4*)((char*)a.present_v + off);
+    u32x4* dk = (u32x4*)((char*)a.present_k + off);
+    u32x4* dv = (u32x4*)((char*)a.present_v + off);
     for (int64_t idx = tid; idx < nw; idx += nthr) {
       const int64_t i = i0 + idx / w16, w = idx % w16;
       const int64_t src = (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb;
-      dk[(pl.kept + i) * w16 + w] = ((const uint4*)((const char*)a.k + src))[w];
-      dv[(pl.kept + i) * w16 + w] = ((const uint4*)((const char*)a.v + src))[w];
+      dk[(pl.kept + i) * w16 + w] = ((const u32x4*)((const char*)a.k + src))[w];
+      dv[(pl.kept + i) * w16 + w] = ((const u32x4*)((const char*)a.v + src))[w];
     }
   }
 }
