@@ -26,6 +26,8 @@ constexpr size_t kHeaderBytes = 256;  // status word + reserved
 #endif
 constexpr int kTargetWorkgroups = SWGQA_TARGET_WORKGROUPS;
 constexpr int kMinKeysPerSplit = 32;
+constexpr int kChunkMinTokens = 16;       // steps of at least this many tokens use MFMA
+constexpr int64_t kChunkMinWorkgroups = 256;
 constexpr int64_t kWholeSliceMinTiles = SWGQA_WHOLE_SLICE_MIN_TILES;
 constexpr int64_t kWholeSliceMaxKeys = SWGQA_WHOLE_SLICE_MAX_KEYS;
 
@@ -47,8 +49,10 @@ swgqa_status validate(const swgqa_params* p) {
 
 // Launch geometry of the attention kernels, a pure function of the
 // parameters.
+enum class Kind { kSplit, kDecode, kChunk };
+
 struct SplitPlan {
-  bool staged;  // the staged decode kernel (else the generic split kernel)
+  Kind kind;    // generic split / staged decode / MFMA chunk kernel
   int nq;       // query tile width ((position, head) pairs)
   int ntiles;   // tiles per (item, KV head)
   int nsplit;   // key splits per tile
@@ -59,13 +63,29 @@ SplitPlan plan_split(const swgqa_params* p) {
   SplitPlan s;
   const int group = p->num_heads / p->kv_num_heads;
   const int per_kv = p->sequence_length * group;  // queries per (item, KV head)
+  s.waves = 4;
+  if (p->sequence_length >= kChunkMinTokens && chunk_kernel_supports(p->dtype, p->head_size)) {
+    // multi-token step on the matrix cores
+    s.kind = Kind::kChunk;
+    s.nq = chunk_rows_per_workgroup();
+    s.ntiles = (per_kv + s.nq - 1) / s.nq;
+    const int64_t span = (s.nq + group - 1) / group + 1;
+    int64_t nkeys = (int64_t)p->local_window_size + span - 1;
+    if (nkeys > p->total_sequence_length) nkeys = p->total_sequence_length;
+    const int64_t base = (int64_t)p->batch_size * p->kv_num_heads * s.ntiles;
+    int64_t ns = base >= kChunkMinWorkgroups ? 1 : (kChunkMinWorkgroups + base - 1) / base;
+    const int64_t ns_max = (nkeys + 4 * chunk_keys_per_block() - 1) / (4 * chunk_keys_per_block());
+    if (ns > ns_max) ns = ns_max;
+    s.nsplit = ns < 1 ? 1 : (int)ns;
+    return s;
+  }
   int nq = 2;
   while (nq < per_kv && nq < 16) nq *= 2;
   // the staged kernel keeps NQ x (elements per 16 bytes) accumulators per lane
   int nq_staged = nq;
   while (nq_staged > 2 && nq_staged * (p->dtype == SWGQA_F32 ? 4 : 8) > 64) nq_staged /= 2;
-  s.staged = decode_kernel_supports(p->dtype, p->head_size, nq_staged);
-  if (s.staged) {
+  s.kind = decode_kernel_supports(p->dtype, p->head_size, nq_staged) ? Kind::kDecode : Kind::kSplit;
+  if (s.kind == Kind::kDecode) {
     nq = nq_staged;
   } else {
     while (nq > 2 && nq * p->head_size > kSplitMaxTileElems) nq /= 2;
@@ -78,8 +98,7 @@ SplitPlan plan_split(const swgqa_params* p) {
   int64_t nkeys = (int64_t)p->local_window_size + span - 1;
   if (nkeys > p->total_sequence_length) nkeys = p->total_sequence_length;
   const int64_t base = (int64_t)p->batch_size * p->kv_num_heads * s.ntiles;
-  s.waves = 4;
-  if (s.staged && (base >= kWholeSliceMinTiles || nkeys <= kWholeSliceMaxKeys)) {
+  if (s.kind == Kind::kDecode && (base >= kWholeSliceMinTiles || nkeys <= kWholeSliceMaxKeys)) {
     // enough tiles to fill the chip with one 8-wave workgroup each, or a
     // window short enough for one workgroup: no split, no merge pass, and
     // the in-place write-back stays inside the workgroup
@@ -193,8 +212,10 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.fuse_writeback = (shared && s.ntiles == 1 && s.nsplit == 1) ? 1 : 0;
   a.waves = s.waves;
 
-  const hipError_t ea = s.staged ? launch_attn_decode(p->dtype, p->head_size, s.nq, a, st)
-                                 : launch_attn_split(p->dtype, p->head_size, s.nq, a, st);
+  const hipError_t ea =
+      s.kind == Kind::kChunk    ? launch_attn_chunk(p->dtype, p->head_size, a, st)
+      : s.kind == Kind::kDecode ? launch_attn_decode(p->dtype, p->head_size, s.nq, a, st)
+                                : launch_attn_split(p->dtype, p->head_size, s.nq, a, st);
   if (ea != hipSuccess) return SWGQA_ERR_HIP;
   if (s.nsplit > 1 && launch_combine(p->dtype, p->head_size, a, st) != hipSuccess)
     return SWGQA_ERR_HIP;

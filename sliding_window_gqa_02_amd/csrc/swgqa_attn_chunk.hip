@@ -1,0 +1,463 @@
+// swgqa_attn_chunk.hip -- grouped-query attention for multi-token steps
+// (prefill, chunked prefill, S >= 16) over a windowed KV cache, on the CDNA4
+// matrix cores.
+//
+// Same contract as the decode kernels: query i of item b at absolute
+// position p = P + i attends to keys p - W < j <= p of [resident rows | S
+// new rows] ("Specify GroupQueryAttention windowed KV cache layout
+// contract", Description; causal rule of "Fix CPU Attention causal mask
+// ..."), keys below P read from cache row j - (P - Lb), the rest straight
+// from the new rows, so a step that evicts history it still reads needs no
+// staging copy ("[CPU] Add windowed kv cache for GQA", staging).
+//
+// A workgroup (4 waves) owns 64 consecutive (position, head) query rows of
+// one KV head's group and walks the key band [p_first - W + 1, p_last] in
+// blocks of 32 keys staged in LDS -- every K/V row staged is used by all the
+// heads of the group.  Per block each wave (16 query rows):
+//   S^T = K . Q^T   16 keys x 16 queries per MFMA (Q^T is the B operand, held
+//                   in registers for the whole band);
+//   softmax         each lane owns one query column, so max / sum need only
+//                   in-lane work plus two cross-lane steps, and every
+//                   (query, key) score is transformed exactly once;
+//   O^T += V^T . P^T  the S^T accumulator registers are the P^T operand as
+//                   they stand (keys on the reduction axis), and O^T keeps
+//                   the same one-query-per-lane-column layout as the softmax
+//                   state, so rescaling needs no shuffles.
+// fp32 uses v_mfma_f32_16x16x4_f32 (full fp32 products); fp16 / bf16 use the
+// 16x16x16 forms.  P enters the PV product rounded to fp16 (the normaliser
+// sums the rounded P, so the result is an exact weighted mean of V), or for
+// bf16 as a hi + lo pair of bf16 values (8 significant bits alone would move
+// a mean of few keys by ~2^-9).
+// The next block's K/V are loaded into registers while the current block is
+// computed.
+#include "swgqa_common.hpp"
+#include "swgqa_internal.hpp"
+#include "swgqa_tail.hpp"
+
+#include <math.h>
+
+namespace swgqa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int BQ = 64;   // query rows per workgroup
+constexpr int BN = 32;   // keys per block
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+template <int DT, int D>
+struct ChunkShape {
+  static constexpr int e = Elem<DT>::bytes;
+  // LDS row strides (elements), chosen so the MFMA operand reads of 16 lanes
+  // on 16 different rows fall in distinct banks
+  static constexpr int KS = (DT == kF32) ? D + 2 : D + 8;   // K rows: [key][d]
+  static constexpr int VS = (DT == kF32) ? D + 4 : BN + 4;  // fp32 V [key][d]; 16-bit V^T [d][key]
+  static constexpr int KELEMS = BN * KS;
+  static constexpr int VELEMS = (DT == kF32) ? BN * VS : D * VS;
+  static constexpr int CHUNKS = BN * D * e / 16;           // 16-byte chunks per block per tensor
+  static constexpr int CPT = (CHUNKS + kThreads - 1) / kThreads;  // per thread
+  static constexpr int DSTEPS = (DT == kF32) ? D / 4 : D / 16;  // S^T MFMA steps
+  static constexpr int DT16 = D / 16;                      // O^T tiles
+  static constexpr bool ok = D >= 16 && D % 16 == 0 && D * e <= 512;
+};
+
+template <int DT> struct LdsT { using T = float; };
+template <> struct LdsT<kF16> { using T = uint16_t; };
+template <> struct LdsT<kBF16> { using T = uint16_t; };
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  union { _Float16 h; uint16_t u; } c;
+  c.h = (_Float16)x;
+  return c.u;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
+  using Sh = ChunkShape<DT, D>;
+  using LT = typename LdsT<DT>::T;
+  constexpr int e = Sh::e, KS = Sh::KS, VS = Sh::VS, CPT = Sh::CPT, DSTEPS = Sh::DSTEPS;
+  constexpr int DT16 = Sh::DT16;
+  constexpr int CPR = D * e / 16;  // 16-byte chunks per row
+  static_assert(Sh::ok, "unsupported chunk shape");
+
+  __shared__ LT sK[Sh::KELEMS];
+  __shared__ LT sV[Sh::VELEMS];
+
+  const int b = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int tile = blockIdx.x / a.nsplit;
+  const int split = blockIdx.x % a.nsplit;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int lq = lane % 16;   // query column of this lane
+  const int lg = lane / 16;   // lane group (0..3)
+
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  const int nq_item = a.S * a.group;
+  const int q0 = tile * BQ;
+
+  if (!pl.ok) {
+    if (tid == 0 && tile == 0 && split == 0 && kvh == 0) flag_status(a.status, kStatusBadItem);
+    for (int idx = tid; idx < BQ * D; idx += kThreads) {
+      const int t = idx / D, d = idx % D;
+      const int qi = q0 + t;
+      if (qi >= nq_item) continue;
+      const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+      const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
+      if (a.nsplit == 1) {
+        if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = 0.0f;
+        else ((uint16_t*)a.out)[row * D + d] = 0;
+      } else {
+        a.opart[(row * a.nsplit + split) * D + d] = 0.0f;
+        if (d == 0) {
+          a.ml[(row * a.nsplit + split) * 2 + 0] = -INFINITY;
+          a.ml[(row * a.nsplit + split) * 2 + 1] = 0.0f;
+        }
+      }
+    }
+    return;
+  }
+
+  // Appends on drifting steps with a shared buffer (rows [Lb, Lb + S) are
+  // beyond every cache row attention reads).
+  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
+    char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    for (int idx = tid; idx < a.S * CPR; idx += kThreads) {
+      const int i = idx / CPR, w = idx % CPR;
+      const int64_t src = ((int64_t)(b * a.S + i) * a.Hkv + kvh) * D * e + w * 16;
+      const int64_t dst = (pl.Lb + i) * (int64_t)D * e + w * 16;
+      *(u32x4*)(pk + dst) = *(const u32x4*)((const char*)a.k + src);
+      *(u32x4*)(pv + dst) = *(const u32x4*)((const char*)a.v + src);
+    }
+  }
+
+  // This lane's query (column lq of wave's 16 rows).
+  const int my_qi = q0 + wave * 16 + lq;
+  const bool my_ok = my_qi < nq_item;
+  const int my_qc = my_ok ? my_qi : nq_item - 1;
+  const int my_i = my_qc / a.group;
+  const int my_h = kvh * a.group + my_qc % a.group;
+  const int64_t my_pos = pl.P + my_i;
+  const int i_first = q0 / a.group;
+  const int i_last = (min(q0 + BQ, nq_item) - 1) / a.group;
+
+  // Q^T operand: fp32 step s holds Q[q][4s + lg]; 16-bit step s holds
+  // Q[q][16s + 4lg .. +3].
+  const char* qrow = (const char*)a.q + ((((int64_t)b * a.S + my_i) * a.Hq + my_h) * D) * e;
+  float qf[DT == kF32 ? DSTEPS : 1];
+  uint32_t qh[DT == kF32 ? 1 : DSTEPS][2];
+  if constexpr (DT == kF32) {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) qf[s] = ((const float*)qrow)[4 * s + lg];
+  } else {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) {
+      const uint2 v = *(const uint2*)(qrow + (16 * s + 4 * lg) * 2);
+      qh[s][0] = v.x;
+      qh[s][1] = v.y;
+    }
+  }
+
+  // Key band of the tile and this split's part of it.
+  const int64_t p_first = pl.P + i_first;
+  const int64_t p_last = pl.P + i_last;
+  const int64_t lo = p_first - a.W + 1 > 0 ? p_first - a.W + 1 : 0;
+  const int64_t nkeys = p_last - lo + 1;
+  const int64_t per = ((nkeys + a.nsplit - 1) / a.nsplit + BN - 1) / BN * BN;
+  const int64_t kb = lo + split * per;
+  const int64_t ke = kb + per < p_last + 1 ? kb + per : p_last + 1;
+
+  const int64_t base = pl.P - pl.Lb;
+  const uint64_t ck = (uint64_t)((const char*)a.past_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e);
+  const uint64_t cv = (uint64_t)((const char*)a.past_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e);
+  const uint64_t nk = (uint64_t)((const char*)a.k + (((int64_t)b * a.S) * a.Hkv + kvh) * D * e);
+  const uint64_t nv = (uint64_t)((const char*)a.v + (((int64_t)b * a.S) * a.Hkv + kvh) * D * e);
+  const int64_t new_stride = (int64_t)a.Hkv * D * e;
+
+  // Block loads into registers: chunk c of the block = key c / CPR, 16-byte
+  // part c % CPR.  Keys outside [kb, ke) load zeros.
+  u32x4 rk[CPT], rv[CPT];
+  auto load_block = [&](int64_t j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * kThreads;
+      const int key = c / CPR, part = c % CPR;
+      const int64_t j = j0 + key;
+      u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (c < Sh::CHUNKS && j < ke) {
+        const bool in_cache = j < pl.P;
+        const uint64_t msk = 0ull - (uint64_t)in_cache;
+        const uint64_t off_c = (uint64_t)((j - base) * D * e + part * 16);
+        const uint64_t off_n = (uint64_t)((j - pl.P) * new_stride + part * 16);
+        const uint64_t ka = ((ck + off_c) & msk) | ((nk + off_n) & ~msk);
+        const uint64_t va = ((cv + off_c) & msk) | ((nv + off_n) & ~msk);
+        kk = *(const u32x4*)ka;
+        vv = *(const u32x4*)va;
+      }
+      rk[u] = kk;
+      rv[u] = vv;
+    }
+  };
+  auto store_block = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * kThreads;
+      if (c >= Sh::CHUNKS) continue;
+      const int key = c / CPR, part = c % CPR;
+      const int d0 = part * (16 / e);
+      if constexpr (DT == kF32) {
+        float* kd = (float*)sK + key * KS + d0;
+        float* vd = (float*)sV + key * VS + d0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kd[w] = __uint_as_float(rk[u][w]);
+          vd[w] = __uint_as_float(rv[u][w]);
+        }
+      } else {
+        uint32_t* kd = (uint32_t*)((uint16_t*)sK + key * KS + d0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) kd[w] = rk[u][w];
+        // V transposed: sV[d][key]
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          ((uint16_t*)sV)[(d0 + 2 * w) * VS + key] = (uint16_t)(rv[u][w] & 0xFFFFu);
+          ((uint16_t*)sV)[(d0 + 2 * w + 1) * VS + key] = (uint16_t)(rv[u][w] >> 16);
+        }
+      }
+    }
+  };
+
+  const bool has_cap = a.softcap > 0.0f;
+  const float cap = a.softcap;
+  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
+  const bool has_bias = a.bias != nullptr;
+  const int64_t bias_row = has_bias
+      ? ((((a.bias_b ? (int64_t)b : 0) * (a.bias_h ? a.Hq : 1) + (a.bias_h ? my_h : 0)) * a.S + my_i) *
+         (int64_t)a.total)
+      : 0;
+
+  float m_run = -INFINITY;  // log2 units, per query (same in all 4 lane groups)
+  float l_run = 0.0f;       // this lane's share of the sum
+  f4 o[DT16];               // O^T tiles: d = 16 dt + 4 lg + r, query lq
+#pragma unroll
+  for (int t = 0; t < DT16; ++t) o[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nblocks = ke > kb ? (int)((ke - kb + BN - 1) / BN) : 0;
+  if (nblocks > 0) load_block(kb);
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const int64_t j0 = kb + (int64_t)blk * BN;
+    __syncthreads();  // previous block's LDS reads are done
+    store_block();
+    __syncthreads();
+    if (blk + 1 < nblocks) load_block(j0 + BN);
+
+    // S^T for the two 16-key tiles of the block
+    f4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (DT == kF32) {
+        const float* kr = (const float*)sK + (kt * 16 + lq) * KS + lg;
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[4 * s], qf[s], acc, 0, 0, 0);
+      } else {
+        const uint16_t* kr = (const uint16_t*)sK + (kt * 16 + lq) * KS + 4 * lg;
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+          const uint2 kv = *(const uint2*)(kr + 16 * s);
+          if constexpr (DT == kF16) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(h4, make_uint2(kv.x, kv.y)),
+                __builtin_bit_cast(h4, make_uint2(qh[s][0], qh[s][1])), acc, 0, 0, 0);
+          } else {
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s4, make_uint2(kv.x, kv.y)),
+                __builtin_bit_cast(s4, make_uint2(qh[s][0], qh[s][1])), acc, 0, 0, 0);
+          }
+        }
+      }
+      sc[kt] = acc;
+    }
+
+    // Scores: key j = j0 + 16 kt + 4 lg + r, query lq.
+    float smax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t j = j0 + kt * 16 + 4 * lg + r;
+        const bool vis = my_ok && j < ke && j <= my_pos && j > my_pos - a.W;
+        float x = sc[kt][r] * a.scale;
+        if (has_cap) {
+          const float y = x * inv_cap;
+          if constexpr (DT == kF32) {
+            x = cap * tanhf(y);
+          } else {
+            const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(
+                                       __builtin_amdgcn_exp2f(2.0f * kLog2e * fabsf(y)) + 1.0f);
+            x = cap * copysignf(t, y);
+          }
+        }
+        if (has_bias && vis) x += load_one<DT>(a.bias, bias_row + j);
+        x = vis ? x * kLog2e : -INFINITY;
+        sc[kt][r] = x;
+        smax = fmaxf(smax, x);
+      }
+    smax = fmaxf(smax, __shfl_xor(smax, 16, kWave));
+    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+    const float m_new = fmaxf(m_run, smax);
+    const float corr = (m_run == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = (sc[kt][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[kt][r] - m_new);
+        if constexpr (DT == kF16) p = (float)(_Float16)p;  // the operand PV uses
+        sc[kt][r] = p;
+        psum += p;
+      }
+    l_run = l_run * corr + psum;
+#pragma unroll
+    for (int t = 0; t < DT16; ++t) o[t] *= corr;
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if constexpr (DT == kF32) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const float* vr = (const float*)sV + (kt * 16 + 4 * lg + t4) * VS + lq;
+#pragma unroll
+          for (int dt = 0; dt < DT16; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * dt], sc[kt][t4], o[dt], 0, 0, 0);
+        }
+      } else {
+        uint32_t pw[2], pl2[2];
+        if constexpr (DT == kF16) {
+          pw[0] = (uint32_t)f32_to_f16_bits(sc[kt][0]) | ((uint32_t)f32_to_f16_bits(sc[kt][1]) << 16);
+          pw[1] = (uint32_t)f32_to_f16_bits(sc[kt][2]) | ((uint32_t)f32_to_f16_bits(sc[kt][3]) << 16);
+        } else {
+          // bf16 keeps 8 significant bits, too few for P: P = hi + lo, both
+          // bf16, and two products (relative error ~2^-17)
+          uint16_t hi[4], lo[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            hi[r] = f32_to_bf16(sc[kt][r]);
+            lo[r] = f32_to_bf16(sc[kt][r] - __uint_as_float((uint32_t)hi[r] << 16));
+          }
+          pw[0] = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+          pw[1] = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+          pl2[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+          pl2[1] = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) {
+          const uint2 vv = *(const uint2*)((const uint16_t*)sV + (16 * dt + lq) * VS + kt * 16 + 4 * lg);
+          if constexpr (DT == kF16) {
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(h4, vv), __builtin_bit_cast(h4, make_uint2(pw[0], pw[1])), o[dt],
+                0, 0, 0);
+          } else {
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s4, vv), __builtin_bit_cast(s4, make_uint2(pw[0], pw[1])), o[dt],
+                0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s4, vv), __builtin_bit_cast(s4, make_uint2(pl2[0], pl2[1])), o[dt],
+                0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // Sum of P over the four lane groups; write O (or the split partial).
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (my_ok) {
+    const int64_t row = ((int64_t)b * a.S + my_i) * a.Hq + my_h;
+    if (a.nsplit == 1) {
+      const float inv = 1.0f / l_run;
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt) {
+        const int d0 = 16 * dt + 4 * lg;
+        if constexpr (DT == kF32) {
+          *(f4*)((float*)a.out + row * D + d0) = o[dt] * inv;
+        } else {
+          uint32_t w0, w1;
+          if constexpr (DT == kF16) {
+            w0 = (uint32_t)f32_to_f16_bits(o[dt][0] * inv) | ((uint32_t)f32_to_f16_bits(o[dt][1] * inv) << 16);
+            w1 = (uint32_t)f32_to_f16_bits(o[dt][2] * inv) | ((uint32_t)f32_to_f16_bits(o[dt][3] * inv) << 16);
+          } else {
+            w0 = (uint32_t)f32_to_bf16(o[dt][0] * inv) | ((uint32_t)f32_to_bf16(o[dt][1] * inv) << 16);
+            w1 = (uint32_t)f32_to_bf16(o[dt][2] * inv) | ((uint32_t)f32_to_bf16(o[dt][3] * inv) << 16);
+          }
+          *(uint2*)((uint16_t*)a.out + row * D + d0) = make_uint2(w0, w1);
+        }
+      }
+    } else {
+      float* op = a.opart + (row * a.nsplit + split) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt) *(f4*)(op + 16 * dt + 4 * lg) = o[dt];
+      if (lg == 0) {
+        a.ml[(row * a.nsplit + split) * 2 + 0] = m_run;
+        a.ml[(row * a.nsplit + split) * 2 + 1] = l_run;
+      }
+    }
+  }
+  slice_tail<DT>(a, pl, b, kvh, D);
+}
+
+template <int DT, int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
+  if constexpr (ChunkShape<DT, D>::ok) {
+    const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
+    attn_chunk_kernel<DT, D><<<grid, kThreads, 0, st>>>(a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_t(int D, const AttnArgs& a, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_d<DT, 16>(a, st);
+    case 32: return launch_d<DT, 32>(a, st);
+    case 64: return launch_d<DT, 64>(a, st);
+    case 128: return launch_d<DT, 128>(a, st);
+    case 256: return launch_d<DT, 256>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool chunk_kernel_supports(int dtype, int D) {
+  if (dtype < kF32 || dtype > kBF16) return false;
+  const int e = dtype == kF32 ? 4 : 2;
+  return D >= 16 && D % 16 == 0 && D <= 256 && D * e <= 512;
+}
+
+int chunk_rows_per_workgroup() { return BQ; }
+int chunk_keys_per_block() { return BN; }
+
+hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t st) {
+  switch (dtype) {
+    case kF32: return launch_t<kF32>(D, a, st);
+    case kF16: return launch_t<kF16>(D, a, st);
+    case kBF16: return launch_t<kBF16>(D, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swgqa

@@ -49,6 +49,12 @@ struct CopyArgs {
 hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
                              hipStream_t stream);
 hipError_t launch_combine(int dtype, int D, const AttnArgs& a, hipStream_t stream);
+// MFMA kernel for multi-token steps (swgqa_attn_chunk.hip): 64 query rows
+// per workgroup, keys in blocks of 32.
+bool chunk_kernel_supports(int dtype, int D);
+int chunk_rows_per_workgroup();
+int chunk_keys_per_block();
+hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 // Staged decode kernel (swgqa_attn_decode.hip): supports row sizes up to
 // 256 bytes and NQ * (16 / element bytes) <= 64.
 bool decode_kernel_supports(int dtype, int D, int nq);

@@ -243,3 +243,56 @@ def test_host_errors_return_before_launch():
     assert sw.forward_status(p, t, t, t, t[16:], t[16:], seq, None, t, t[32:], t[32:], ws) == sw.ERR_ALIAS
     assert sw.forward_status(p, t, t, t, t, t, seq, None, t, t, t, ws, workspace_bytes=16) == sw.ERR_ARG
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Multi-token steps (S >= 16) run on the matrix-core kernel.
+def _bias_nan_outside(cfg, syn, P, S, total):
+    bias = syn.bias_f32(np.arange(len(P)), P, S, total)
+    j = np.arange(total)[None, None, None, :]
+    p = np.asarray(P)[:, None, None, None] + np.arange(S)[None, None, :, None]
+    vis = (j <= p) & (j > p - cfg.W)
+    return synth.to_storage(np.where(vis, bias, np.float32(np.nan)), cfg.dtype)
+
+
+CHUNK = [
+    Cfg(B=3, Hq=8, Hkv=2, D=64, C=110, W=100, seed=31, dtype=synth.F32, softcap=20.0),
+    Cfg(B=3, Hq=8, Hkv=2, D=128, C=110, W=100, seed=32, dtype=synth.F16),
+    Cfg(B=2, Hq=12, Hkv=3, D=128, C=90, W=64, seed=33, dtype=synth.BF16, softcap=30.0),
+    Cfg(B=2, Hq=4, Hkv=4, D=32, C=70, W=70, seed=34, dtype=synth.F16),
+    Cfg(B=1, Hq=16, Hkv=2, D=16, C=48, W=40, seed=35, dtype=synth.F32),
+]
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("cfg", CHUNK, ids=lambda c: f"D{c.D}g{c.Hq // c.Hkv}t{c.dtype}cap{int(c.softcap)}")
+def test_chunked_steps_ragged_bias(cfg, mode):
+    say(f"chunked {cfg} mode={mode}")
+    syn = cfg.synth()
+    vers = Versions(cfg.B)
+    P0 = np.array([0, 57, 133][:cfg.B])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, mode=mode, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S, with_bias in [(32, True), (17, False), (48, True), (150, False), (16, True), (1, False)]:
+        total = int((P + S).max())
+        bias = _bias_nan_outside(cfg, syn, P, S, total) if with_bias else None
+        run.step(P, S, bias=bias, total=total)
+        P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+def test_chunk_key_splits_long_window():
+    """Few (item, KV head) slices and a long window: the chunk kernel splits
+    the key band across workgroups and a merge kernel combines them."""
+    cfg = Cfg(B=1, Hq=4, Hkv=1, D=128, C=1600, W=1500, seed=36, dtype=synth.BF16, softcap=50.0)
+    syn = cfg.synth()
+    vers = Versions(1)
+    P0 = np.array([1700])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S in [64, 64, 1, 40]:
+        run.step(P, S)
+        P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")
