@@ -38,6 +38,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 #ifndef SWGQA_DEC_DEPTH
 #define SWGQA_DEC_DEPTH 3
 #endif
+// K/V rows are read once per step: streaming (non-temporal) loads, measured
+// ~10% faster on the 32-item serving decode.
+#ifndef SWGQA_DEC_NT
+#define SWGQA_DEC_NT 1
+#endif
+
 
 template <int DT, int D, int NQ>
 struct DecShape {
@@ -106,7 +112,8 @@ __device__ __forceinline__ float chunk_dot(const uint32_t* q, const uint32_t* k,
 }
 
 template <int DT, int D, int NQ, int kWaves, int DEPTH>
-__global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWaves * kWave)
+__attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kernel(AttnArgs a) {
   constexpr int kThreads = kWaves * kWave;
   using Sh = DecShape<DT, D, NQ>;
   constexpr int e = Sh::e, EPL = Sh::EPL, LPR = Sh::LPR, RPW = Sh::RPW, U = Sh::U;
@@ -201,6 +208,12 @@ __global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a)
   const int64_t ke = kb + chunk < p_last + 1 ? kb + chunk : p_last + 1;
   const int nst = ke > kb ? (int)((ke - kb + SR - 1) / SR) : 0;
 
+  // visibility of key kb + jr for this lane's query, as 32-bit bounds on jr
+  const int64_t vlo = my_pos - a.W + 1 - kb;
+  const int64_t vhi = (my_pos < ke - 1 ? my_pos : ke - 1) - kb;
+  const int32_t vis_lo = my_q_ok ? (int32_t)(vlo < -(int64_t)0x7fffffff ? -0x7fffffff : vlo) : 1;
+  const int32_t vis_hi = my_q_ok ? (int32_t)vhi : 0;
+
   const int64_t base = pl.P - pl.Lb;
   const char* cache_k = (const char*)a.past_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
   const char* cache_v = (const char*)a.past_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
@@ -249,13 +262,21 @@ __global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a)
       const uint64_t vaddr = kaddr + ((cv_minus_ck & msk) | (nv_minus_nk & ~msk));
       const char* kp = (const char*)kaddr;
       const char* vp = (const char*)vaddr;
-      uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = make_uint4(0u, 0u, 0u, 0u);
+      u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (ok) {
-        kk = *(const uint4*)kp;
-        vv = *(const uint4*)vp;
+#if SWGQA_DEC_NT
+        kk = __builtin_nontemporal_load((const u32x4*)kp);
+        vv = __builtin_nontemporal_load((const u32x4*)vp);
+#else
+        kk = *(const u32x4*)kp;
+        vv = *(const u32x4*)vp;
+#endif
       }
-      kr[u][0] = kk.x; kr[u][1] = kk.y; kr[u][2] = kk.z; kr[u][3] = kk.w;
-      vr[u][0] = vv.x; vr[u][1] = vv.y; vr[u][2] = vv.z; vr[u][3] = vv.w;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        kr[u][w] = kk[w];
+        vr[u][w] = vv[w];
+      }
     }
   };
 
@@ -288,8 +309,8 @@ __global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a)
         for (int w = 0; w < LPR; ++w) x += pp[w];
       }
       x *= a.scale;
-      const int64_t j = kb + (int64_t)st * SR + row;
-      const bool vis = my_q_ok && j < ke && j <= my_pos && j > my_pos - a.W;
+      const int32_t jr = st * SR + row;
+      const bool vis = jr >= vis_lo && jr <= vis_hi;
       if (has_cap) {
         const float y = x * inv_cap;
         if constexpr (DT == kF32) {
@@ -302,7 +323,7 @@ __global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a)
           x = cap * copysignf(t, y);
         }
       }
-      if (has_bias && vis) x += load_one<DT>(a.bias, bias_row + j);
+      if (has_bias && vis) x += load_one<DT>(a.bias, bias_row + kb + jr);
       s[k] = vis ? x * kLog2e : -INFINITY;
       smax = fmaxf(smax, s[k]);
     }
@@ -322,12 +343,18 @@ __global__ __launch_bounds__(kWaves * kWave) void attn_decode_kernel(AttnArgs a)
     wave_lds_fence();
     // C. rescale and accumulate V
     float cr[NQ];
+    bool rescale = false;
 #pragma unroll
-    for (int t = 0; t < NQ; ++t) cr[t] = cbuf[t];
+    for (int t = 0; t < NQ; ++t) {
+      cr[t] = cbuf[t];
+      rescale |= cr[t] != 1.0f;
+    }
+    if (rescale) {  // the same in every lane: skipped once the maxima settle
 #pragma unroll
-    for (int t = 0; t < NQ; ++t)
+      for (int t = 0; t < NQ; ++t)
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) acc[t][k] *= cr[t];
+        for (int k = 0; k < EPL; ++k) acc[t][k] *= cr[t];
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = u * RPW + rslot;

@@ -45,8 +45,18 @@ __host__ __device__ __forceinline__ int64_t resident_len(int64_t T, int64_t C,
   return T - G * ((T - C + G - 1) / G);
 }
 
+// The same for the lengths a step can see: T = seqlens_k + 1 <= 2^31 and
+// 1 <= W <= C < 2^31, so ceil((T - C) / G) = (T - C - 1) / G + 1 with a
+// 32-bit unsigned division (the 64-bit one is a long software sequence).
+__device__ __forceinline__ int64_t resident_len_step(int64_t T, int32_t C, int32_t W) {
+  if (T <= C) return T;
+  const uint32_t G = (uint32_t)(C - W + 1);
+  const uint32_t q = (uint32_t)(T - C - 1) / G + 1u;
+  return T - (int64_t)G * q;
+}
+
 __device__ __forceinline__ ItemPlan plan_item(int32_t seqlen_k, int64_t S,
-                                              int64_t C, int64_t W,
+                                              int32_t C, int32_t W,
                                               int64_t total) {
   ItemPlan pl;
   pl.T = (int64_t)seqlen_k + 1;
@@ -56,8 +66,8 @@ __device__ __forceinline__ ItemPlan plan_item(int32_t seqlen_k, int64_t S,
     pl.T = pl.P = pl.Lb = pl.La = pl.kept = pl.shift = -1;
     return pl;
   }
-  pl.Lb = resident_len(pl.P, C, W);
-  pl.La = resident_len(pl.T, C, W);
+  pl.Lb = resident_len_step(pl.P, C, W);
+  pl.La = resident_len_step(pl.T, C, W);
   pl.kept = pl.La - S;
   pl.shift = pl.Lb + S - pl.La;
   return pl;
