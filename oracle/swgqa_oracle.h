@@ -18,6 +18,10 @@
  *   attention_bias (B or 1, Hq or 1, S, total_sequence_length) or NULL
  *   output (B, S, Hq*D)
  *
+ * Pins: tests/test_oracle_pins.py.  Parity unpinned: the order of softcap and
+ * attention_bias when both are given (scale, softcap, then bias) -- no page
+ * fixes it and no workload combines them.
+ *
  * Status codes: 0 ok, 1 bad argument, 2 unsupported, 3 partial aliasing of a
  * past and present buffer, 4 invalid per-item lengths (that item's output is
  * zero-filled and its present rows are left untouched; the other items are
