@@ -124,20 +124,6 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
     return;
   }
 
-  // Appends on drifting steps with a shared buffer (rows [Lb, Lb + S) are
-  // beyond every cache row attention reads).
-  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
-    char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
-    char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
-    for (int idx = tid; idx < a.S * CPR; idx += kThreads) {
-      const int i = idx / CPR, w = idx % CPR;
-      const int64_t src = ((int64_t)(b * a.S + i) * a.Hkv + kvh) * D * e + w * 16;
-      const int64_t dst = (pl.Lb + i) * (int64_t)D * e + w * 16;
-      *(u32x4*)(pk + dst) = *(const u32x4*)((const char*)a.k + src);
-      *(u32x4*)(pv + dst) = *(const u32x4*)((const char*)a.v + src);
-    }
-  }
-
   // This lane's query (column lq of wave's 16 rows).
   const int my_qi = q0 + wave * 16 + lq;
   const bool my_ok = my_qi < nq_item;
@@ -414,6 +400,20 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
       }
     }
   }
+  // Appends on drifting steps with a shared buffer: rows [Lb, Lb + S) lie
+  // beyond every cache row attention reads, so they are written last.
+  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
+    char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    for (int idx = tid; idx < a.S * CPR; idx += kThreads) {
+      const int i = idx / CPR, w = idx % CPR;
+      const int64_t src = ((int64_t)(b * a.S + i) * a.Hkv + kvh) * D * e + w * 16;
+      const int64_t dst = (pl.Lb + i) * (int64_t)D * e + w * 16;
+      *(u32x4*)(pk + dst) = *(const u32x4*)((const char*)a.k + src);
+      *(u32x4*)(pv + dst) = *(const u32x4*)((const char*)a.v + src);
+    }
+  }
+
   slice_tail<DT>(a, pl, b, kvh, D);
 }
 

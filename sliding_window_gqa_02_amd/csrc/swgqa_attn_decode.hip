@@ -137,9 +137,22 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   __shared__ float s_l[kWaves][NQ];
   __shared__ float s_acc[kWaves][NQ][D];
 
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
   const int nq_item = a.S * a.group;
   const int q0 = tile * NQ;
+  // Query tile: (position, head) pairs q0 .. q0 + NQ - 1, position-major.
+  // Loaded before the plan: their addresses do not depend on seqlens_k.
+  const int i_first = q0 / a.group;
+  const int i_last = (min(q0 + NQ, nq_item) - 1) / a.group;
+  uint32_t qw[NQ][4];
+#pragma unroll
+  for (int t = 0; t < NQ; ++t) {
+    const int qi = min(q0 + t, nq_item - 1);
+    const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+    const uint4 v = *(const uint4*)((const char*)a.q +
+                                    ((((int64_t)b * a.S + i) * a.Hq + h) * D + sub * EPL) * e);
+    qw[t][0] = v.x; qw[t][1] = v.y; qw[t][2] = v.z; qw[t][3] = v.w;
+  }
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
 
   if (!pl.ok) {
     if (tid == 0 && tile == 0 && split == 0 && kvh == 0) flag_status(a.status, kStatusBadItem);
@@ -163,33 +176,6 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
     return;
   }
 
-  // Appends on drifting steps with a shared buffer (rows [Lb, Lb + S) are
-  // beyond every row attention reads).
-  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
-    constexpr int W16 = D * e / 16;
-    char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
-    char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
-    for (int idx = tid; idx < a.S * W16; idx += kThreads) {
-      const int i = idx / W16, w = idx % W16;
-      const int64_t src = ((int64_t)(b * a.S + i) * a.Hkv + kvh) * D * e + w * 16;
-      const int64_t dst = (pl.Lb + i) * (int64_t)D * e + w * 16;
-      *(uint4*)(pk + dst) = *(const uint4*)((const char*)a.k + src);
-      *(uint4*)(pv + dst) = *(const uint4*)((const char*)a.v + src);
-    }
-  }
-
-  // Query tile: (position, head) pairs q0 .. q0 + NQ - 1, position-major.
-  const int i_first = q0 / a.group;
-  const int i_last = (min(q0 + NQ, nq_item) - 1) / a.group;
-  uint32_t qw[NQ][4];
-#pragma unroll
-  for (int t = 0; t < NQ; ++t) {
-    const int qi = min(q0 + t, nq_item - 1);
-    const int i = qi / a.group, h = kvh * a.group + qi % a.group;
-    const uint4 v = *(const uint4*)((const char*)a.q +
-                                    ((((int64_t)b * a.S + i) * a.Hq + h) * D + sub * EPL) * e);
-    qw[t][0] = v.x; qw[t][1] = v.y; qw[t][2] = v.z; qw[t][3] = v.w;
-  }
   // the query this lane scores in phase B (same for all its pairs)
   const int my_q = lane % NQ;
   const int my_qi = q0 + my_q;
@@ -455,6 +441,22 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
       }
     }
   }
+  // Appends on drifting steps with a shared buffer: rows [Lb, Lb + S) lie
+  // beyond every row attention reads, so they are written last, off the
+  // critical path of the loads above.
+  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
+    constexpr int W16 = D * e / 16;
+    char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
+    for (int idx = tid; idx < a.S * W16; idx += kThreads) {
+      const int i = idx / W16, w = idx % W16;
+      const int64_t src = ((int64_t)(b * a.S + i) * a.Hkv + kvh) * D * e + w * 16;
+      const int64_t dst = (pl.Lb + i) * (int64_t)D * e + w * 16;
+      *(uint4*)(pk + dst) = *(const uint4*)((const char*)a.k + src);
+      *(uint4*)(pv + dst) = *(const uint4*)((const char*)a.v + src);
+    }
+  }
+
   slice_tail<DT>(a, pl, b, kvh, D);
 }
 
