@@ -103,14 +103,16 @@ typedef struct {
 } swgqa_plan_entry;
 
 /* Bytes of device workspace swgqa_forward needs for these parameters: the
- * status word in bytes [0, 256), then key-split partials (scratch).  0 if the
- * parameters are invalid.  Pure host function.  A workspace of at least this
- * size serves any parameter set whose own size is not larger. */
+ * status word in bytes [0, 4), per-(item, KV head) arrival counters in bytes
+ * [256, 16384) that every call leaves at zero, then key-split partials
+ * (scratch).  0 if the parameters are invalid.  Pure host function.  A
+ * workspace of at least this size serves any parameter set whose own size is
+ * not larger. */
 size_t swgqa_workspace_size(const swgqa_params* params);
 
-/* Zeroes the first workspace_bytes of the workspace, status word included
- * (enqueued on `stream`; a small kernel, no memset node).  Call once on a
- * fresh workspace. */
+/* Zeroes the first workspace_bytes of the workspace, status word and
+ * counters included (enqueued on `stream`; a small kernel, no memset node).
+ * Call once on a fresh workspace, before its first swgqa_forward. */
 swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes,
                                   void* stream);
 

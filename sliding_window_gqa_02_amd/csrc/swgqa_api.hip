@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
 
@@ -14,7 +16,11 @@ namespace {
 
 using namespace swgqa;
 
-constexpr size_t kHeaderBytes = 256;  // status word + reserved
+// Workspace: status word at byte 0, per-slice arrival counters from byte
+// 256 to kHeaderBytes (zero between calls), then key-split partials.
+constexpr size_t kStatusBytes = 256;
+constexpr size_t kHeaderBytes = 16384;
+constexpr int64_t kMaxSliceCounters = (int64_t)((kHeaderBytes - kStatusBytes) / 4);
 #ifndef SWGQA_TARGET_WORKGROUPS
 #define SWGQA_TARGET_WORKGROUPS 2048
 #endif
@@ -24,12 +30,18 @@ constexpr size_t kHeaderBytes = 256;  // status word + reserved
 #ifndef SWGQA_WHOLE_SLICE_MAX_KEYS
 #define SWGQA_WHOLE_SLICE_MAX_KEYS 256
 #endif
+// With few (item, KV head) slices, the staged decode kernel narrows its
+// query tiles until the launch has at least this many workgroups.
+#ifndef SWGQA_DECODE_MIN_WORKGROUPS
+#define SWGQA_DECODE_MIN_WORKGROUPS 64
+#endif
 constexpr int kTargetWorkgroups = SWGQA_TARGET_WORKGROUPS;
 constexpr int kMinKeysPerSplit = 32;
 constexpr int kChunkMinTokens = 16;       // steps of at least this many tokens use MFMA
 constexpr int64_t kChunkMinWorkgroups = 256;
 constexpr int64_t kWholeSliceMinTiles = SWGQA_WHOLE_SLICE_MIN_TILES;
 constexpr int64_t kWholeSliceMaxKeys = SWGQA_WHOLE_SLICE_MAX_KEYS;
+constexpr int64_t kDecodeMinWorkgroups = SWGQA_DECODE_MIN_WORKGROUPS;
 
 size_t elem_bytes(int dt) { return dt == SWGQA_F32 ? 4 : 2; }
 
@@ -69,7 +81,7 @@ SplitPlan plan_split(const swgqa_params* p) {
     s.kind = Kind::kChunk;
     s.nq = chunk_rows_per_workgroup();
     s.ntiles = (per_kv + s.nq - 1) / s.nq;
-    const int64_t span = (s.nq + group - 1) / group + 1;
+    const int64_t span = std::min<int64_t>(p->sequence_length, (s.nq + group - 1) / group + 1);
     int64_t nkeys = (int64_t)p->local_window_size + span - 1;
     if (nkeys > p->total_sequence_length) nkeys = p->total_sequence_length;
     const int64_t base = (int64_t)p->batch_size * p->kv_num_heads * s.ntiles;
@@ -94,16 +106,25 @@ SplitPlan plan_split(const swgqa_params* p) {
   s.ntiles = (per_kv + nq - 1) / nq;
   // key rows a tile can touch: the window of its first position plus the
   // positions it spans
-  const int64_t span = (nq + group - 1) / group + 1;
+  const int64_t span = std::min<int64_t>(p->sequence_length, (nq + group - 1) / group + 1);
   int64_t nkeys = (int64_t)p->local_window_size + span - 1;
   if (nkeys > p->total_sequence_length) nkeys = p->total_sequence_length;
   const int64_t base = (int64_t)p->batch_size * p->kv_num_heads * s.ntiles;
   if (s.kind == Kind::kDecode && (base >= kWholeSliceMinTiles || nkeys <= kWholeSliceMaxKeys)) {
-    // enough tiles to fill the chip with one 8-wave workgroup each, or a
-    // window short enough for one workgroup: no split, no merge pass, and
-    // the in-place write-back stays inside the workgroup
+    // enough tiles to fill the chip with one workgroup each, or a window
+    // short enough for one workgroup: no key split, no merge pass, and the
+    // in-place write-back stays inside the kernel
+    const int64_t slices = (int64_t)p->batch_size * p->kv_num_heads;
+    while (s.nq > 2 && slices * s.ntiles < kDecodeMinWorkgroups) {
+      // narrower tiles: more workgroups, each with less work per key row
+      s.nq /= 2;
+      s.ntiles = (per_kv + s.nq - 1) / s.nq;
+    }
+    const int64_t stages =
+        (nkeys + decode_stage_rows(p->dtype, p->head_size, s.nq) - 1) /
+        decode_stage_rows(p->dtype, p->head_size, s.nq);
     s.nsplit = 1;
-    s.waves = 8;
+    s.waves = stages <= 4 ? 4 : 8;
     return s;
   }
   int64_t ns = base > 0 ? (kTargetWorkgroups + base - 1) / base : 1;
@@ -189,6 +210,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.bias = attention_bias;
   a.out = output;
   a.status = (uint32_t*)workspace;
+  a.slice_counters = (uint32_t*)((char*)workspace + kStatusBytes);
   float* part = (float*)((char*)workspace + kHeaderBytes);
   a.opart = part;
   a.ml = part + (size_t)p->batch_size * p->sequence_length * p->num_heads * s.nsplit *
@@ -209,7 +231,11 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.softcap = p->softcap;
   a.bias_b = p->bias_dim0_is_batch ? 1 : 0;
   a.bias_h = p->bias_dim1_is_heads ? 1 : 0;
-  a.fuse_writeback = (shared && s.ntiles == 1 && s.nsplit == 1) ? 1 : 0;
+  // in-kernel write-back: one workgroup per slice, or (staged decode) the
+  // last query tile of each slice, tracked by a counter
+  const bool counted = s.kind == Kind::kDecode &&
+                       (int64_t)p->batch_size * p->kv_num_heads <= kMaxSliceCounters;
+  a.fuse_writeback = (shared && s.nsplit == 1 && (s.ntiles == 1 || counted)) ? 1 : 0;
   a.waves = s.waves;
 
   const hipError_t ea =

@@ -184,8 +184,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
         const uint64_t off_n = (uint64_t)((j - pl.P) * new_stride + part * 16);
         const uint64_t ka = ((ck + off_c) & msk) | ((nk + off_n) & ~msk);
         const uint64_t va = ((cv + off_c) & msk) | ((nv + off_n) & ~msk);
-        kk = *(const u32x4*)ka;
-        vv = *(const u32x4*)va;
+        kk = load16_global<false>(ka);
+        vv = load16_global<false>(va);
       }
       rk[u] = kk;
       rv[u] = vv;

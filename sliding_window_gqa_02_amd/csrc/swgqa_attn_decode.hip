@@ -246,17 +246,10 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
           ((ck_addr + (uint64_t)(((j - base) * D + sub * EPL) * e)) & msk) |
           ((nk_addr + (uint64_t)((j - pl.P) * new_stride + sub * EPL * e)) & ~msk);
       const uint64_t vaddr = kaddr + ((cv_minus_ck & msk) | (nv_minus_nk & ~msk));
-      const char* kp = (const char*)kaddr;
-      const char* vp = (const char*)vaddr;
       u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (ok) {
-#if SWGQA_DEC_NT
-        kk = __builtin_nontemporal_load((const u32x4*)kp);
-        vv = __builtin_nontemporal_load((const u32x4*)vp);
-#else
-        kk = *(const u32x4*)kp;
-        vv = *(const u32x4*)vp;
-#endif
+        kk = load16_global<SWGQA_DEC_NT>(kaddr);
+        vv = load16_global<SWGQA_DEC_NT>(vaddr);
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -475,6 +468,29 @@ hipError_t launch_nq(const AttnArgs& a, hipStream_t st) {
 }
 
 template <int DT, int D>
+int stage_rows(int nq) {
+  switch (nq) {
+    case 2: return DecShape<DT, D, 2>::SR;
+    case 4: return DecShape<DT, D, 4>::SR;
+    case 8: return DecShape<DT, D, 8>::SR;
+    case 16: return DecShape<DT, D, 16>::SR;
+    default: return 1;
+  }
+}
+
+template <int DT>
+int stage_rows_t(int D, int nq) {
+  switch (D) {
+    case 8: return stage_rows<DT, 8>(nq);
+    case 16: return stage_rows<DT, 16>(nq);
+    case 32: return stage_rows<DT, 32>(nq);
+    case 64: return stage_rows<DT, 64>(nq);
+    case 128: return stage_rows<DT, 128>(nq);
+    default: return 1;
+  }
+}
+
+template <int DT, int D>
 bool shape_ok(int nq) {
   switch (nq) {
     case 2: return DecShape<DT, D, 2>::ok;
@@ -528,6 +544,15 @@ bool decode_kernel_supports(int dtype, int D, int nq) {
     case kF16: return ok_t<kF16>(D, nq);
     case kBF16: return ok_t<kBF16>(D, nq);
     default: return false;
+  }
+}
+
+int decode_stage_rows(int dtype, int D, int nq) {
+  switch (dtype) {
+    case kF32: return stage_rows_t<kF32>(D, nq);
+    case kF16: return stage_rows_t<kF16>(D, nq);
+    case kBF16: return stage_rows_t<kBF16>(D, nq);
+    default: return 1;
   }
 }
 

@@ -164,6 +164,17 @@ __device__ __forceinline__ void store_words(void* p, const uint32_t* w) {
   }
 }
 
+// 16-byte load from a global-memory address held as an integer.  Casting to
+// an address-space-1 pointer makes it a GLOBAL instruction; through a generic
+// pointer it would be a FLAT one, which also counts against the LDS wait
+// counter, so every wait for an LDS result would wait for it as well.
+template <bool NT>
+__device__ __forceinline__ u32x4 load16_global(uint64_t addr) {
+  typedef const u32x4 __attribute__((address_space(1)))* gptr;
+  if constexpr (NT) return __builtin_nontemporal_load((gptr)addr);
+  else return *(gptr)addr;
+}
+
 // Marks the workspace status word (sticky).
 __device__ __forceinline__ void flag_status(uint32_t* status, uint32_t bits) {
   atomicOr(status, bits);

@@ -21,6 +21,9 @@ struct AttnArgs {
   float* opart;         // split partial accumulators (rows of D floats)
   float* ml;            // split partial (max, sum) pairs, log2 domain
   uint32_t* status;
+  // per-slice arrival counters for the in-kernel write-back of multi-tile
+  // launches (zero between calls)
+  uint32_t* slice_counters;
   // fused append on drifting steps (shared buffer only; may be NULL)
   void* present_k;
   void* present_v;
@@ -28,7 +31,7 @@ struct AttnArgs {
   int32_t ntiles, nsplit;
   float scale, softcap;
   int32_t bias_b, bias_h;
-  int32_t fuse_writeback;  // shared buffer and one workgroup per slice
+  int32_t fuse_writeback;  // shared buffer, one key split: write-back in the kernel
   int32_t waves;           // waves per workgroup of the staged kernel
 };
 
@@ -58,6 +61,8 @@ hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t st
 // Staged decode kernel (swgqa_attn_decode.hip): supports row sizes up to
 // 256 bytes and NQ * (16 / element bytes) <= 64.
 bool decode_kernel_supports(int dtype, int D, int nq);
+// Key rows one wave of the staged decode kernel takes per stage.
+int decode_stage_rows(int dtype, int D, int nq);
 hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
                               hipStream_t stream);
 hipError_t launch_writeback(const CopyArgs& a, hipStream_t stream);

@@ -4,11 +4,13 @@
 // GroupQueryAttention windowed KV cache layout contract", Description: rows
 // [0, L(T)) hold the newest L(T) positions; "[CPU] Add windowed kv cache for
 // GQA", block compaction, skipped on drifting steps where the append was
-// already done during attention).  Used at the end of an attention
-// workgroup that owns the whole slice, after a barrier: no row it overwrites
-// is still to be read.  (Cross-workgroup hand-off via device-scope fences was
-// measured far slower here -- each release fence writes back L2 -- so other
-// launch shapes use a separate write-back kernel.)
+// already done during attention).  Runs at the end of the attention kernel,
+// once no row it overwrites is still to be read: after a barrier when one
+// workgroup reads the slice; with several query tiles per slice, in the
+// tile that arrives last on the slice's counter.  The counter and its
+// release/acquire fences are used only on compacting steps (each agent-scope
+// release writes back this XCD's L2, measured far too slow to pay on every
+// step); drifting steps only append, to rows no tile reads.
 #pragma once
 
 #include "swgqa_common.hpp"
@@ -71,15 +73,32 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
   }
 }
 
-// The end of a step for a workgroup that owns its whole (item, KV head)
-// slice (one query tile, one key split): once every wave has finished
-// reading, the cache write-back of the slice runs in the same workgroup.
-// Other launch shapes merge splits and rewrite the cache in separate kernels.
+// The end of a step for one workgroup of slice (b, kvh).  With one key split
+// the write-back runs here: directly when this workgroup is the slice's only
+// reader, else in the last of the a.ntiles query tiles to finish.  Each tile
+// counts its arrival with an acq_rel read-modify-write at agent scope after a
+// barrier, i.e. after all its reads of the slice; the last arrival therefore
+// happens after every read of every tile, resets the counter for the next
+// call, and rewrites the slice.  Other launch shapes rewrite the cache in a
+// separate kernel.
 template <int DT>
 __device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl, int b, int kvh,
                                            int D) {
-  if (!a.fuse_writeback || pl.shift == 0) return;  // drifting: appended up front
-  __syncthreads();  // all reads of this slice are done
+  if (!a.fuse_writeback || pl.shift == 0) return;  // drifting: appended by tile 0
+  __syncthreads();  // all reads of this slice by this workgroup are done
+  if (a.ntiles > 1) {
+    __shared__ uint32_t s_last;
+    if (threadIdx.x == 0) {
+      uint32_t* ctr = a.slice_counters + ((int64_t)b * a.Hkv + kvh);
+      const uint32_t seen =
+          __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t last = seen + 1u == (uint32_t)a.ntiles ? 1u : 0u;
+      if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+  }
   slice_writeback_shared(a, pl, b, kvh, D, Elem<DT>::bytes);
 }
 
