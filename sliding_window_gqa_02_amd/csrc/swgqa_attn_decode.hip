@@ -184,15 +184,20 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   const int my_h = kvh * a.group + (my_q_ok ? my_qi % a.group : 0);
   const int64_t my_pos = pl.P + my_i;
 
-  // Union key range of the tile, split evenly.
+  // Union key range of the tile, split evenly (n < 2^31: keys are positions
+  // below total_sequence_length).
   const int64_t p_first = pl.P + i_first;
   const int64_t p_last = pl.P + i_last;
   const int64_t lo = p_first - a.W + 1 > 0 ? p_first - a.W + 1 : 0;
   const int64_t n = p_last - lo + 1;
-  const int64_t chunk = (n + a.nsplit - 1) / a.nsplit;
+  const int64_t chunk =
+      a.nsplit == 1 ? n : (int64_t)(((uint32_t)n + (uint32_t)a.nsplit - 1u) / (uint32_t)a.nsplit);
   const int64_t kb = lo + split * chunk;
   const int64_t ke = kb + chunk < p_last + 1 ? kb + chunk : p_last + 1;
-  const int nst = ke > kb ? (int)((ke - kb + SR - 1) / SR) : 0;
+  const int32_t nk = ke > kb ? (int32_t)(ke - kb) : 0;  // keys kb + jr, 0 <= jr < nk
+  const int nst = (nk + SR - 1) / SR;
+  // keys with jr < ncache are resident cache rows, the others new rows
+  const int32_t ncache = (int32_t)(pl.P - kb < 0 ? 0 : (pl.P - kb < nk ? pl.P - kb : nk));
 
   // visibility of key kb + jr for this lane's query, as 32-bit bounds on jr
   const int64_t vlo = my_pos - a.W + 1 - kb;
@@ -200,17 +205,20 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   const int32_t vis_lo = my_q_ok ? (int32_t)(vlo < -(int64_t)0x7fffffff ? -0x7fffffff : vlo) : 1;
   const int32_t vis_hi = my_q_ok ? (int32_t)vhi : 0;
 
-  const int64_t base = pl.P - pl.Lb;
-  const char* cache_k = (const char*)a.past_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
-  const char* cache_v = (const char*)a.past_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
-  const int64_t new_stride = (int64_t)a.Hkv * D * e;   // bytes between new rows
-  const char* new_k = (const char*)a.k + (((int64_t)b * a.S) * a.Hkv + kvh) * D * e;
-  const char* new_v = (const char*)a.v + (((int64_t)b * a.S) * a.Hkv + kvh) * D * e;
-
-  const uint64_t ck_addr = (uint64_t)cache_k;
-  const uint64_t nk_addr = (uint64_t)new_k;
-  const uint64_t cv_minus_ck = (uint64_t)cache_v - ck_addr;
-  const uint64_t nv_minus_nk = (uint64_t)new_v - nk_addr;
+  // Byte addresses of key jr for this lane's 16-byte chunk: cache row
+  // kb + jr - (P - Lb) of the slice, or new row kb + jr - P of the step.
+  constexpr int kRowBytes = D * e;
+  constexpr int kRowShift = __builtin_ctz(kRowBytes);
+  static_assert((kRowBytes & (kRowBytes - 1)) == 0, "row bytes must be a power of two");
+  const int64_t slice_row0 = (int64_t)(b * a.Hkv + kvh) * a.C + (kb - (pl.P - pl.Lb));
+  const uint64_t ck_lane = (uint64_t)a.past_k + (uint64_t)(slice_row0 * kRowBytes) + sub * 16;
+  const uint64_t cv_lane = (uint64_t)a.past_v + (uint64_t)(slice_row0 * kRowBytes) + sub * 16;
+  const int64_t new_stride = (int64_t)a.Hkv * kRowBytes;  // bytes between new rows
+  const int64_t new_row0 = (int64_t)b * a.S + (kb + ncache - pl.P);  // new row of jr = ncache
+  const uint64_t nk_lane = (uint64_t)a.k + (uint64_t)((new_row0 * a.Hkv + kvh) * kRowBytes) + sub * 16;
+  const uint64_t nv_lane = (uint64_t)a.v + (uint64_t)((new_row0 * a.Hkv + kvh) * kRowBytes) + sub * 16;
+  const uint64_t dv_cache = cv_lane - ck_lane;
+  const uint64_t dv_new = nv_lane - nk_lane;
 
   const bool has_cap = a.softcap > 0.0f;
   const float cap = a.softcap;
@@ -233,24 +241,37 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   float* pbuf = s_p[wave];
   float* cbuf = s_corr[wave];
 
+  // Loads of one stage, issued unconditionally: rows past the split's end
+  // are clamped to its last key (finite data whose scores the mask removes),
+  // so the compiler can count the loads in flight and wait only for the
+  // stage being computed.
   auto load_stage = [&](int st, uint32_t (&kr)[U][4], uint32_t (&vr)[U][4]) __attribute__((always_inline)) {
+    const uint32_t s0 = (uint32_t)min(st, nst) * SR;  // no overflow: nst * SR < 2^31 + SR
+    const uint32_t last = (uint32_t)(nk - 1);
+    uint64_t ka[U], va[U];
+    if (min(s0 + SR, (uint32_t)nk) <= (uint32_t)ncache) {  // uniform: only cache rows
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t off = (uint64_t)min(s0 + u * RPW + rslot, last) << kRowShift;
+        ka[u] = ck_lane + off;
+        va[u] = cv_lane + off;
+      }
+    } else {
+      // branch-free mask select: a plain select between these bases is
+      // turned into a private-memory lookup table by the compiler
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t jr = min(s0 + u * RPW + rslot, last);
+        const uint64_t msk = 0ull - (uint64_t)(jr < (uint32_t)ncache);
+        ka[u] = ((ck_lane + ((uint64_t)jr << kRowShift)) & msk) |
+                ((nk_lane + (uint64_t)(((int64_t)jr - ncache) * new_stride)) & ~msk);
+        va[u] = ka[u] + ((dv_cache & msk) | (dv_new & ~msk));
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t j = kb + (int64_t)st * SR + u * RPW + rslot;
-      const bool ok = st < nst && j < ke;
-      const bool in_cache = j < pl.P;
-      // branch-free mask select: a plain select between these uniform bases
-      // is turned into a private-memory lookup table by the compiler
-      const uint64_t msk = 0ull - (uint64_t)in_cache;
-      const uint64_t kaddr =
-          ((ck_addr + (uint64_t)(((j - base) * D + sub * EPL) * e)) & msk) |
-          ((nk_addr + (uint64_t)((j - pl.P) * new_stride + sub * EPL * e)) & ~msk);
-      const uint64_t vaddr = kaddr + ((cv_minus_ck & msk) | (nv_minus_nk & ~msk));
-      u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (ok) {
-        kk = load16_global<SWGQA_DEC_NT>(kaddr);
-        vv = load16_global<SWGQA_DEC_NT>(vaddr);
-      }
+      const u32x4 kk = load16_global<SWGQA_DEC_NT>(ka[u]);
+      const u32x4 vv = load16_global<SWGQA_DEC_NT>(va[u]);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         kr[u][w] = kk[w];
@@ -355,8 +376,10 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   // DEPTH - 1 stages are in flight while one stage is computed.
   uint32_t k0[U][4], v0[U][4], k1[U][4], v1[U][4];
   int st = wave;
-  load_stage(st, k0, v0);
-  if constexpr (DEPTH == 3) {
+  if (nk == 0) {
+    // empty split: nothing to read
+  } else if constexpr (DEPTH == 3) {
+    load_stage(st, k0, v0);
     uint32_t k2[U][4], v2[U][4];
     load_stage(st + kWaves, k1, v1);
     while (st < nst) {
@@ -373,6 +396,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
       st += kWaves;
     }
   } else {
+    load_stage(st, k0, v0);
     while (st < nst) {
       load_stage(st + kWaves, k1, v1);
       compute_stage(st, k0, v0);
