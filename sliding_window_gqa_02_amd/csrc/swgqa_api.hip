@@ -225,6 +225,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.W = p->local_window_size;
   a.total = p->total_sequence_length;
   a.group = p->num_heads / p->kv_num_heads;
+  a.gdiv = make_gap_div((uint32_t)(p->capacity - p->local_window_size + 1));
   a.ntiles = s.ntiles;
   a.nsplit = s.nsplit;
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_size);
@@ -263,6 +264,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   c.C = p->capacity;
   c.W = p->local_window_size;
   c.total = p->total_sequence_length;
+  c.gdiv = a.gdiv;
   c.D = p->head_size;
   c.elem_bytes = (int32_t)e;
   c.skip_drifting = shared ? 1 : 0;  // drifting appends were done by attention
@@ -285,6 +287,10 @@ swgqa_status swgqa_plan(const swgqa_params* p, const int32_t* seqlens_k,
 
 int64_t swgqa_resident_length(int64_t T, int64_t C, int64_t W) {
   if (W < 1 || C < W || T < 0) return -1;
+  // the kernels' form (multiply-shift division by the gap) wherever it
+  // applies, so host tests exercise it
+  if (T <= ((int64_t)1 << 31) && C < ((int64_t)1 << 31))
+    return resident_len_step(T, (int32_t)C, make_gap_div((uint32_t)(C - W + 1)));
   return resident_len(T, C, W);
 }
 

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
   const int lq = lane % 16;   // query column of this lane
   const int lg = lane / 16;   // lane group (0..3)
 
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   const int nq_item = a.S * a.group;
   const int q0 = tile * BQ;
 

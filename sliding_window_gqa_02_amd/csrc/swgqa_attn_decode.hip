@@ -122,8 +122,10 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
 
   const int b = blockIdx.z;
   const int kvh = blockIdx.y;
-  const int tile = blockIdx.x / a.nsplit;
-  const int split = blockIdx.x % a.nsplit;
+  // seqlens_k first: the plan and every K/V address wait on it
+  const int32_t seqlen = a.seqlens[b];
+  const int tile = a.nsplit == 1 ? (int)blockIdx.x : (int)blockIdx.x / a.nsplit;
+  const int split = a.nsplit == 1 ? 0 : (int)blockIdx.x % a.nsplit;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -137,22 +139,48 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   __shared__ float s_l[kWaves][NQ];
   __shared__ float s_acc[kWaves][NQ][D];
 
+  // New rows of a drifting step are appended by tile 0 of split 0 (shared
+  // buffer only): rows [Lb, Lb + S) lie beyond every row this step reads, so
+  // they can be written as soon as Lb is known.  The sources do not depend on
+  // the plan and are loaded first.
+  constexpr int W16 = D * e / 16;
+  const bool appender = a.present_k != nullptr && tile == 0 && split == 0;
+  const bool early_append = appender && a.S * W16 <= kThreads;
+  u32x4 app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
+  if (early_append && tid < a.S * W16) {
+    const int64_t src = ((int64_t)(b * a.S + tid / W16) * a.Hkv + kvh) * D * e + (tid % W16) * 16;
+    app_k = *(const u32x4*)((const char*)a.k + src);
+    app_v = *(const u32x4*)((const char*)a.v + src);
+  }
+
   const int nq_item = a.S * a.group;
   const int q0 = tile * NQ;
-  // Query tile: (position, head) pairs q0 .. q0 + NQ - 1, position-major.
-  // Loaded before the plan: their addresses do not depend on seqlens_k.
+  // Query tile: (position, head) pairs q0 .. q0 + NQ - 1, position-major,
+  // walked with a carry (pairs past the item's last repeat it).  Loaded
+  // before the plan: their addresses do not depend on seqlens_k.
   const int i_first = q0 / a.group;
-  const int i_last = (min(q0 + NQ, nq_item) - 1) / a.group;
+  int i_last = i_first;
   uint32_t qw[NQ][4];
+  {
+    int h = q0 - i_first * a.group;
 #pragma unroll
-  for (int t = 0; t < NQ; ++t) {
-    const int qi = min(q0 + t, nq_item - 1);
-    const int i = qi / a.group, h = kvh * a.group + qi % a.group;
-    const uint4 v = *(const uint4*)((const char*)a.q +
-                                    ((((int64_t)b * a.S + i) * a.Hq + h) * D + sub * EPL) * e);
-    qw[t][0] = v.x; qw[t][1] = v.y; qw[t][2] = v.z; qw[t][3] = v.w;
+    for (int t = 0; t < NQ; ++t) {
+      const int64_t row = ((int64_t)b * a.S + i_last) * a.Hq + kvh * a.group + h;
+      const uint4 v = *(const uint4*)((const char*)a.q + (row * D + sub * EPL) * e);
+      qw[t][0] = v.x; qw[t][1] = v.y; qw[t][2] = v.z; qw[t][3] = v.w;
+      if (t + 1 < NQ && q0 + t + 1 < nq_item && ++h == a.group) {
+        h = 0;
+        ++i_last;
+      }
+    }
   }
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  const ItemPlan pl = plan_item(seqlen, a.S, a.C, a.gdiv, a.total);
+  if (early_append && pl.ok && pl.shift == 0 && tid < a.S * W16) {
+    const int64_t dst = ((int64_t)(b * a.Hkv + kvh) * a.C + pl.Lb + tid / W16) * D * e +
+                        (tid % W16) * 16;
+    *(u32x4*)((char*)a.present_k + dst) = app_k;
+    *(u32x4*)((char*)a.present_v + dst) = app_v;
+  }
 
   if (!pl.ok) {
     if (tid == 0 && tile == 0 && split == 0 && kvh == 0) flag_status(a.status, kStatusBadItem);
@@ -378,6 +406,12 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   int st = wave;
   if (nk == 0) {
     // empty split: nothing to read
+  } else if (nst <= kWaves) {
+    // at most one stage per wave: nothing to overlap
+    if (wave < nst) {
+      load_stage(wave, k0, v0);
+      compute_stage(wave, k0, v0);
+    }
   } else if constexpr (DEPTH == 3) {
     load_stage(st, k0, v0);
     uint32_t k2[U][4], v2[U][4];
@@ -458,11 +492,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
       }
     }
   }
-  // Appends on drifting steps with a shared buffer: rows [Lb, Lb + S) lie
-  // beyond every row attention reads, so they are written last, off the
-  // critical path of the loads above.
-  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
-    constexpr int W16 = D * e / 16;
+  // Appends of more rows than threads, after attention.
+  if (appender && !early_append && pl.shift == 0) {
     char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
     char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * e;
     for (int idx = tid; idx < a.S * W16; idx += kThreads) {

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
   const int rslot = lane / LPR;   // row slot within a wave step
   const int sub = lane % LPR;     // element chunk within the row
 
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   const int nq_item = a.S * a.group;
   const int q0 = tile * NQ;
 

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int D) {
   const int b = (int)(row / ((int64_t)a.S * a.Hq));
   const int d = threadIdx.x;
   if (d >= D) return;
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   float o = 0.0f;
   if (pl.ok) {
     float M = -INFINITY;

@@ -45,19 +45,50 @@ __host__ __device__ __forceinline__ int64_t resident_len(int64_t T, int64_t C,
   return T - G * ((T - C + G - 1) / G);
 }
 
-// The same for the lengths a step can see: T = seqlens_k + 1 <= 2^31 and
-// 1 <= W <= C < 2^31, so ceil((T - C) / G) = (T - C - 1) / G + 1 with a
-// 32-bit unsigned division (the 64-bit one is a long software sequence).
-__device__ __forceinline__ int64_t resident_len_step(int64_t T, int32_t C, int32_t W) {
-  if (T <= C) return T;
-  const uint32_t G = (uint32_t)(C - W + 1);
-  const uint32_t q = (uint32_t)(T - C - 1) / G + 1u;
-  return T - (int64_t)G * q;
+// Division by the gap G = C - W + 1, an invariant of the call, as a multiply
+// and two shifts (Granlund and Montgomery, "Division by Invariant Integers
+// using Multiplication", PLDI 1994, the round-up method for unsigned N-bit
+// division, N = 32): with l = ceil(log2 G), m = floor(2^32 (2^l - G) / G) + 1,
+// t = mulhi(m, n), the quotient floor(n / G) = (t + ((n - t) >> min(l, 1)))
+// >> max(l - 1, 0) for every 0 <= n < 2^32.  The magic is made on the host.
+struct GapDiv {
+  uint32_t G;
+  uint32_t magic;
+  uint32_t sh1, sh2;
+};
+
+inline GapDiv make_gap_div(uint32_t G) {  // 1 <= G < 2^31
+  uint32_t l = 0;
+  while ((1ull << l) < G) ++l;
+  GapDiv d;
+  d.G = G;
+  d.magic = (uint32_t)((((1ull << l) - G) << 32) / G + 1);
+  d.sh1 = l < 1 ? l : 1;
+  d.sh2 = l > 1 ? l - 1 : 0;
+  return d;
 }
 
-__device__ __forceinline__ ItemPlan plan_item(int32_t seqlen_k, int64_t S,
-                                              int32_t C, int32_t W,
-                                              int64_t total) {
+__host__ __device__ __forceinline__ uint32_t div_gap(uint32_t n, const GapDiv& d) {
+#ifdef __HIP_DEVICE_COMPILE__
+  const uint32_t t = __umulhi(d.magic, n);
+#else
+  const uint32_t t = (uint32_t)(((uint64_t)d.magic * n) >> 32);
+#endif
+  return (t + ((n - t) >> d.sh1)) >> d.sh2;
+}
+
+// L(T) for the lengths a step can see: 0 <= T <= 2^31 and 1 <= W <= C < 2^31,
+// so ceil((T - C) / G) = (T - C - 1) / G + 1 with a 32-bit numerator.
+__host__ __device__ __forceinline__ int64_t resident_len_step(int64_t T, int32_t C,
+                                                              const GapDiv& gd) {
+  if (T <= C) return T;
+  const uint32_t q = div_gap((uint32_t)(T - C - 1), gd) + 1u;
+  return T - (int64_t)gd.G * q;
+}
+
+__host__ __device__ __forceinline__ ItemPlan plan_item(int32_t seqlen_k, int64_t S,
+                                                       int32_t C, const GapDiv& gd,
+                                                       int64_t total) {
   ItemPlan pl;
   pl.T = (int64_t)seqlen_k + 1;
   pl.P = pl.T - S;
@@ -66,8 +97,8 @@ __device__ __forceinline__ ItemPlan plan_item(int32_t seqlen_k, int64_t S,
     pl.T = pl.P = pl.Lb = pl.La = pl.kept = pl.shift = -1;
     return pl;
   }
-  pl.Lb = resident_len_step(pl.P, C, W);
-  pl.La = resident_len_step(pl.T, C, W);
+  pl.Lb = resident_len_step(pl.P, C, gd);
+  pl.La = resident_len_step(pl.T, C, gd);
   pl.kept = pl.La - S;
   pl.shift = pl.Lb + S - pl.La;
   return pl;

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
   const int which = blockIdx.z;  // 0: key cache, 1: value cache
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.W, a.total);
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   if (!pl.ok) return;
 
   const void* past = which ? a.past_v : a.past_k;
@@ -89,10 +89,10 @@ __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
 }
 
 __global__ void plan_kernel(const int32_t* seqlens, int32_t B, int32_t S,
-                            int32_t C, int32_t W, int32_t total, int64_t* out) {
+                            int32_t C, int32_t W, GapDiv gdiv, int32_t total, int64_t* out) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
-  const ItemPlan pl = plan_item(seqlens[b], S, C, W, total);
+  const ItemPlan pl = plan_item(seqlens[b], S, C, gdiv, total);
   int64_t* o = out + 8 * (int64_t)b;
   if (!pl.ok) {
     for (int f = 0; f < 8; ++f) o[f] = -1;
@@ -127,7 +127,8 @@ hipError_t launch_writeback(const CopyArgs& a, hipStream_t st) {
 hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
                        int32_t W, int32_t total, int64_t* out, hipStream_t st) {
   const int threads = 64;
-  plan_kernel<<<(B + threads - 1) / threads, threads, 0, st>>>(seqlens, B, S, C, W, total, out);
+  plan_kernel<<<(B + threads - 1) / threads, threads, 0, st>>>(
+      seqlens, B, S, C, W, make_gap_div((uint32_t)(C - W + 1)), total, out);
   return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "swgqa_common.hpp"
+
 namespace swgqa {
 
 // Arguments shared by the attention kernels.  Pointers are device pointers;
@@ -28,6 +30,7 @@ struct AttnArgs {
   void* present_k;
   void* present_v;
   int32_t B, S, Hq, Hkv, C, W, total, group;
+  GapDiv gdiv;  // division by the gap C - W + 1
   int32_t ntiles, nsplit;
   float scale, softcap;
   int32_t bias_b, bias_h;
@@ -44,6 +47,7 @@ struct CopyArgs {
   void* present_v;
   const int32_t* seqlens;
   int32_t B, S, Hkv, C, W, total, D;
+  GapDiv gdiv;
   int32_t elem_bytes;
   int32_t skip_drifting;  // shared buffer and the append already fused
 };

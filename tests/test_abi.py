@@ -52,6 +52,32 @@ def test_resident_length_and_rollback_match_oracle():
     assert not sw.rollback_exact(5, 6, 8, 4)   # k > T
 
 
+def test_resident_length_full_32bit_range_matches_oracle():
+    """The library computes L(T) with a multiply-shift division by the gap
+    G = C - W + 1; pin it to the oracle's plain integer division over the
+    whole range a step can see (T <= 2^31, C < 2^31), powers of two and
+    their neighbours for G included."""
+    rng = np.random.default_rng(11)
+    top = 2**31 - 1
+    cases = []
+    for _ in range(20000):
+        C = int(rng.integers(1, top + 1))
+        W = int(rng.integers(1, C + 1))
+        T = int(rng.integers(0, 2**31 + 1))
+        cases.append((T, C, W))
+    for k in range(31):
+        for G in (2**k - 1, 2**k, 2**k + 1):
+            if not 1 <= G <= top:
+                continue
+            C = int(rng.integers(G, top + 1))
+            W = C - G + 1
+            for T in (0, C, C + 1, C + G, C + G + 1, 2**31, int(rng.integers(C, 2**31 + 1))):
+                cases.append((T, C, W))
+    cases += [(2**31, top, 1), (2**31, top, top), (2**31 - 5, 7, 7), (123456789, 1, 1)]
+    for T, C, W in cases:
+        assert sw.resident_length(T, C, W) == oracle.resident_length(T, C, W), (T, C, W)
+
+
 def test_workspace_size():
     p = sw.make_params(32, 1, 32, 8, 128, 4608, 4096, 40000, sw.BF16)
     n = sw.workspace_size(p)
