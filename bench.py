@@ -48,15 +48,18 @@ class Workload:
         self.C, self.W, self.dtype, self.scale, self.softcap, self.seed = C, W, dtype, scale, softcap, seed
         self.e = 4 if dtype == 0 else 2
 
-    def step_bytes(self, T: np.ndarray, S: int, sw) -> dict:
+    def step_bytes(self, T: np.ndarray, S: int, sw, bias: bool = False) -> dict:
         """Algorithmic HBM bytes of one step for items with lengths T (after
         the step): distinct K/V rows the queries read, Q read, output write,
-        appended rows, and rows moved by block compaction (read + write)."""
+        appended rows, rows moved by block compaction (read + write), and the
+        attention_bias entries of visible keys."""
         row = self.D * self.e
         P = T - S
         n_kv = np.minimum(T, self.W + S - 1)
         kv_read = int(np.sum(self.Hkv * 2 * n_kv * row))
         qo = 2 * len(T) * S * self.Hq * row
+        if bias:
+            qo += int(np.sum(self.visible_keys(T, S))) * self.Hq * self.e
         La = np.array([sw.resident_length(int(t), self.C, self.W) for t in T])
         Lb = np.array([sw.resident_length(int(p), self.C, self.W) for p in P])
         shift = Lb + S - La
@@ -65,6 +68,16 @@ class Workload:
         moved = int(np.sum(np.where((shift > 0) & (kept > 0), self.Hkv * 2 * 2 * kept * row, 0)))
         return {"kv_read": kv_read, "qo": qo, "append": append, "compaction": moved,
                 "total": kv_read + qo + append + moved}
+
+
+    def visible_keys(self, T: np.ndarray, S: int) -> np.ndarray:
+        """Per item: sum over its S queries of the keys each one sees."""
+        P = (np.asarray(T) - S)[:, None] + np.arange(S)[None, :]  # query positions
+        return np.minimum(P + 1, self.W).sum(axis=1)
+
+    def step_flops(self, T: np.ndarray, S: int) -> int:
+        """QK^T and PV multiply-adds over the visible (query, key) pairs, x2."""
+        return int(4 * self.D * self.Hq * np.sum(self.visible_keys(T, S)))
 
 
 def storage_torch_dtype(torch, dtype):
@@ -79,28 +92,31 @@ def to_dev(torch, a):
 
 
 class DecodeLoop:
-    """Device-resident decode loop: inputs for every step staged in HBM, one
-    C-ABI call per step with precomputed arguments."""
+    """Device-resident loop of steps of S tokens each: inputs for every step
+    staged in HBM, one C-ABI call per step with precomputed arguments."""
 
-    def __init__(self, torch, sw, wl: Workload, P0: np.ndarray, nsteps: int, K, V):
+    def __init__(self, torch, sw, wl: Workload, P0: np.ndarray, nsteps: int, K, V,
+                 S: int = 1, bias=None, total: int | None = None):
         import synth
         self.torch, self.sw, self.wl = torch, sw, wl
-        self.nsteps = nsteps
+        self.nsteps, self.S = nsteps, S
         syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
         B = wl.B
         qs, ks, vs = [], [], []
         for s in range(nsteps):
-            q, k, v = syn.step_inputs(P0 + s, 1)
+            q, k, v = syn.step_inputs(P0 + s * S, S)
             qs.append(q), ks.append(k), vs.append(v)
-        self.q = to_dev(torch, np.stack(qs))        # (n, B, 1, Hq*D)
+        self.q = to_dev(torch, np.stack(qs))        # (n, B, S, Hq*D)
         self.k = to_dev(torch, np.stack(ks))
         self.v = to_dev(torch, np.stack(vs))
-        self.seq = to_dev(torch, (P0[None, :] + np.arange(nsteps)[:, None]).astype(np.int32))
+        self.seq = to_dev(torch, (P0[None, :] + S * np.arange(nsteps)[:, None] + S - 1)
+                          .astype(np.int32))
         self.out = torch.empty_like(self.q)
         self.K, self.V = K, V
-        self.T = P0[None, :] + np.arange(nsteps)[:, None] + 1
-        total = int(self.T.max())
-        self.p = sw.make_params(B, 1, wl.Hq, wl.Hkv, wl.D, wl.C, wl.W, total, wl.dtype,
+        self.bias = bias
+        self.T = P0[None, :] + S * (np.arange(nsteps)[:, None] + 1)
+        total = int(self.T.max()) if total is None else total
+        self.p = sw.make_params(B, S, wl.Hq, wl.Hkv, wl.D, wl.C, wl.W, total, wl.dtype,
                                 wl.scale, wl.softcap)
         nbytes = sw.workspace_size(self.p)
         self.ws = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda:0")
@@ -108,12 +124,13 @@ class DecodeLoop:
         lib = sw.load()
         self.fn = lib.swgqa_forward
         vp = ctypes.c_void_p
+        bp = None if bias is None else vp(bias.data_ptr())
         self.args = []
         for s in range(nsteps):
             self.args.append((ctypes.byref(self.p), vp(self.q[s].data_ptr()),
                               vp(self.k[s].data_ptr()), vp(self.v[s].data_ptr()),
                               vp(K.data_ptr()), vp(V.data_ptr()), vp(self.seq[s].data_ptr()),
-                              None, vp(self.out[s].data_ptr()), vp(K.data_ptr()),
+                              bp, vp(self.out[s].data_ptr()), vp(K.data_ptr()),
                               vp(V.data_ptr()), vp(self.ws.data_ptr()),
                               ctypes.c_size_t(nbytes)))
 
@@ -130,7 +147,11 @@ class DecodeLoop:
                 raise RuntimeError(f"swgqa_forward failed at step {s}: {self.sw.status_string(rc)}")
 
     def bytes_per_step(self):
-        return [self.wl.step_bytes(self.T[s], 1, self.sw) for s in range(self.nsteps)]
+        return [self.wl.step_bytes(self.T[s], self.S, self.sw, self.bias is not None)
+                for s in range(self.nsteps)]
+
+    def flops_per_step(self):
+        return [self.wl.step_flops(self.T[s], self.S) for s in range(self.nsteps)]
 
 
 def time_decode(torch, loop: DecodeLoop, snapshot, use_graph: bool):
@@ -352,6 +373,89 @@ def cpu_baseline(wl: Workload, P: int, max_steps: int, seconds: float):
             "ms_per_step": round(t_used / n * 1e3, 3)}
 
 
+def loop_stats(torch, loop: DecodeLoop, snap, tokens_per_step: int):
+    """Graph-replayed step time and throughput of a step loop, plus the eager
+    per-step event times split by whether the step compacted."""
+    r = time_decode(torch, loop, snap, True)
+    graph = bool(r.get("graph_ok") and r["graph_s"])
+    step_ms = r["graph_kernel_ms"] if graph else float(np.mean(r["step_ms"]))
+    wall = r["graph_s"] if graph else r["eager_s"]
+    byts = loop.bytes_per_step()
+    compacting = np.array([b["compaction"] > 0 for b in byts])
+    eager_us = r["step_ms"] * 1e3
+    out = {"mode": "hip_graph" if graph else "eager",
+           "tokens_per_s": round(tokens_per_step * loop.nsteps / wall, 1),
+           "step_us": round(step_ms * 1e3, 3),
+           "steps": loop.nsteps,
+           "compacting_steps": int(compacting.sum()),
+           "eager_step_us_p50": round(float(np.median(eager_us)), 3)}
+    if compacting.any() and (~compacting).any():
+        out["eager_step_us_p50_compacting"] = round(float(np.median(eager_us[compacting])), 3)
+        out["eager_step_us_p50_drifting"] = round(float(np.median(eager_us[~compacting])), 3)
+    total = sum(b["total"] for b in byts) / loop.nsteps
+    kv = sum(b["kv_read"] for b in byts) / loop.nsteps
+    moved = sum(b["compaction"] for b in byts) / loop.nsteps
+    out["hbm"] = {"algorithmic_bytes_per_step": int(total), "kv_read_bytes_per_step": int(kv),
+                  "compaction_bytes_per_step": int(moved),
+                  "achieved_GBps": round(total / (step_ms / 1e3) / 1e9, 2),
+                  "frac_of_peak": round(total / (step_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 5)}
+    return out, step_ms
+
+
+def small_slack(torch, sw):
+    """B=1, 64 Q / 8 KV heads x 64, fp32, W=128, C=136 (G=9): 400 decode
+    steps after a 512-token prompt, a block compaction every 9 steps."""
+    wl = Workload("small_slack", B=1, Hq=64, Hkv=8, D=64, C=136, W=128, dtype=0,
+                  scale=0.125, seed=1003)
+    P0 = np.array([512])
+    K, V = seeded_cache(torch, sw, wl, P0)
+    snap = (K.clone(), V.clone())
+    loop = DecodeLoop(torch, sw, wl, P0, 400, K, V)
+    loop.run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    out, _ = loop_stats(torch, loop, snap, 1)
+    out["workload"] = ("decode after a 512-token prompt, B=1, 64 Q / 8 KV heads x 64, fp32, "
+                       "W=128, C=136 (G=9), 400 steps")
+    return out
+
+
+def chunked_and_verify(torch, sw):
+    """B=4, 32 Q / 8 KV heads x 128, fp16, W=1024, C=1032, fp16 attention_bias
+    N(0, 0.1) of width total_sequence_length: 32-token prompt chunks on items
+    whose past lengths are uniform in [1024, 4096] (multi-token steps on the
+    matrix cores), then verify steps of 8 draft tokens."""
+    import synth
+    wl = Workload("chunked_verify", B=4, Hq=32, Hkv=8, D=128, C=1032, W=1024, dtype=1,
+                  seed=1004)
+    rng = np.random.default_rng(1004)
+    P0 = rng.integers(1024, 4097, size=4)
+    nchunk, nverify = 32, 64
+    total = int(P0.max()) + 32 * nchunk + 8 * nverify + 8
+    syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
+    res = []
+    for S, nsteps, start in ((32, nchunk, P0), (8, nverify, P0 + 32 * nchunk)):
+        bias = to_dev(torch, synth.to_storage(
+            syn.bias_f32(np.arange(4), np.zeros(4, np.int64), S, total), wl.dtype))
+        K, V = seeded_cache(torch, sw, wl, start)
+        snap = (K.clone(), V.clone())
+        loop = DecodeLoop(torch, sw, wl, start, nsteps, K, V, S=S, bias=bias, total=total)
+        loop.run(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        out, step_ms = loop_stats(torch, loop, snap, 4 * S)
+        flops = float(np.mean(loop.flops_per_step()))
+        peak = 2500.0  # dense fp16 MFMA, TFLOP/s
+        out["mfma"] = {"achieved_TFLOPs": round(flops / (step_ms / 1e3) / 1e12, 3),
+                       "peak_TFLOPs": peak,
+                       "frac": round(flops / (step_ms / 1e3) / 1e12 / peak, 5),
+                       "flops_per_step": int(flops)}
+        out["workload"] = (f"B=4 steps of {S} tokens, 32 Q / 8 KV heads x 128, fp16 cache, "
+                           f"W=1024, C=1032, fp16 bias, past lengths U[1024, 4096]"
+                           + (", all drafts accepted" if S == 8 else ""))
+        res.append(out)
+        del loop, K, V, snap, bias
+    return res[0], res[1]
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -365,6 +469,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=512)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the small-slack, chunked-prefill and verify workloads")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -474,6 +580,12 @@ def main():
             "roofline": srl,
         }
         del Ks, Vs, ssnap, sloop
+
+    if not args.no_extra:
+        log("small-slack decode ...")
+        result["small_slack"] = small_slack(torch, sw)
+        log("chunked prefill and verify ...")
+        result["chunked_prefill"], result["verify"] = chunked_and_verify(torch, sw)
 
     result["copy_reference"] = copy_reference(torch, args.copy_mib)
 

@@ -12,20 +12,18 @@
 // This kernel runs after attention on the same stream, so in the shared
 // buffer mode (present == past) no row a query reads is overwritten early.
 // In place, the move [shift, Lb) -> [0, kept) overlaps itself whenever
-// kept > shift; it is done by one workgroup per (item, KV head, K|V) in
-// passes of at most `shift` rows with a barrier between passes: a pass's
-// destination rows were sources only of earlier passes, whose loads have
-// completed.  The append waits for the whole move, since new rows may land on
-// rows the move still reads.
+// kept > shift; it is done by one workgroup per (item, KV head, K|V) with the
+// pass-wise register-staged move of swgqa_tail.hpp.  The append waits for
+// the whole move, since new rows may land on rows the move still reads.
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
+#include "swgqa_tail.hpp"
 
 namespace swgqa {
 
 namespace {
 
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;   // 16-byte words per thread per pass
 
 __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
   const int kvh = blockIdx.x;
@@ -50,25 +48,7 @@ __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
   // 1. Surviving old rows: [shift, shift + kept) -> [0, kept).
   if (pl.kept > 0 && (!shared || pl.shift > 0)) {
     if (shared) {
-      const int64_t cap_rows = (int64_t)kCopyThreads * kCopyUnroll / w16;
-      const int64_t pass = pl.shift < cap_rows ? pl.shift : (cap_rows > 0 ? cap_rows : 1);
-      for (int64_t r0 = 0; r0 < pl.kept; r0 += pass) {
-        const int64_t nr = pl.kept - r0 < pass ? pl.kept - r0 : pass;
-        const int64_t nw = nr * w16;
-        u32x4 buf[kCopyUnroll];
-#pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-          const int64_t idx = tid + (int64_t)u * kCopyThreads;
-          if (idx < nw) buf[u] = src[(pl.shift + r0) * w16 + idx];
-        }
-#pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-          const int64_t idx = tid + (int64_t)u * kCopyThreads;
-          if (idx < nw) dst[r0 * w16 + idx] = buf[u];
-        }
-        // every load of this pass completes before the next pass stores
-        __syncthreads();
-      }
+      move_rows_in_place(dst, nullptr, w16, pl.shift, pl.kept, tid, kCopyThreads);
     } else {
       const int64_t nw = pl.kept * w16;
       for (int64_t idx = tid; idx < nw; idx += kCopyThreads)

@@ -18,29 +18,39 @@
 
 namespace swgqa {
 
-constexpr int kMoveUnroll = 16;  // 16-byte words per thread per pass
+constexpr int kMoveUnroll = 16;  // 16-byte words per thread and tensor per pass
 
-// In-place move of one cache slice, rows [shift, shift + kept) -> [0, kept),
-// in passes of at most `shift` rows: a pass's destination rows were sources
-// only of earlier passes, whose loads completed before the barrier.
-__device__ __forceinline__ void move_rows_in_place(u32x4* slice, int64_t w16, int64_t shift,
-                                                   int64_t kept, int tid, int nthr) {
+// In-place move of rows [shift, shift + kept) -> [0, kept) of the K slice and,
+// if `v` is not null, of the V slice at the same offsets.  Passes take as many
+// rows as the workgroup holds in registers: every load of a pass is issued
+// (clamped to a valid word), then -- if the pass is longer than `shift`, so
+// that its destinations overlap its own sources -- a barrier, then its
+// stores, then a barrier before the next pass, whose destinations are this
+// pass's sources.
+__device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w16,
+                                                   int64_t shift, int64_t kept, int tid,
+                                                   int nthr) {
   const int64_t cap_rows = (int64_t)nthr * kMoveUnroll / w16;
-  const int64_t pass = shift < cap_rows ? shift : (cap_rows > 0 ? cap_rows : 1);
+  const int64_t pass = cap_rows > 0 ? cap_rows : 1;
   for (int64_t r0 = 0; r0 < kept; r0 += pass) {
     const int64_t nr = kept - r0 < pass ? kept - r0 : pass;
     const int64_t nw = nr * w16;
-    // all loads of the pass first (clamped to a valid word), then the stores
-    u32x4 buf[kMoveUnroll];
+    u32x4 bk[kMoveUnroll], bv[kMoveUnroll];
 #pragma unroll
     for (int u = 0; u < kMoveUnroll; ++u) {
       const int64_t idx = tid + (int64_t)u * nthr;
-      buf[u] = slice[(shift + r0) * w16 + (idx < nw ? idx : nw - 1)];
+      const int64_t at = (shift + r0) * w16 + (idx < nw ? idx : nw - 1);
+      bk[u] = k[at];
+      if (v) bv[u] = v[at];
     }
+    if (nr > shift) __syncthreads();
 #pragma unroll
     for (int u = 0; u < kMoveUnroll; ++u) {
       const int64_t idx = tid + (int64_t)u * nthr;
-      if (idx < nw) slice[r0 * w16 + idx] = buf[u];
+      if (idx < nw) {
+        k[r0 * w16 + idx] = bk[u];
+        if (v) v[r0 * w16 + idx] = bv[u];
+      }
     }
     __syncthreads();
   }
@@ -55,10 +65,9 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   if (pl.shift > 0) {
-    if (pl.kept > 0) {
-      move_rows_in_place((u32x4*)((char*)a.present_k + off), w16, pl.shift, pl.kept, tid, nthr);
-      move_rows_in_place((u32x4*)((char*)a.present_v + off), w16, pl.shift, pl.kept, tid, nthr);
-    }
+    if (pl.kept > 0)
+      move_rows_in_place((u32x4*)((char*)a.present_k + off), (u32x4*)((char*)a.present_v + off),
+                         w16, pl.shift, pl.kept, tid, nthr);
     // new rows after the move (they may land on rows the move read)
     const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
     const int64_t nw = (a.S - i0) * w16;
