@@ -37,8 +37,17 @@ constexpr int64_t kMaxSliceCounters = (int64_t)((kHeaderBytes - kStatusBytes) / 
 #endif
 constexpr int kTargetWorkgroups = SWGQA_TARGET_WORKGROUPS;
 constexpr int kMinKeysPerSplit = 32;
+// Multi-token steps with at least this many query rows per KV head
+// ((position, head) pairs) run on the matrix cores.
+#ifndef SWGQA_CHUNK_MIN_ROWS
+#define SWGQA_CHUNK_MIN_ROWS 32
+#endif
+#ifndef SWGQA_CHUNK_MIN_WORKGROUPS
+#define SWGQA_CHUNK_MIN_WORKGROUPS 256
+#endif
 constexpr int kChunkMinTokens = 16;       // steps of at least this many tokens use MFMA
-constexpr int64_t kChunkMinWorkgroups = 256;
+constexpr int kChunkMinRows = SWGQA_CHUNK_MIN_ROWS;
+constexpr int64_t kChunkMinWorkgroups = SWGQA_CHUNK_MIN_WORKGROUPS;
 constexpr int64_t kWholeSliceMinTiles = SWGQA_WHOLE_SLICE_MIN_TILES;
 constexpr int64_t kWholeSliceMaxKeys = SWGQA_WHOLE_SLICE_MAX_KEYS;
 constexpr int64_t kDecodeMinWorkgroups = SWGQA_DECODE_MIN_WORKGROUPS;
@@ -76,7 +85,9 @@ SplitPlan plan_split(const swgqa_params* p) {
   const int group = p->num_heads / p->kv_num_heads;
   const int per_kv = p->sequence_length * group;  // queries per (item, KV head)
   s.waves = 4;
-  if (p->sequence_length >= kChunkMinTokens && chunk_kernel_supports(p->dtype, p->head_size)) {
+  const bool multi_token = p->sequence_length >= kChunkMinTokens ||
+                           (p->sequence_length >= 2 && per_kv >= kChunkMinRows);
+  if (multi_token && chunk_kernel_supports(p->dtype, p->head_size)) {
     // multi-token step on the matrix cores
     s.kind = Kind::kChunk;
     s.nq = chunk_rows_per_workgroup();

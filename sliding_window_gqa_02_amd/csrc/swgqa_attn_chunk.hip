@@ -70,13 +70,20 @@ template <int DT> struct LdsT { using T = float; };
 template <> struct LdsT<kF16> { using T = uint16_t; };
 template <> struct LdsT<kBF16> { using T = uint16_t; };
 
+// Key swizzle of row d of the transposed V tile (16-bit types): XOR of key
+// bits 2..4 with d / 8, so groups of 4 consecutive keys stay contiguous.
+__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) << 2; }
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   union { _Float16 h; uint16_t u; } c;
   c.h = (_Float16)x;
   return c.u;
 }
 
-template <int DT, int D>
+// BIAS: attention_bias present (a separate instantiation, so that the loads
+// of a block are the same on every path and the compiler can wait for
+// exactly the block it stages).
+template <int DT, int D, bool BIAS>
 __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
   using Sh = ChunkShape<DT, D>;
   using LT = typename LdsT<DT>::T;
@@ -167,35 +174,54 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
   const uint64_t nv = (uint64_t)((const char*)a.v + (((int64_t)b * a.S) * a.Hkv + kvh) * D * e);
   const int64_t new_stride = (int64_t)a.Hkv * D * e;
 
-  // Block loads into registers: chunk c of the block = key c / CPR, 16-byte
-  // part c % CPR.  Keys outside [kb, ke) load zeros.
-  u32x4 rk[CPT], rv[CPT];
-  auto load_block = [&](int64_t j0) __attribute__((always_inline)) {
+  const bool has_cap = a.softcap > 0.0f;
+  const float cap = a.softcap;
+  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
+  constexpr bool has_bias = BIAS;
+  const int64_t bias_row = has_bias
+      ? ((((a.bias_b ? (int64_t)b : 0) * (a.bias_h ? a.Hq : 1) + (a.bias_h ? my_h : 0)) * a.S + my_i) *
+         (int64_t)a.total)
+      : 0;
+
+  // Block loads into registers, issued unconditionally (so the compiler can
+  // wait for exactly the loads it needs): chunk c of the block = key c / CPR,
+  // 16-byte part c % CPR; keys past the band's end are clamped to its last
+  // key (finite data the mask removes); chunks past the block repeat the last
+  // one and are not stored.  The attention_bias entries this lane scores in
+  // the block (keys j0 + 16 kt + 4 lg + r) come with them.
+  struct BlockRegs {
+    u32x4 k[CPT], v[CPT];
+    float bias[8];
+  };
+  auto load_block = [&](int64_t j0, BlockRegs& rg) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * kThreads;
+      const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
       const int key = c / CPR, part = c % CPR;
-      const int64_t j = j0 + key;
-      u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (c < Sh::CHUNKS && j < ke) {
-        const bool in_cache = j < pl.P;
-        const uint64_t msk = 0ull - (uint64_t)in_cache;
-        const uint64_t off_c = (uint64_t)((j - base) * D * e + part * 16);
-        const uint64_t off_n = (uint64_t)((j - pl.P) * new_stride + part * 16);
-        const uint64_t ka = ((ck + off_c) & msk) | ((nk + off_n) & ~msk);
-        const uint64_t va = ((cv + off_c) & msk) | ((nv + off_n) & ~msk);
-        kk = load16_global<false>(ka);
-        vv = load16_global<false>(va);
-      }
-      rk[u] = kk;
-      rv[u] = vv;
+      const int64_t j = min(j0 + key, ke - 1);
+      const bool in_cache = j < pl.P;
+      const uint64_t msk = 0ull - (uint64_t)in_cache;
+      const uint64_t off_c = (uint64_t)((j - base) * D * e + part * 16);
+      const uint64_t off_n = (uint64_t)((j - pl.P) * new_stride + part * 16);
+      const uint64_t ka = ((ck + off_c) & msk) | ((nk + off_n) & ~msk);
+      const uint64_t va = ((cv + off_c) & msk) | ((nv + off_n) & ~msk);
+      rg.k[u] = load16_global<false>(ka);
+      rg.v[u] = load16_global<false>(va);
+    }
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          rg.bias[kt * 4 + r] = load_one<DT>(a.bias, bias_row + min(j0 + kt * 16 + 4 * lg + r, ke - 1));
     }
   };
-  auto store_block = [&]() __attribute__((always_inline)) {
+  auto store_block = [&](const BlockRegs& rg) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = tid + u * kThreads;
-      if (c >= Sh::CHUNKS) continue;
+      if constexpr (Sh::CHUNKS % kThreads != 0)
+        if (c >= Sh::CHUNKS) continue;
       const int key = c / CPR, part = c % CPR;
       const int d0 = part * (16 / e);
       if constexpr (DT == kF32) {
@@ -203,31 +229,29 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
         float* vd = (float*)sV + key * VS + d0;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          kd[w] = __uint_as_float(rk[u][w]);
-          vd[w] = __uint_as_float(rv[u][w]);
+          kd[w] = __uint_as_float(rg.k[u][w]);
+          vd[w] = __uint_as_float(rg.v[u][w]);
         }
       } else {
-        uint32_t* kd = (uint32_t*)((uint16_t*)sK + key * KS + d0);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) kd[w] = rk[u][w];
-        // V transposed: sV[d][key]
+        // K rows are 16-byte aligned: one store per chunk
+        *(u32x4*)((uint16_t*)sK + key * KS + d0) = rg.k[u];
+        // V transposed, sV[d][key ^ swz(d)]: the 16 parts of a key row land
+        // on rows 8 apart, which the swizzle spreads over the banks
+        const int kx = key ^ vt_swizzle(d0);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          ((uint16_t*)sV)[(d0 + 2 * w) * VS + key] = (uint16_t)(rv[u][w] & 0xFFFFu);
-          ((uint16_t*)sV)[(d0 + 2 * w + 1) * VS + key] = (uint16_t)(rv[u][w] >> 16);
+          ((uint16_t*)sV)[(d0 + 2 * w) * VS + kx] = (uint16_t)(rg.v[u][w] & 0xFFFFu);
+          ((uint16_t*)sV)[(d0 + 2 * w + 1) * VS + kx] = (uint16_t)(rg.v[u][w] >> 16);
         }
       }
     }
   };
 
-  const bool has_cap = a.softcap > 0.0f;
-  const float cap = a.softcap;
-  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
-  const bool has_bias = a.bias != nullptr;
-  const int64_t bias_row = has_bias
-      ? ((((a.bias_b ? (int64_t)b : 0) * (a.bias_h ? a.Hq : 1) + (a.bias_h ? my_h : 0)) * a.S + my_i) *
-         (int64_t)a.total)
-      : 0;
+  // visibility of key kb + jr for this lane's query, as 32-bit bounds on jr
+  const int64_t vlo = my_pos - a.W + 1 - kb;
+  const int64_t vhi = (my_pos < ke - 1 ? my_pos : ke - 1) - kb;
+  const int32_t vis_lo = my_ok ? (int32_t)(vlo < -(int64_t)0x7fffffff ? -0x7fffffff : vlo) : 1;
+  const int32_t vis_hi = my_ok ? (int32_t)vhi : 0;
 
   float m_run = -INFINITY;  // log2 units, per query (same in all 4 lane groups)
   float l_run = 0.0f;       // this lane's share of the sum
@@ -236,14 +260,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
   for (int t = 0; t < DT16; ++t) o[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nblocks = ke > kb ? (int)((ke - kb + BN - 1) / BN) : 0;
-  if (nblocks > 0) load_block(kb);
-  for (int blk = 0; blk < nblocks; ++blk) {
-    const int64_t j0 = kb + (int64_t)blk * BN;
-    __syncthreads();  // previous block's LDS reads are done
-    store_block();
-    __syncthreads();
-    if (blk + 1 < nblocks) load_block(j0 + BN);
-
+  // One block: scores, online softmax, PV, from the block staged in LDS.
+  auto compute_block = [&](int blk, const float* bias_blk) __attribute__((always_inline)) {
     // S^T for the two 16-key tiles of the block
     f4 sc[2];
 #pragma unroll
@@ -279,8 +297,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t j = j0 + kt * 16 + 4 * lg + r;
-        const bool vis = my_ok && j < ke && j <= my_pos && j > my_pos - a.W;
+        const int32_t jr = blk * BN + kt * 16 + 4 * lg + r;
+        const bool vis = jr >= vis_lo && jr <= vis_hi;
         float x = sc[kt][r] * a.scale;
         if (has_cap) {
           const float y = x * inv_cap;
@@ -292,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
             x = cap * copysignf(t, y);
           }
         }
-        if (has_bias && vis) x += load_one<DT>(a.bias, bias_row + j);
+        if (has_bias) x += bias_blk[kt * 4 + r];
         x = vis ? x * kLog2e : -INFINITY;
         sc[kt][r] = x;
         smax = fmaxf(smax, x);
@@ -348,7 +366,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {
-          const uint2 vv = *(const uint2*)((const uint16_t*)sV + (16 * dt + lq) * VS + kt * 16 + 4 * lg);
+          const uint2 vv = *(const uint2*)((const uint16_t*)sV + (16 * dt + lq) * VS +
+                                           ((kt * 16 + 4 * lg) ^ vt_swizzle(16 * dt + lq)));
           if constexpr (DT == kF16) {
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
                 __builtin_bit_cast(h4, vv), __builtin_bit_cast(h4, make_uint2(pw[0], pw[1])), o[dt],
@@ -363,6 +382,34 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
           }
         }
       }
+    }
+  };
+  // A block's K/V/bias loads are issued three blocks ahead (register ring of
+  // three), so two blocks of loads stay in flight while one is computed;
+  // blocks past the band's end reload its last block.
+  auto block_start = [&](int blk) { return kb + (int64_t)min(blk, nblocks - 1) * BN; };
+  auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
+    __syncthreads();  // the previous block's LDS reads are done
+    store_block(rg);
+    float bias_blk[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) bias_blk[r] = has_bias ? rg.bias[r] : 0.0f;
+    __syncthreads();
+    load_block(block_start(blk + 3), rg);
+    compute_block(blk, bias_blk);
+  };
+  if (nblocks > 0) {
+    BlockRegs r0, r1, r2;
+    load_block(block_start(0), r0);
+    load_block(block_start(1), r1);
+    load_block(block_start(2), r2);
+    for (int blk = 0; blk < nblocks;) {
+      step(blk, r0);
+      if (++blk >= nblocks) break;
+      step(blk, r1);
+      if (++blk >= nblocks) break;
+      step(blk, r2);
+      ++blk;
     }
   }
 
@@ -421,7 +468,10 @@ template <int DT, int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   if constexpr (ChunkShape<DT, D>::ok) {
     const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
-    attn_chunk_kernel<DT, D><<<grid, kThreads, 0, st>>>(a);
+    if (a.bias)
+      attn_chunk_kernel<DT, D, true><<<grid, kThreads, 0, st>>>(a);
+    else
+      attn_chunk_kernel<DT, D, false><<<grid, kThreads, 0, st>>>(a);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

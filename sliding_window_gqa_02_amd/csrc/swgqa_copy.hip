@@ -25,10 +25,21 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 
+// Column parts per row: the workgroups of one (item, KV head, K|V) slice
+// each move a disjoint set of 16-byte words of every row, so they need no
+// ordering between them.
+__host__ __device__ inline int writeback_columns(int w16) { return w16 < 4 ? w16 : 4; }
+
 __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  const int which = blockIdx.z;  // 0: key cache, 1: value cache
+  const int64_t rowb = (int64_t)a.D * a.elem_bytes;
+  const int64_t w16 = rowb / 16;  // 16-byte words per row (a power of two)
+  const int ncol = writeback_columns((int)w16);
+  const int which = blockIdx.z / ncol;  // 0: key cache, 1: value cache
+  const int col = blockIdx.z % ncol;
+  const int64_t wn = w16 / ncol;        // words of each row this workgroup moves
+  const int wlog = __builtin_ctzll(wn);
   const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   if (!pl.ok) return;
 
@@ -38,32 +49,32 @@ __global__ __launch_bounds__(kCopyThreads) void writeback_kernel(CopyArgs a) {
   const bool shared = present == past;
   if (shared && pl.shift == 0 && a.skip_drifting) return;  // appended by attention
 
-  const int64_t rowb = (int64_t)a.D * a.elem_bytes;
-  const int64_t w16 = rowb / 16;  // 16-byte words per row
   const int64_t slice = ((int64_t)b * a.Hkv + kvh) * a.C * rowb;
-  const u32x4* src = (const u32x4*)((const char*)past + slice);
-  u32x4* dst = (u32x4*)((char*)present + slice);
+  const u32x4* src = (const u32x4*)((const char*)past + slice) + col * wn;
+  u32x4* dst = (u32x4*)((char*)present + slice) + col * wn;
   const int tid = threadIdx.x;
 
   // 1. Surviving old rows: [shift, shift + kept) -> [0, kept).
   if (pl.kept > 0 && (!shared || pl.shift > 0)) {
     if (shared) {
-      move_rows_in_place(dst, nullptr, w16, pl.shift, pl.kept, tid, kCopyThreads);
+      move_rows_in_place(dst, nullptr, w16, wlog, pl.shift, pl.kept, tid, kCopyThreads);
     } else {
-      const int64_t nw = pl.kept * w16;
-      for (int64_t idx = tid; idx < nw; idx += kCopyThreads)
-        dst[idx] = src[pl.shift * w16 + idx];
+      const int64_t nw = pl.kept * wn;
+      for (int64_t idx = tid; idx < nw; idx += kCopyThreads) {
+        const int64_t r = idx >> wlog, w = idx & (wn - 1);
+        dst[r * w16 + w] = src[(pl.shift + r) * w16 + w];
+      }
     }
   }
   __syncthreads();
 
   // 2. New rows i in [max(0, -kept), S) -> row kept + i.
   const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
-  const int64_t nw = (a.S - i0) * w16;
+  const int64_t nw = (a.S - i0) * wn;
   for (int64_t idx = tid; idx < nw; idx += kCopyThreads) {
-    const int64_t i = i0 + idx / w16;
-    const int64_t w = idx % w16;
-    const u32x4* s = (const u32x4*)(fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb);
+    const int64_t i = i0 + (idx >> wlog);
+    const int64_t w = idx & (wn - 1);
+    const u32x4* s = (const u32x4*)(fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb) + col * wn;
     dst[(pl.kept + i) * w16 + w] = s[w];
   }
 }
@@ -99,7 +110,7 @@ __global__ void zero_words_kernel(uint32_t* words, size_t n) {
 }  // namespace
 
 hipError_t launch_writeback(const CopyArgs& a, hipStream_t st) {
-  const dim3 grid(a.Hkv, a.B, 2);
+  const dim3 grid(a.Hkv, a.B, 2 * writeback_columns(a.D * a.elem_bytes / 16));
   writeback_kernel<<<grid, kCopyThreads, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -21,25 +21,28 @@ namespace swgqa {
 constexpr int kMoveUnroll = 16;  // 16-byte words per thread and tensor per pass
 
 // In-place move of rows [shift, shift + kept) -> [0, kept) of the K slice and,
-// if `v` is not null, of the V slice at the same offsets.  Passes take as many
+// if `v` is not null, of the V slice at the same offsets; rows are `w16`
+// 16-byte words apart and words [0, 2^wlog) of each row move (a column part
+// of the row when several workgroups share a slice).  Passes take as many
 // rows as the workgroup holds in registers: every load of a pass is issued
 // (clamped to a valid word), then -- if the pass is longer than `shift`, so
 // that its destinations overlap its own sources -- a barrier, then its
 // stores, then a barrier before the next pass, whose destinations are this
 // pass's sources.
-__device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w16,
+__device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w16, int wlog,
                                                    int64_t shift, int64_t kept, int tid,
                                                    int nthr) {
-  const int64_t cap_rows = (int64_t)nthr * kMoveUnroll / w16;
+  const int64_t cap_rows = ((int64_t)nthr * kMoveUnroll) >> wlog;
   const int64_t pass = cap_rows > 0 ? cap_rows : 1;
+  const int64_t wmask = ((int64_t)1 << wlog) - 1;
   for (int64_t r0 = 0; r0 < kept; r0 += pass) {
     const int64_t nr = kept - r0 < pass ? kept - r0 : pass;
-    const int64_t nw = nr * w16;
+    const int64_t nw = nr << wlog;
     u32x4 bk[kMoveUnroll], bv[kMoveUnroll];
 #pragma unroll
     for (int u = 0; u < kMoveUnroll; ++u) {
-      const int64_t idx = tid + (int64_t)u * nthr;
-      const int64_t at = (shift + r0) * w16 + (idx < nw ? idx : nw - 1);
+      const int64_t idx = min(tid + (int64_t)u * nthr, nw - 1);
+      const int64_t at = (shift + r0 + (idx >> wlog)) * w16 + (idx & wmask);
       bk[u] = k[at];
       if (v) bv[u] = v[at];
     }
@@ -48,8 +51,9 @@ __device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w
     for (int u = 0; u < kMoveUnroll; ++u) {
       const int64_t idx = tid + (int64_t)u * nthr;
       if (idx < nw) {
-        k[r0 * w16 + idx] = bk[u];
-        if (v) v[r0 * w16 + idx] = bv[u];
+        const int64_t at = (r0 + (idx >> wlog)) * w16 + (idx & wmask);
+        k[at] = bk[u];
+        if (v) v[at] = bv[u];
       }
     }
     __syncthreads();
@@ -67,7 +71,7 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
   if (pl.shift > 0) {
     if (pl.kept > 0)
       move_rows_in_place((u32x4*)((char*)a.present_k + off), (u32x4*)((char*)a.present_v + off),
-                         w16, pl.shift, pl.kept, tid, nthr);
+                         w16, __builtin_ctzll(w16), pl.shift, pl.kept, tid, nthr);
     // new rows after the move (they may land on rows the move read)
     const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
     const int64_t nw = (a.S - i0) * w16;
