@@ -105,9 +105,40 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
   const int lq = lane % 16;   // query column of this lane
   const int lg = lane / 16;   // lane group (0..3)
 
-  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
+  // seqlens_k first: the plan and every K/V address wait on it
+  const int32_t seqlen = a.seqlens[b];
   const int nq_item = a.S * a.group;
   const int q0 = tile * BQ;
+
+  // This lane's query (column lq of wave's 16 rows), loaded before the
+  // plan: its address does not depend on seqlens_k.
+  const int my_qi = q0 + wave * 16 + lq;
+  const bool my_ok = my_qi < nq_item;
+  const int my_qc = my_ok ? my_qi : nq_item - 1;
+  const int my_i = my_qc / a.group;
+  const int my_h = kvh * a.group + my_qc % a.group;
+  const int i_first = q0 / a.group;
+  const int i_last = (min(q0 + BQ, nq_item) - 1) / a.group;
+
+  // Q^T operand: fp32 step s holds Q[q][4s + lg]; 16-bit step s holds
+  // Q[q][16s + 4lg .. +3].
+  const char* qrow = (const char*)a.q + ((((int64_t)b * a.S + my_i) * a.Hq + my_h) * D) * e;
+  float qf[DT == kF32 ? DSTEPS : 1];
+  uint32_t qh[DT == kF32 ? 1 : DSTEPS][2];
+  if constexpr (DT == kF32) {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) qf[s] = ((const float*)qrow)[4 * s + lg];
+  } else {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) {
+      const uint2 v = *(const uint2*)(qrow + (16 * s + 4 * lg) * 2);
+      qh[s][0] = v.x;
+      qh[s][1] = v.y;
+    }
+  }
+
+  const ItemPlan pl = plan_item(seqlen, a.S, a.C, a.gdiv, a.total);
+  const int64_t my_pos = pl.P + my_i;
 
   if (!pl.ok) {
     if (tid == 0 && tile == 0 && split == 0 && kvh == 0) flag_status(a.status, kStatusBadItem);
@@ -129,33 +160,6 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
       }
     }
     return;
-  }
-
-  // This lane's query (column lq of wave's 16 rows).
-  const int my_qi = q0 + wave * 16 + lq;
-  const bool my_ok = my_qi < nq_item;
-  const int my_qc = my_ok ? my_qi : nq_item - 1;
-  const int my_i = my_qc / a.group;
-  const int my_h = kvh * a.group + my_qc % a.group;
-  const int64_t my_pos = pl.P + my_i;
-  const int i_first = q0 / a.group;
-  const int i_last = (min(q0 + BQ, nq_item) - 1) / a.group;
-
-  // Q^T operand: fp32 step s holds Q[q][4s + lg]; 16-bit step s holds
-  // Q[q][16s + 4lg .. +3].
-  const char* qrow = (const char*)a.q + ((((int64_t)b * a.S + my_i) * a.Hq + my_h) * D) * e;
-  float qf[DT == kF32 ? DSTEPS : 1];
-  uint32_t qh[DT == kF32 ? 1 : DSTEPS][2];
-  if constexpr (DT == kF32) {
-#pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) qf[s] = ((const float*)qrow)[4 * s + lg];
-  } else {
-#pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) {
-      const uint2 v = *(const uint2*)(qrow + (16 * s + 4 * lg) * 2);
-      qh[s][0] = v.x;
-      qh[s][1] = v.y;
-    }
   }
 
   // Key band of the tile and this split's part of it.
@@ -193,27 +197,62 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
     u32x4 k[CPT], v[CPT];
     float bias[8];
   };
-  auto load_block = [&](int64_t j0, BlockRegs& rg) __attribute__((always_inline)) {
+  // Per-lane parts of the addresses: chunk u of a block is key kc + j0,
+  // 16-byte part pc; blocks made only of cache rows (nearly all) add j0 rows
+  // to these, the rest take the two-segment select with clamping.
+  constexpr int kRowB = D * e;
+  uint64_t kc_lane[CPT], vc_lane[CPT];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
-      const int key = c / CPR, part = c % CPR;
-      const int64_t j = min(j0 + key, ke - 1);
-      const bool in_cache = j < pl.P;
-      const uint64_t msk = 0ull - (uint64_t)in_cache;
-      const uint64_t off_c = (uint64_t)((j - base) * D * e + part * 16);
-      const uint64_t off_n = (uint64_t)((j - pl.P) * new_stride + part * 16);
-      const uint64_t ka = ((ck + off_c) & msk) | ((nk + off_n) & ~msk);
-      const uint64_t va = ((cv + off_c) & msk) | ((nv + off_n) & ~msk);
-      rg.k[u] = load16_global<false>(ka);
-      rg.v[u] = load16_global<false>(va);
+  for (int u = 0; u < CPT; ++u) {
+    const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
+    const uint64_t off = (uint64_t)(((int64_t)(c / CPR) - base) * kRowB + (c % CPR) * 16);
+    kc_lane[u] = ck + off;
+    vc_lane[u] = cv + off;
+  }
+  const uint64_t bias_lane =
+      BIAS ? (uint64_t)a.bias + (uint64_t)((bias_row + 4 * lg) * e) : 0;
+  const int64_t cache_end = pl.P < ke ? pl.P : ke;  // keys below this are cache rows
+  auto load_block = [&](int64_t j0, BlockRegs& rg) __attribute__((always_inline)) {
+    if (j0 + BN <= cache_end) {  // uniform
+      const uint64_t boff = (uint64_t)(j0 * kRowB);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        rg.k[u] = load16_global<false>(kc_lane[u] + boff);
+        rg.v[u] = load16_global<false>(vc_lane[u] + boff);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
+        const int key = c / CPR, part = c % CPR;
+        const int64_t j = min(j0 + key, ke - 1);
+        const bool in_cache = j < pl.P;
+        const uint64_t msk = 0ull - (uint64_t)in_cache;
+        const uint64_t off_c = (uint64_t)((j - base) * D * e + part * 16);
+        const uint64_t off_n = (uint64_t)((j - pl.P) * new_stride + part * 16);
+        const uint64_t ka = ((ck + off_c) & msk) | ((nk + off_n) & ~msk);
+        const uint64_t va = ((cv + off_c) & msk) | ((nv + off_n) & ~msk);
+        rg.k[u] = load16_global<false>(ka);
+        rg.v[u] = load16_global<false>(va);
+      }
     }
     if constexpr (BIAS) {
+      if (j0 + BN <= ke) {  // uniform
+        // keys j0 + 16 kt + 4 lg + [0, 4): one 4-element load per tile, at
+        // element (not vector) alignment -- global memory takes unaligned
+        // vector loads on this target
+        const uint64_t bb = bias_lane + (uint64_t)(j0 * e);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt) load4_elems_unaligned<DT>(bb + kt * 16 * e, &rg.bias[kt * 4]);
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          rg.bias[kt * 4 + r] = load_one<DT>(a.bias, bias_row + min(j0 + kt * 16 + 4 * lg + r, ke - 1));
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            rg.bias[kt * 4 + r] =
+                load_elem_global<DT>((uint64_t)a.bias +
+                                     (uint64_t)((bias_row + min(j0 + kt * 16 + 4 * lg + r, ke - 1)) * e));
+      }
     }
   };
   auto store_block = [&](const BlockRegs& rg) __attribute__((always_inline)) {
@@ -321,18 +360,28 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
     const float corr = (m_run == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.0f;
+    uint32_t p16[2][2] = {{0u, 0u}, {0u, 0u}};  // fp16: P as the PV operand, packed
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = (sc[kt][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[kt][r] - m_new);
-        if constexpr (DT == kF16) p = (float)(_Float16)p;  // the operand PV uses
+        if constexpr (DT == kF16) {
+          // the normaliser sums P as rounded for the product
+          const uint32_t h = f32_to_f16_bits(p);
+          p16[kt][r / 2] |= h << (16 * (r % 2));
+          p = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+        }
         sc[kt][r] = p;
         psum += p;
       }
     l_run = l_run * corr + psum;
+    // rescale only when some query's maximum moved: after the first blocks
+    // the maxima settle and this is skipped
+    if (__any(corr != 1.0f)) {
 #pragma unroll
-    for (int t = 0; t < DT16; ++t) o[t] *= corr;
+      for (int t = 0; t < DT16; ++t) o[t] *= corr;
+    }
 
     // O^T += V^T . P^T
 #pragma unroll
@@ -348,8 +397,8 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
       } else {
         uint32_t pw[2], pl2[2];
         if constexpr (DT == kF16) {
-          pw[0] = (uint32_t)f32_to_f16_bits(sc[kt][0]) | ((uint32_t)f32_to_f16_bits(sc[kt][1]) << 16);
-          pw[1] = (uint32_t)f32_to_f16_bits(sc[kt][2]) | ((uint32_t)f32_to_f16_bits(sc[kt][3]) << 16);
+          pw[0] = p16[kt][0];
+          pw[1] = p16[kt][1];
         } else {
           // bf16 keeps 8 significant bits, too few for P: P = hi + lo, both
           // bf16, and two products (relative error ~2^-17)

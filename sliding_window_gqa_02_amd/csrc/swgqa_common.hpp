@@ -206,6 +206,37 @@ __device__ __forceinline__ u32x4 load16_global(uint64_t addr) {
   else return *(gptr)addr;
 }
 
+// One element at a global-memory address held as an integer, as float.
+template <int DT>
+__device__ __forceinline__ float load_elem_global(uint64_t addr) {
+  if constexpr (DT == kF32) {
+    return *(const float __attribute__((address_space(1)))*)addr;
+  } else if constexpr (DT == kF16) {
+    return (float)*(const _Float16 __attribute__((address_space(1)))*)addr;
+  } else {
+    return __uint_as_float((uint32_t)*(const uint16_t __attribute__((address_space(1)))*)addr << 16);
+  }
+}
+
+// Four consecutive elements at a global address aligned only to the element
+// size, as floats (one vector load; AMD global memory accepts unaligned
+// vector accesses).
+template <int DT>
+__device__ __forceinline__ void load4_elems_unaligned(uint64_t addr, float* out) {
+  if constexpr (DT == kF32) {
+    typedef u32x4 v_t __attribute__((aligned(4)));
+    const v_t w = *(const v_t __attribute__((address_space(1)))*)addr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typedef u32x2 v_t __attribute__((aligned(2)));
+    const v_t w = *(const v_t __attribute__((address_space(1)))*)addr;
+    unpack_word<DT>(w[0], out);
+    unpack_word<DT>(w[1], out + 2);
+  }
+}
+
 // Marks the workspace status word (sticky).
 __device__ __forceinline__ void flag_status(uint32_t* status, uint32_t bits) {
   atomicOr(status, bits);
