@@ -32,8 +32,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published
-# kernels that run each decode step of the two decode workloads
-HEADLINE_KERNEL = "attn_decode_kernel<0, 64, 8, 8, 3>"
+# kernels that run each decode step of the two decode workloads (the
+# library's launch planner picks them from the shapes: 2-query tiles x 4 per
+# KV head and 4 waves for the pages' shape, one 4-query tile and 8 waves per
+# slice for the batched serving decode)
+HEADLINE_KERNEL = "attn_decode_kernel<0, 64, 2, 4, 3>"
 SERVING_KERNEL = "attn_decode_kernel<2, 128, 4, 8, 3>"
 
 

@@ -239,6 +239,8 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.gdiv = make_gap_div((uint32_t)(p->capacity - p->local_window_size + 1));
   a.ntiles = s.ntiles;
   a.nsplit = s.nsplit;
+  a.tdiv = make_gap_div((uint32_t)(s.ntiles * s.nsplit));
+  a.hdiv = make_gap_div((uint32_t)p->kv_num_heads);
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_size);
   a.softcap = p->softcap;
   a.bias_b = p->bias_dim0_is_batch ? 1 : 0;

@@ -95,10 +95,16 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
   __shared__ LT sK[Sh::KELEMS];
   __shared__ LT sV[Sh::VELEMS];
 
-  const int b = blockIdx.z;
-  const int kvh = blockIdx.y;
-  const int tile = blockIdx.x / a.nsplit;
-  const int split = blockIdx.x % a.nsplit;
+  // work item P of the launch: slice P / T, item (tile, split) P % T
+  const uint32_t T = gridDim.x;  // ntiles * nsplit
+  const uint32_t P = xcd_contiguous(blockIdx.x + T * (blockIdx.y + gridDim.y * blockIdx.z),
+                                    T * gridDim.y * gridDim.z);
+  const uint32_t slice = div_gap(P, a.tdiv);
+  const uint32_t t = P - slice * T;
+  const int b = (int)div_gap(slice, a.hdiv);
+  const int kvh = (int)slice - b * a.Hkv;
+  const int tile = (int)t / a.nsplit;
+  const int split = (int)t % a.nsplit;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;

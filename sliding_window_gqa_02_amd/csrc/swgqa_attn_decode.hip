@@ -120,12 +120,18 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   constexpr int SR = Sh::SR, PAIRS = Sh::PAIRS, PPL = Sh::PPL;
   static_assert(Sh::ok, "unsupported decode shape");
 
-  const int b = blockIdx.z;
-  const int kvh = blockIdx.y;
+  // work item P of the launch: slice P / T, item (tile, split) P % T
+  const uint32_t T = gridDim.x;  // ntiles * nsplit
+  const uint32_t P = xcd_contiguous(blockIdx.x + T * (blockIdx.y + gridDim.y * blockIdx.z),
+                                    T * gridDim.y * gridDim.z);
+  const uint32_t slice = div_gap(P, a.tdiv);
+  const uint32_t t = P - slice * T;
+  const int b = (int)div_gap(slice, a.hdiv);
+  const int kvh = (int)slice - b * a.Hkv;
   // seqlens_k first: the plan and every K/V address wait on it
   const int32_t seqlen = a.seqlens[b];
-  const int tile = a.nsplit == 1 ? (int)blockIdx.x : (int)blockIdx.x / a.nsplit;
-  const int split = a.nsplit == 1 ? 0 : (int)blockIdx.x % a.nsplit;
+  const int tile = a.nsplit == 1 ? (int)t : (int)t / a.nsplit;
+  const int split = a.nsplit == 1 ? 0 : (int)t % a.nsplit;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;

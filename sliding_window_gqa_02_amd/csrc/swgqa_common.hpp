@@ -77,6 +77,20 @@ __host__ __device__ __forceinline__ uint32_t div_gap(uint32_t n, const GapDiv& d
   return (t + ((n - t) >> d.sh1)) >> d.sh2;
 }
 
+// XCD-aware placement.  The workgroups of a launch are dealt to the chip's 8
+// XCDs, each with its own L2, round-robin by linear id.  This maps linear id
+// L (of N) to a work index P such that every XCD receives one contiguous
+// range of P: consecutive work items -- the query tiles and key splits of one
+// (item, KV head) slice, which read the same K/V rows -- then share an L2.
+// XCD x holds ids x, x + 8, ...: q + (x < r) of them for N = 8q + r, and
+// receives P in [x q + min(x, r), (x + 1) q + min(x + 1, r)).
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t L, uint32_t N) {
+  constexpr uint32_t kXcds = 8;
+  const uint32_t x = L % kXcds, k = L / kXcds;
+  const uint32_t q = N / kXcds, r = N % kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // L(T) for the lengths a step can see: 0 <= T <= 2^31 and 1 <= W <= C < 2^31,
 // so ceil((T - C) / G) = (T - C - 1) / G + 1 with a 32-bit numerator.
 __host__ __device__ __forceinline__ int64_t resident_len_step(int64_t T, int32_t C,

@@ -31,6 +31,8 @@ struct AttnArgs {
   void* present_v;
   int32_t B, S, Hq, Hkv, C, W, total, group;
   GapDiv gdiv;  // division by the gap C - W + 1
+  GapDiv tdiv;  // division by ntiles * nsplit (work items per slice)
+  GapDiv hdiv;  // division by Hkv
   int32_t ntiles, nsplit;
   float scale, softcap;
   int32_t bias_b, bias_h;
