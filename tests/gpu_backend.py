@@ -145,6 +145,11 @@ class GpuBackend:
         status = sw.device_status(ws, clear=True)
         return status, to_host(out, cfg.dtype)
 
+    def counters_zero(self) -> bool:
+        """The per-slice arrival counters (workspace bytes [256, 16384)) are
+        zero between calls."""
+        return self.ws is None or int(self.ws[64:4096].abs().sum().item()) == 0
+
     def present_host(self):
         return to_host(self.K, self.cfg.dtype), to_host(self.V, self.cfg.dtype)
 

@@ -97,5 +97,6 @@ class Lockstep:
             rest = as_f64(gk[b, :, first_poisoned:], cfg.dtype)
             assert np.isnan(rest).all(), what + " wrote beyond the resident range"
         assert self.gpu.intact(), what + " canary overwritten"
+        assert self.gpu.counters_zero(), what + " a slice counter was left non-zero"
         self.steps += 1
         return out_g, out_o, plan

@@ -197,6 +197,34 @@ def test_small_slack_400_decodes():
     say(f"  worst scaled error {run.worst:.3g}")
 
 
+# One workspace, sized for a long-window key-split step (partials), then
+# reused for decode steps of a few-slice shape whose query tiles share each
+# slice and compact through the per-slice counters: the counters sit in the
+# fixed workspace header, never under another call's partials.
+def test_workspace_reuse_split_then_counted_compaction():
+    big = Cfg(B=1, Hq=4, Hkv=1, D=128, C=1600, W=1500, seed=37, dtype=synth.BF16)
+    say("workspace reuse: key splits, then counted compaction")
+    import sliding_window_gqa_02_amd as sw
+    p_big = sw.make_params(1, 1, 4, 1, 128, 1600, 1500, 3001, synth.BF16)
+    small = Cfg(B=1, Hq=16, Hkv=2, D=64, C=20, W=12, seed=38)
+    ws_bytes = max(sw.workspace_size(p_big), 1 << 16)
+    run_big = Lockstep(big)
+    run_big.gpu.ws = torch.zeros(ws_bytes // 4, dtype=torch.int32, device="cuda:0")
+    run_big.gpu.ws_bytes = ws_bytes
+    sw.workspace_init(run_big.gpu.ws)
+    run_big.step([0], 1500)
+    run_big.step([1500], 1)   # decode over a 1500-key window: key splits + combine
+    run = Lockstep(small)
+    run.gpu.ws, run.gpu.ws_bytes = run_big.gpu.ws, ws_bytes
+    run.step([0], 15)
+    events = 0
+    for T in range(16, 60):
+        _, _, plan = run.step([T - 1], 1)
+        events += int(plan[0, 5] > 0)
+    assert events >= 4
+    say(f"  worst scaled error {run.worst:.3g}, {events} compactions")
+
+
 # ---------------------------------------------------------------------------
 def test_invalid_items_flagged_zeroed_untouched():
     import sliding_window_gqa_02_amd as sw
