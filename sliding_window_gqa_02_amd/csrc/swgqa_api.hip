@@ -257,11 +257,12 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
       : s.kind == Kind::kDecode ? launch_attn_decode(p->dtype, p->head_size, s.nq, a, st)
                                 : launch_attn_split(p->dtype, p->head_size, s.nq, a, st);
   if (ea != hipSuccess) return SWGQA_ERR_HIP;
-  if (s.nsplit > 1 && launch_combine(p->dtype, p->head_size, a, st) != hipSuccess)
-    return SWGQA_ERR_HIP;
-  // The write-back: done inside the attention kernel when one workgroup owns
-  // each slice in place; otherwise a kernel of its own, after every read.
-  if (a.fuse_writeback) return SWGQA_OK;
+  // What the attention kernel did not finish -- the merge of key splits, the
+  // write-back when it is not done in the attention kernel -- runs in one
+  // more launch, after every read.
+  const bool merge = s.nsplit > 1;
+  const bool writeback = !a.fuse_writeback;
+  if (!merge && !writeback) return SWGQA_OK;
 
   CopyArgs c;
   c.past_k = past_key;
@@ -281,7 +282,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   c.D = p->head_size;
   c.elem_bytes = (int32_t)e;
   c.skip_drifting = shared ? 1 : 0;  // drifting appends were done by attention
-  if (launch_writeback(c, st) != hipSuccess) return SWGQA_ERR_HIP;
+  if (launch_step_tail(p->dtype, a, c, merge, writeback, st) != hipSuccess) return SWGQA_ERR_HIP;
   return SWGQA_OK;
 }
 

@@ -20,7 +20,7 @@
 // slot keeps its own online-softmax state (max, sum, accumulator); row slots
 // and waves are merged once at the end.  With one split the workgroup writes
 // the output; otherwise it writes (max, sum, accumulator) partials that
-// swgqa_combine.hip merges.
+// the step-tail kernel (swgqa_step_tail.hip) merges.
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
 #include "swgqa_tail.hpp"

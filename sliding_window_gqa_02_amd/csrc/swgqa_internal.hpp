@@ -57,7 +57,6 @@ struct CopyArgs {
 // Split-K attention for short steps; returns hipSuccess or the launch error.
 hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
                              hipStream_t stream);
-hipError_t launch_combine(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 // MFMA kernel for multi-token steps (swgqa_attn_chunk.hip): 64 query rows
 // per workgroup, keys in blocks of 32.
 bool chunk_kernel_supports(int dtype, int D);
@@ -71,7 +70,9 @@ bool decode_kernel_supports(int dtype, int D, int nq);
 int decode_stage_rows(int dtype, int D, int nq);
 hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
                               hipStream_t stream);
-hipError_t launch_writeback(const CopyArgs& a, hipStream_t stream);
+// Split merge and/or cache write-back after the attention kernel, one launch.
+hipError_t launch_step_tail(int dtype, const AttnArgs& a, const CopyArgs& c, bool merge,
+                            bool writeback, hipStream_t stream);
 hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
                        int32_t W, int32_t total, int64_t* out, hipStream_t stream);
 hipError_t launch_zero_words(uint32_t* words, size_t n, hipStream_t stream);

@@ -1,0 +1,162 @@
+// swgqa_step_tail.hip -- the work that follows the attention kernel when it
+// does not finish the step itself, in one launch: the merge of key-split
+// partials into the output, and the cache write-back (append + block
+// compaction).  The two parts touch disjoint memory (partials and output;
+// cache rows and new rows) and run side by side in one grid: the first
+// workgroups merge, the rest rewrite the cache.
+//
+// Merge: for every query row, m = max_s m_s, l = sum_s l_s 2^(m_s - m),
+// out = sum_s acc_s 2^(m_s - m) / l (log2 units, the online-softmax merge),
+// rounded to nearest-even in the output type.  Items whose seqlens_k is out
+// of range get zero rows, as the attention kernels give them.
+//
+// Write-back: after a step, rows [0, La) of present hold the newest La rows
+// of the logical concatenation [resident rows | S new rows] ("Specify
+// GroupQueryAttention windowed KV cache layout contract", Description).  In
+// cache terms ("[CPU] Add windowed kv cache for GQA", key design decisions):
+// the old rows [shift, Lb) move to [0, kept) -- only when a gap-sized block is
+// reclaimed (shift > 0); on drifting steps nothing moves -- and the new rows
+// land after them.  Rows a step of S > C never keeps are dropped.  This runs
+// after attention on the same stream, so in the shared-buffer mode (present
+// == past) no row a query reads is overwritten early.  In place, the move
+// overlaps itself whenever kept > shift; it is done per (item, KV head,
+// K|V, column part) with the pass-wise register-staged move of
+// swgqa_tail.hpp.  The append waits for the whole move, since new rows may
+// land on rows the move still reads.
+#include "swgqa_common.hpp"
+#include "swgqa_internal.hpp"
+#include "swgqa_tail.hpp"
+
+namespace swgqa {
+
+namespace {
+
+constexpr int kTailThreads = 256;
+
+// Column parts per row: the workgroups of one (item, KV head, K|V) slice
+// each move a disjoint set of 16-byte words of every row, so they need no
+// ordering between them.
+__host__ __device__ inline int writeback_columns(int w16) { return w16 < 4 ? w16 : 4; }
+
+// Merge of query rows: D / 4 threads per row, four outputs each.
+template <int DT>
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t blk) {
+  const int tpr = D / 4;
+  const int rows_per_block = kTailThreads / tpr;
+  const uint32_t nrows = (uint32_t)a.B * a.S * a.Hq;
+  const uint32_t row = blk * rows_per_block + threadIdx.x / tpr;
+  if (row >= nrows) return;
+  const int d = (int)(threadIdx.x % tpr) * 4;
+  const int b = (int)(row / (uint32_t)(a.S * a.Hq));
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
+  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (pl.ok) {
+    const int64_t r0 = (int64_t)row * a.nsplit;
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ml[(r0 + s) * 2]);
+    float L = 0.0f;
+    float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = a.ml[(r0 + s) * 2];
+      const float c = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+      L += a.ml[(r0 + s) * 2 + 1] * c;
+      const float4 p = *(const float4*)(a.opart + (r0 + s) * D + d);
+      A[0] += p.x * c;
+      A[1] += p.y * c;
+      A[2] += p.z * c;
+      A[3] += p.w * c;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = A[i] / L;
+  }
+  const int64_t at = (int64_t)row * D + d;
+  if constexpr (DT == kF32) {
+    *(float4*)((float*)a.out + at) = make_float4(o[0], o[1], o[2], o[3]);
+  } else {
+    const uint32_t w0 = pack_word<DT>(o), w1 = pack_word<DT>(o + 2);
+    *(uint2*)((uint16_t*)a.out + at) = make_uint2(w0, w1);
+  }
+}
+
+// Write-back of one (item, KV head, K|V, column part).
+__device__ __forceinline__ void writeback_part(const CopyArgs& a, uint32_t idx) {
+  const int64_t rowb = (int64_t)a.D * a.elem_bytes;
+  const int64_t w16 = rowb / 16;  // 16-byte words per row (a power of two)
+  const int ncol = writeback_columns((int)w16);
+  const int kvh = (int)(idx % (uint32_t)a.Hkv);
+  const uint32_t rest = idx / (uint32_t)a.Hkv;
+  const int b = (int)(rest % (uint32_t)a.B);
+  const int z = (int)(rest / (uint32_t)a.B);
+  const int which = z / ncol;  // 0: key cache, 1: value cache
+  const int col = z % ncol;
+  const int64_t wn = w16 / ncol;  // words of each row this workgroup moves
+  const int wlog = __builtin_ctzll(wn);
+  const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
+  if (!pl.ok) return;
+
+  const void* past = which ? a.past_v : a.past_k;
+  void* present = which ? a.present_v : a.present_k;
+  const char* fresh = (const char*)(which ? a.v : a.k);
+  const bool shared = present == past;
+  if (shared && pl.shift == 0 && a.skip_drifting) return;  // appended by attention
+
+  const int64_t slice = ((int64_t)b * a.Hkv + kvh) * a.C * rowb;
+  const u32x4* src = (const u32x4*)((const char*)past + slice) + col * wn;
+  u32x4* dst = (u32x4*)((char*)present + slice) + col * wn;
+  const int tid = threadIdx.x;
+
+  // 1. Surviving old rows: [shift, shift + kept) -> [0, kept).
+  if (pl.kept > 0 && (!shared || pl.shift > 0)) {
+    if (shared) {
+      move_rows_in_place(dst, nullptr, w16, wlog, pl.shift, pl.kept, tid, kTailThreads);
+    } else {
+      const int64_t nw = pl.kept * wn;
+      for (int64_t i = tid; i < nw; i += kTailThreads) {
+        const int64_t r = i >> wlog, w = i & (wn - 1);
+        dst[r * w16 + w] = src[(pl.shift + r) * w16 + w];
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. New rows i in [max(0, -kept), S) -> row kept + i.
+  const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
+  const int64_t nw = (a.S - i0) * wn;
+  for (int64_t j = tid; j < nw; j += kTailThreads) {
+    const int64_t i = i0 + (j >> wlog);
+    const int64_t w = j & (wn - 1);
+    const u32x4* s = (const u32x4*)(fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb) + col * wn;
+    dst[(pl.kept + i) * w16 + w] = s[w];
+  }
+}
+
+// Workgroups [0, merge_blocks) merge, the rest write back.
+template <int DT>
+__global__ __launch_bounds__(kTailThreads) void step_tail_kernel(AttnArgs a, CopyArgs c,
+                                                                 uint32_t merge_blocks) {
+  if (blockIdx.x < merge_blocks) merge_rows<DT>(a, c.D, blockIdx.x);
+  else writeback_part(c, blockIdx.x - merge_blocks);
+}
+
+}  // namespace
+
+hipError_t launch_step_tail(int dtype, const AttnArgs& a, const CopyArgs& c, bool merge,
+                            bool writeback, hipStream_t st) {
+  const int D = c.D;
+  const uint32_t rows = (uint32_t)a.B * a.S * a.Hq;
+  const uint32_t rows_per_block = kTailThreads / (D / 4);
+  const uint32_t merge_blocks = merge ? (rows + rows_per_block - 1) / rows_per_block : 0;
+  const uint32_t wb_blocks =
+      writeback ? (uint32_t)c.Hkv * c.B * 2 * writeback_columns(D * c.elem_bytes / 16) : 0;
+  const uint32_t blocks = merge_blocks + wb_blocks;
+  if (blocks == 0) return hipSuccess;
+  switch (dtype) {
+    case kF32: step_tail_kernel<kF32><<<blocks, kTailThreads, 0, st>>>(a, c, merge_blocks); break;
+    case kF16: step_tail_kernel<kF16><<<blocks, kTailThreads, 0, st>>>(a, c, merge_blocks); break;
+    case kBF16: step_tail_kernel<kBF16><<<blocks, kTailThreads, 0, st>>>(a, c, merge_blocks); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace swgqa
