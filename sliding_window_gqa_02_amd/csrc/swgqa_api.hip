@@ -47,6 +47,10 @@ constexpr int kMinKeysPerSplit = 32;
 #endif
 constexpr int kChunkMinTokens = 16;       // steps of at least this many tokens use MFMA
 constexpr int kChunkMinRows = SWGQA_CHUNK_MIN_ROWS;
+#ifndef SWGQA_CHUNK_WIDE_ROWS
+#define SWGQA_CHUNK_WIDE_ROWS 128
+#endif
+constexpr int kChunkWideRows = SWGQA_CHUNK_WIDE_ROWS;
 constexpr int64_t kChunkMinWorkgroups = SWGQA_CHUNK_MIN_WORKGROUPS;
 constexpr int64_t kWholeSliceMinTiles = SWGQA_WHOLE_SLICE_MIN_TILES;
 constexpr int64_t kWholeSliceMaxKeys = SWGQA_WHOLE_SLICE_MAX_KEYS;
@@ -90,7 +94,12 @@ SplitPlan plan_split(const swgqa_params* p) {
   if (multi_token && chunk_kernel_supports(p->dtype, p->head_size)) {
     // multi-token step on the matrix cores
     s.kind = Kind::kChunk;
-    s.nq = chunk_rows_per_workgroup();
+    // 16-bit types: 8-wave workgroups (128 query rows) once a KV head has
+    // that many rows -- twice the matrix work per staged K/V block, two
+    // waves per SIMD (measured slower for fp32, whose operands take twice
+    // the registers)
+    s.waves = (p->dtype != SWGQA_F32 && per_kv >= kChunkWideRows) ? 8 : 4;
+    s.nq = chunk_rows_per_workgroup(s.waves);
     s.ntiles = (per_kv + s.nq - 1) / s.nq;
     const int64_t span = std::min<int64_t>(p->sequence_length, (s.nq + group - 1) / group + 1);
     int64_t nkeys = (int64_t)p->local_window_size + span - 1;

@@ -40,9 +40,7 @@ namespace swgqa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int BQ = 64;   // query rows per workgroup
+// A workgroup of NW waves (4 or 8) owns 16 NW query rows.
 constexpr int BN = 32;   // keys per block
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -50,8 +48,9 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 
-template <int DT, int D>
+template <int DT, int D, int NW>
 struct ChunkShape {
+  static constexpr int kThreads = NW * kWave;
   static constexpr int e = Elem<DT>::bytes;
   // LDS row strides (elements), chosen so the MFMA operand reads of 16 lanes
   // on 16 different rows fall in distinct banks
@@ -83,9 +82,11 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 // BIAS: attention_bias present (a separate instantiation, so that the loads
 // of a block are the same on every path and the compiler can wait for
 // exactly the block it stages).
-template <int DT, int D, bool BIAS>
-__global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
-  using Sh = ChunkShape<DT, D>;
+template <int DT, int D, bool BIAS, int NW>
+__global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
+  using Sh = ChunkShape<DT, D, NW>;
+  constexpr int kThreads = Sh::kThreads;
+  constexpr int BQ = 16 * NW;  // query rows per workgroup
   using LT = typename LdsT<DT>::T;
   constexpr int e = Sh::e, KS = Sh::KS, VS = Sh::VS, CPT = Sh::CPT, DSTEPS = Sh::DSTEPS;
   constexpr int DT16 = Sh::DT16;
@@ -519,15 +520,20 @@ __global__ __launch_bounds__(kThreads) void attn_chunk_kernel(AttnArgs a) {
   slice_tail<DT>(a, pl, b, kvh, D);
 }
 
+template <int DT, int D, int NW>
+hipError_t launch_w(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
+  if (a.bias)
+    attn_chunk_kernel<DT, D, true, NW><<<grid, NW * kWave, 0, st>>>(a);
+  else
+    attn_chunk_kernel<DT, D, false, NW><<<grid, NW * kWave, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
-  if constexpr (ChunkShape<DT, D>::ok) {
-    const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
-    if (a.bias)
-      attn_chunk_kernel<DT, D, true><<<grid, kThreads, 0, st>>>(a);
-    else
-      attn_chunk_kernel<DT, D, false><<<grid, kThreads, 0, st>>>(a);
-    return hipGetLastError();
+  if constexpr (ChunkShape<DT, D, 4>::ok) {
+    return a.waves == 8 ? launch_w<DT, D, 8>(a, st) : launch_w<DT, D, 4>(a, st);
   } else {
     return hipErrorInvalidValue;
   }
@@ -553,7 +559,7 @@ bool chunk_kernel_supports(int dtype, int D) {
   return D >= 16 && D % 16 == 0 && D <= 256 && D * e <= 512;
 }
 
-int chunk_rows_per_workgroup() { return BQ; }
+int chunk_rows_per_workgroup(int waves) { return 16 * waves; }
 int chunk_keys_per_block() { return BN; }
 
 hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t st) {

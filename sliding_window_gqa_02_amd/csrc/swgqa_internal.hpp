@@ -57,10 +57,10 @@ struct CopyArgs {
 // Split-K attention for short steps; returns hipSuccess or the launch error.
 hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
                              hipStream_t stream);
-// MFMA kernel for multi-token steps (swgqa_attn_chunk.hip): 64 query rows
-// per workgroup, keys in blocks of 32.
+// MFMA kernel for multi-token steps (swgqa_attn_chunk.hip): 16 query rows
+// per wave, 4 or 8 waves per workgroup, keys in blocks of 32.
 bool chunk_kernel_supports(int dtype, int D);
-int chunk_rows_per_workgroup();
+int chunk_rows_per_workgroup(int waves);  // 4 or 8 waves
 int chunk_keys_per_block();
 hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 // Staged decode kernel (swgqa_attn_decode.hip): supports row sizes up to
