@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   const int lg = lane / 16;   // lane group (0..3)
 
   // seqlens_k first: the plan and every K/V address wait on it
-  const int32_t seqlen = a.seqlens[b];
+  const int32_t seqlen = load_seqlen(a.seqlens, b);
   const int nq_item = a.S * a.group;
   const int q0 = tile * BQ;
 

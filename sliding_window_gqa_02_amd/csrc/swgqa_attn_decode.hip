@@ -129,7 +129,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   const int b = (int)div_gap(slice, a.hdiv);
   const int kvh = (int)slice - b * a.Hkv;
   // seqlens_k first: the plan and every K/V address wait on it
-  const int32_t seqlen = a.seqlens[b];
+  const int32_t seqlen = load_seqlen(a.seqlens, b);
   const int tile = a.nsplit == 1 ? (int)t : (int)t / a.nsplit;
   const int split = a.nsplit == 1 ? 0 : (int)t % a.nsplit;
   const int tid = threadIdx.x;

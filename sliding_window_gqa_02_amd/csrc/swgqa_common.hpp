@@ -251,6 +251,13 @@ __device__ __forceinline__ void load4_elems_unaligned(uint64_t addr, float* out)
   }
 }
 
+// seqlens_k[b] (uniform across the workgroup) through the scalar data cache:
+// the array is read-only for the whole launch, and one scalar fetch per CU
+// replaces a vector load from every wave.
+__device__ __forceinline__ int32_t load_seqlen(const int32_t* seqlens, int b) {
+  return ((const int32_t __attribute__((address_space(4)))*)seqlens)[b];
+}
+
 // Marks the workspace status word (sticky).
 __device__ __forceinline__ void flag_status(uint32_t* status, uint32_t bits) {
   atomicOr(status, bits);
