@@ -12,8 +12,10 @@ run eagerly with per-step HIP events (kernel time for the roofline).
 
 Also reported: prefill times, the batched-serving decode (B=32, 32 Q / 8 KV
 heads x 128, bf16, W=4096, C=4608, softcap 50, 128 steps) with its own
-roofline, and the CPU oracle timed on a bounded sample of the headline
-workload.  Prints one JSON line.
+roofline, the small-slack decode (C=136), chunked-prefill (S=32) and verify
+(S=8) steps of B=4 fp16 items with bias, a capacity sweep at the pages' shape,
+and the CPU oracle timed on a bounded sample of the headline workload (all
+host cores, and 8 threads as on the pages).  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -333,7 +335,7 @@ def copy_reference(torch, mib: int):
             "GBps": round(bytes_moved / (best / 1e3) / 1e9, 1)}
 
 
-def cpu_baseline(wl: Workload, P: int, max_steps: int, seconds: float):
+def cpu_baseline(wl: Workload, P: int, max_steps: int, seconds: float, threads: int = 0):
     """The oracle (fp64, OpenMP over (item, head)) on decode steps of the
     headline workload, from a cache holding the contract layout at length P."""
     import oracle
@@ -350,7 +352,7 @@ def cpu_baseline(wl: Workload, P: int, max_steps: int, seconds: float):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    threads = oracle.set_threads(cores)
+    threads = oracle.set_threads(threads if threads > 0 else cores)
     n = 0
     t_used = 0.0
     while n < max_steps and t_used < seconds:
@@ -419,6 +421,29 @@ def small_slack(torch, sw):
     out, _ = loop_stats(torch, loop, snap, 1)
     out["workload"] = ("decode after a 512-token prompt, B=1, 64 Q / 8 KV heads x 64, fp32, "
                        "W=128, C=136 (G=9), 400 steps")
+    return out
+
+
+def capacity_sweep(torch, sw, slacks=(0, 4, 16, 32, 128, 256, 384), steps=800):
+    """Decode step time against capacity at the pages' shape (W=128): the
+    cache at T=2048 (as a 2048-token prefill leaves it), then `steps` decode
+    steps, for C = W + slack."""
+    out = []
+    for slack in slacks:
+        C = 128 + slack
+        wl = Workload(f"sweep_c{C}", B=1, Hq=64, Hkv=8, D=64, C=C, W=128, dtype=0, scale=0.125,
+                      seed=1002)
+        P0 = np.array([2048])
+        K, V = seeded_cache(torch, sw, wl, P0)
+        snap = (K.clone(), V.clone())
+        loop = DecodeLoop(torch, sw, wl, P0, steps, K, V)
+        loop.run(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        st, _ = loop_stats(torch, loop, snap, 1)
+        out.append({"capacity": C, "gap": C - 128 + 1, "step_us": st["step_us"],
+                    "compacting_steps": st["compacting_steps"],
+                    "eager_step_us_p50": st["eager_step_us_p50"]})
+        del loop, K, V, snap
     return out
 
 
@@ -589,12 +614,20 @@ def main():
         result["small_slack"] = small_slack(torch, sw)
         log("chunked prefill and verify ...")
         result["chunked_prefill"], result["verify"] = chunked_and_verify(torch, sw)
+        log("capacity sweep ...")
+        result["capacity_sweep"] = {
+            "workload": "pages' shape (B=1, 64 Q / 8 KV heads x 64, fp32, W=128), cache at "
+                        "T=2048, 800 decode steps, C = W + slack",
+            "points": capacity_sweep(torch, sw)}
 
     result["copy_reference"] = copy_reference(torch, args.copy_mib)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(headline, args.prompt, 400_000, args.cpu_seconds)
+        # and at the pages' 8 intra-op threads, for comparison with their figure
+        result["cpu_baseline_8_threads"] = cpu_baseline(headline, args.prompt, 400_000,
+                                                        args.cpu_seconds / 2, threads=8)
 
     print(json.dumps(result), flush=True)
 
