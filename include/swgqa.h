@@ -21,7 +21,8 @@
  *    seqlens_k = total length - 1 per item, total_sequence_length, the
  *    shared-buffer and separate-buffer modes, attributes num_heads,
  *    kv_num_heads, scale (default 1/sqrt(head_size)), local_window_size,
- *    softcap.
+ *    softcap, smooth_softmax, and the optional input head_sink (one value
+ *    per query head).
  *  - "Fix CPU Attention causal mask for q_len=1 with past_key and kv_len > 1"
  *    (onnxruntime PR #34226), Description: query i sees key j iff
  *    j <= i + past_sequence_length.
@@ -32,6 +33,12 @@
  *    logical concatenation of the resident rows and the S new rows;
  *  - score = scale * q.k, then softcap*tanh(score/softcap) when softcap > 0,
  *    then + attention_bias[b|0][h|0][i][j]; softmax; weighted sum of V;
+ *  - softmax sink: with head_sink given, one more logit head_sink[h] (used
+ *    as given: not scaled, capped or biased) joins the softmax denominator
+ *    with a zero value row -- out = sum_j e^{s_j} v_j / (e^{sink} +
+ *    sum_j e^{s_j}); with smooth_softmax != 0 and no head_sink that logit
+ *    is 0 (the Investigation Report, sections 1.1 and 1.3, names head_sink
+ *    and smooth_softmax without defining them; this is the plainest reading);
  *  - query head h reads KV head h / (num_heads / kv_num_heads);
  *  - present rows [0, L(T)) receive the newest L(T) rows of that
  *    concatenation (byte copies); rows [L(T), C) are unspecified.
@@ -90,6 +97,7 @@ typedef struct {
   int32_t dtype;                 /* swgqa_dtype of every tensor below */
   int32_t bias_dim0_is_batch;    /* bias dim 0: B (1) or 1 (0) */
   int32_t bias_dim1_is_heads;    /* bias dim 1: Hq (1) or 1 (0) */
+  int32_t smooth_softmax;        /* 0 or 1: a sink logit of 0 when head_sink is NULL */
 } swgqa_params;
 
 /* Plan record of one item, all int64: T, P, Lb = L(P), La = L(T),
@@ -122,6 +130,7 @@ swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes,
  *   past_key/value (B, Hkv, C, D)        rows [0, L(P_b)) valid on entry
  *   seqlens_k      int32 (B)             total length T_b = seqlens_k[b]+1
  *   attention_bias NULL or (B|1, Hq|1, S, total_sequence_length)
+ *   head_sink      NULL or (Hq)          per-head sink logit
  *   output         (B, S, Hq*D)
  *   present_key/value (B, Hkv, C, D)     == past (shared buffer, in place)
  *                                        or disjoint from it
@@ -131,7 +140,8 @@ swgqa_status swgqa_forward(const swgqa_params* params, const void* query,
                            const void* key, const void* value,
                            const void* past_key, const void* past_value,
                            const int32_t* seqlens_k,
-                           const void* attention_bias, void* output,
+                           const void* attention_bias, const void* head_sink,
+                           void* output,
                            void* present_key, void* present_value,
                            void* workspace, size_t workspace_bytes,
                            void* stream);

@@ -51,6 +51,7 @@ class Params(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("bias_dim0_is_batch", ctypes.c_int32),
         ("bias_dim1_is_heads", ctypes.c_int32),
+        ("smooth_softmax", ctypes.c_int32),
     ]
 
 
@@ -70,9 +71,9 @@ def lib():
         L.swgqa_oracle_plan.restype = ctypes.c_int
         L.swgqa_oracle_plan.argtypes = [ctypes.POINTER(Params), vp, vp]
         L.swgqa_oracle_forward.restype = ctypes.c_int
-        L.swgqa_oracle_forward.argtypes = [ctypes.POINTER(Params)] + [vp] * 11
+        L.swgqa_oracle_forward.argtypes = [ctypes.POINTER(Params)] + [vp] * 12
         L.swgqa_oracle_forward_compact_first.restype = ctypes.c_int
-        L.swgqa_oracle_forward_compact_first.argtypes = [ctypes.POINTER(Params)] + [vp] * 8
+        L.swgqa_oracle_forward_compact_first.argtypes = [ctypes.POINTER(Params)] + [vp] * 9
         L.swgqa_oracle_decode.restype = ctypes.c_double
         L.swgqa_oracle_decode.argtypes = [i32, ctypes.c_uint32]
         L.swgqa_oracle_encode.restype = ctypes.c_uint32
@@ -84,9 +85,9 @@ def lib():
 
 
 def make_params(B, S, Hq, Hkv, D, C, W, total, dtype=F32, scale=0.0,
-                softcap=0.0, bias_batch=1, bias_heads=1) -> Params:
+                softcap=0.0, bias_batch=1, bias_heads=1, smooth_softmax=0) -> Params:
     return Params(B, S, Hq, Hkv, D, C, W, total, scale, softcap, dtype,
-                  bias_batch, bias_heads)
+                  bias_batch, bias_heads, smooth_softmax)
 
 
 def _ptr(a):
@@ -116,7 +117,7 @@ def plan(p: Params, seqlens_k: np.ndarray):
 
 
 def forward(p: Params, query, key, value, past_key, past_value, seqlens_k,
-            bias=None, present_key=None, present_value=None, output=None):
+            bias=None, present_key=None, present_value=None, output=None, head_sink=None):
     """Runs one step.  present_* default to past_* (in place: the arrays are
     modified).  Returns (status, output, plan)."""
     seqlens_k = np.ascontiguousarray(seqlens_k, dtype=np.int32)
@@ -131,18 +132,18 @@ def forward(p: Params, query, key, value, past_key, past_value, seqlens_k,
     planbuf = np.zeros((p.batch_size, 8), dtype=np.int64)
     st = lib().swgqa_oracle_forward(
         ctypes.byref(p), _ptr(query), _ptr(key), _ptr(value), _ptr(past_key),
-        _ptr(past_value), _ptr(seqlens_k), _ptr(bias), _ptr(output),
+        _ptr(past_value), _ptr(seqlens_k), _ptr(bias), _ptr(head_sink), _ptr(output),
         _ptr(present_key), _ptr(present_value), _ptr(planbuf))
     return st, output, planbuf
 
 
 def forward_compact_first(p: Params, query, key, value, cache_key, cache_value,
-                          seqlens_k, bias=None):
+                          seqlens_k, bias=None, head_sink=None):
     seqlens_k = np.ascontiguousarray(seqlens_k, dtype=np.int32)
     output = np.empty_like(query)
     st = lib().swgqa_oracle_forward_compact_first(
         ctypes.byref(p), _ptr(query), _ptr(key), _ptr(value), _ptr(cache_key),
-        _ptr(cache_value), _ptr(seqlens_k), _ptr(bias), _ptr(output))
+        _ptr(cache_value), _ptr(seqlens_k), _ptr(bias), _ptr(head_sink), _ptr(output))
     return st, output
 
 

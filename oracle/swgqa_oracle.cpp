@@ -34,7 +34,12 @@
 //  * query head h reads KV head h / (Hq/Hkv);
 //  * seqlens_k[b]+1 < S or > total_sequence_length is an error for item b;
 //  * outputs are rounded to nearest-even from fp64; cache rows are byte
-//    copies.
+//    copies;
+//  * softmax sink (Investigation Report sections 1.1 and 1.3 name the input
+//    head_sink, one value per query head, and the attribute smooth_softmax
+//    without defining them): one more logit -- head_sink[h] as given, or 0
+//    when only smooth_softmax is set -- joins the softmax denominator with a
+//    zero value row: out = sum_j e^{s_j} v_j / (e^{sink} + sum_j e^{s_j}).
 
 #include "swgqa_oracle.h"
 
@@ -180,6 +185,7 @@ int validate(const swgqa_oracle_params* p) {
   if (p->total_sequence_length < 1) return 1;
   if (p->dtype < 0 || p->dtype > 2) return 2;
   if (!(p->scale >= 0.0f) || !(p->softcap >= 0.0f)) return 1;
+  if (p->smooth_softmax != 0 && p->smooth_softmax != 1) return 1;
   return 0;
 }
 
@@ -224,8 +230,8 @@ void attend_one(const swgqa_oracle_params* p, const void* qrow, size_t qoff,
                 const std::vector<size_t>& koff,
                 const std::vector<const void*>& vrow,
                 const std::vector<size_t>& voff, const std::vector<int64_t>& js,
-                double scale, const void* bias, int64_t b, int64_t h, int64_t i,
-                void* out, size_t ooff) {
+                double scale, const void* bias, const void* sink, int64_t b, int64_t h,
+                int64_t i, void* out, size_t ooff) {
   const int64_t D = p->head_size;
   const size_t n = js.size();
   std::vector<double> s(n);
@@ -237,7 +243,11 @@ void attend_one(const swgqa_oracle_params* p, const void* qrow, size_t qoff,
     s[t] = finish_score(p, dot, scale, bias, b, h, i, js[t]);
     if (s[t] > m) m = s[t];
   }
-  double l = 0.0;
+  // the sink logit joins the denominator only (its value row is zero)
+  const bool has_sink = sink != nullptr || p->smooth_softmax != 0;
+  const double sink_logit = sink ? load(p->dtype, sink, (size_t)h) : 0.0;
+  if (has_sink && sink_logit > m) m = sink_logit;
+  double l = has_sink ? std::exp(sink_logit - m) : 0.0;
   for (size_t t = 0; t < n; ++t) {
     s[t] = std::exp(s[t] - m);
     l += s[t];
@@ -293,8 +303,8 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
                          const void* key, const void* value,
                          const void* past_key, const void* past_value,
                          const int32_t* seqlens_k, const void* attention_bias,
-                         void* output, void* present_key, void* present_value,
-                         int64_t* plan_out) {
+                         const void* head_sink, void* output, void* present_key,
+                         void* present_value, int64_t* plan_out) {
   const int v = validate(p);
   if (v) return v;
   const int64_t B = p->batch_size, S = p->sequence_length, Hq = p->num_heads,
@@ -388,7 +398,7 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
           js.push_back(j);
         }
         attend_one(p, query, (size_t)((b * S + i) * Hq + h) * D, kr, ko, vr, vo,
-                   js, scale, attention_bias, b, h, i, output,
+                   js, scale, attention_bias, head_sink, b, h, i, output,
                    (size_t)((b * S + i) * Hq + h) * D);
       }
     }
@@ -418,7 +428,7 @@ int swgqa_oracle_forward_compact_first(const swgqa_oracle_params* p,
                                        void* cache_value,
                                        const int32_t* seqlens_k,
                                        const void* attention_bias,
-                                       void* output) {
+                                       const void* head_sink, void* output) {
   const int v = validate(p);
   if (v) return v;
   const int64_t B = p->batch_size, S = p->sequence_length, Hq = p->num_heads,
@@ -473,7 +483,7 @@ int swgqa_oracle_forward_compact_first(const swgqa_oracle_params* p,
           js.push_back(j);
         }
         attend_one(p, query, (size_t)((b * S + i) * Hq + h) * D, kr, ko, vr, vo,
-                   js, scale, attention_bias, b, h, i, output,
+                   js, scale, attention_bias, head_sink, b, h, i, output,
                    (size_t)((b * S + i) * Hq + h) * D);
       }
     }

@@ -16,6 +16,9 @@
  *   past/present key/value (B, Hkv, C, D)    ("BNSH")
  *   seqlens_k int32 (B)            total length of item b is seqlens_k[b]+1
  *   attention_bias (B or 1, Hq or 1, S, total_sequence_length) or NULL
+ *   head_sink (Hq) or NULL: per-head sink logit joining every softmax
+ *     denominator with a zero value row (used as given); with
+ *     smooth_softmax set and no head_sink, the sink logit is 0
  *   output (B, S, Hq*D)
  *
  * Pins: tests/test_oracle_pins.py.  Parity unpinned: the order of softcap and
@@ -51,6 +54,7 @@ typedef struct {
   int32_t dtype;                 /* 0 fp32, 1 fp16, 2 bf16 */
   int32_t bias_dim0_is_batch;    /* bias dim 0 is B (1) or 1 (0) */
   int32_t bias_dim1_is_heads;    /* bias dim 1 is Hq (1) or 1 (0) */
+  int32_t smooth_softmax;        /* 0/1: sink logit 0 when head_sink is NULL */
 } swgqa_oracle_params;
 
 /* Eight int64 per item: T, P, Lb=L(P), La=L(T), kept=La-S,
@@ -82,8 +86,8 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p,
                          const void* query, const void* key, const void* value,
                          const void* past_key, const void* past_value,
                          const int32_t* seqlens_k, const void* attention_bias,
-                         void* output, void* present_key, void* present_value,
-                         int64_t* plan_out);
+                         const void* head_sink, void* output, void* present_key,
+                         void* present_value, int64_t* plan_out);
 
 /* Compact-first variant (in place, cache_key/cache_value are both past and
  * present): move the surviving resident rows to the front, append the new
@@ -97,7 +101,7 @@ int swgqa_oracle_forward_compact_first(const swgqa_oracle_params* p,
                                        void* cache_value,
                                        const int32_t* seqlens_k,
                                        const void* attention_bias,
-                                       void* output);
+                                       const void* head_sink, void* output);
 
 /* Element conversions the oracle uses, exported so that tests can pin them
  * against independent routines.  dtype as above; bits in the low 16/32 bits. */

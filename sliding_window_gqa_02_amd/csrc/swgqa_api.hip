@@ -67,6 +67,7 @@ swgqa_status validate(const swgqa_params* p) {
   if (p->local_window_size < 1 || p->local_window_size > p->capacity) return SWGQA_ERR_ARG;
   if (p->total_sequence_length < 1) return SWGQA_ERR_ARG;
   if (!(p->scale >= 0.0f) || !(p->softcap >= 0.0f)) return SWGQA_ERR_ARG;
+  if (p->smooth_softmax != 0 && p->smooth_softmax != 1) return SWGQA_ERR_ARG;
   if (p->dtype < SWGQA_F32 || p->dtype > SWGQA_BF16) return SWGQA_ERR_UNSUPPORTED;
   if (!head_size_supported(p->head_size)) return SWGQA_ERR_UNSUPPORTED;
   return SWGQA_OK;
@@ -192,7 +193,8 @@ swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes, void*
 swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void* key,
                            const void* value, const void* past_key,
                            const void* past_value, const int32_t* seqlens_k,
-                           const void* attention_bias, void* output,
+                           const void* attention_bias, const void* head_sink,
+                           void* output,
                            void* present_key, void* present_value, void* workspace,
                            size_t workspace_bytes, void* stream) {
   const swgqa_status v = validate(p);
@@ -228,6 +230,8 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.past_v = past_value;
   a.seqlens = seqlens_k;
   a.bias = attention_bias;
+  a.sink = head_sink;
+  a.smooth = p->smooth_softmax;
   a.out = output;
   a.status = (uint32_t*)workspace;
   a.slice_counters = (uint32_t*)((char*)workspace + kStatusBytes);

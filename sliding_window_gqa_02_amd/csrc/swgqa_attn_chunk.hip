@@ -475,7 +475,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   if (my_ok) {
     const int64_t row = ((int64_t)b * a.S + my_i) * a.Hq + my_h;
     if (a.nsplit == 1) {
-      const float inv = 1.0f / l_run;
+      float m_fin = m_run;
+      const float inv = fold_sink<DT>(a.sink, a.smooth, my_h, m_fin, l_run) / l_run;
 #pragma unroll
       for (int dt = 0; dt < DT16; ++dt) {
         const int d0 = 16 * dt + 4 * lg;

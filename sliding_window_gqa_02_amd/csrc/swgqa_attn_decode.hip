@@ -486,7 +486,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
     const int i = qi / a.group, h = kvh * a.group + qi % a.group;
     const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
     if (a.nsplit == 1) {
-      const float o = A / L;
+      const float c = fold_sink<DT>(a.sink, a.smooth, h, M, L);
+      const float o = A * c / L;
       if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = o;
       else if constexpr (DT == kF16) ((_Float16*)a.out)[row * D + d] = (_Float16)o;
       else ((uint16_t*)a.out)[row * D + d] = f32_to_bf16(o);

@@ -258,6 +258,22 @@ __device__ __forceinline__ int32_t load_seqlen(const int32_t* seqlens, int b) {
   return ((const int32_t __attribute__((address_space(4)))*)seqlens)[b];
 }
 
+// Softmax sink of query head h: folds one more logit (head_sink[h], or 0 for
+// smooth_softmax) into a finished online-softmax state (running maximum m
+// and sum l, log2 units; the accumulators scale by the returned factor).  The
+// sink's value row is zero, so only the denominator grows.
+template <int DT>
+__device__ __forceinline__ float fold_sink(const void* sink, int smooth, int h, float& m,
+                                           float& l) {
+  if (sink == nullptr && smooth == 0) return 1.0f;
+  const float s2 = (sink ? load_one<DT>(sink, h) : 0.0f) * 1.4426950408889634f;
+  const float m2 = fmaxf(m, s2);
+  const float c = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - m2);
+  l = l * c + __builtin_amdgcn_exp2f(s2 - m2);
+  m = m2;
+  return c;
+}
+
 // Marks the workspace status word (sticky).
 __device__ __forceinline__ void flag_status(uint32_t* status, uint32_t bits) {
   atomicOr(status, bits);

@@ -36,6 +36,10 @@ struct AttnArgs {
   int32_t ntiles, nsplit;
   float scale, softcap;
   int32_t bias_b, bias_h;
+  // softmax sink: head_sink (Hq elements) or, with smooth != 0 and no
+  // head_sink, a logit of 0; it joins the denominator with a zero value row
+  const void* sink;
+  int32_t smooth;
   int32_t fuse_writeback;  // shared buffer, one key split: write-back in the kernel
   int32_t waves;           // waves per workgroup of the staged kernel
 };

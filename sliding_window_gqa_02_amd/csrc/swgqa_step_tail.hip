@@ -66,8 +66,9 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t bl
       A[2] += p.z * c;
       A[3] += p.w * c;
     }
+    const float c = fold_sink<DT>(a.sink, a.smooth, (int)(row % (uint32_t)a.Hq), M, L);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = A[i] / L;
+    for (int i = 0; i < 4; ++i) o[i] = A[i] * c / L;
   }
   const int64_t at = (int64_t)row * D + d;
   if constexpr (DT == kF32) {

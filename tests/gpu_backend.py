@@ -122,7 +122,8 @@ class GpuBackend:
         B = len(seqlens)
         total = int(seqlens.max()) + 1 if total is None else total
         p = sw.make_params(B, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, total,
-                           cfg.dtype, cfg.scale, cfg.softcap, *bias_bcast)
+                           cfg.dtype, cfg.scale, cfg.softcap, *bias_bcast,
+                           smooth_softmax=int(cfg.smooth))
         if poison:
             self.poison_unspecified(seqlens.astype(np.int64) + 1 - S)
         dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
@@ -139,7 +140,9 @@ class GpuBackend:
         else:
             nxt = self.cur
             prk, prv = pk, pv
-        sw.forward(p, dq, dk, dv, pk, pv, dseq, dbias, out, prk, prv, ws)
+        sink = cfg.head_sink()
+        dsink = None if sink is None else to_dev(sink)
+        sw.forward(p, dq, dk, dv, pk, pv, dseq, dbias, out, prk, prv, ws, head_sink=dsink)
         torch.cuda.synchronize()
         self.cur = nxt
         status = sw.device_status(ws, clear=True)

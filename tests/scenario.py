@@ -31,6 +31,8 @@ class Cfg:
     seed: int = 1
     v_pos: bool = False
     zero_q: bool = False
+    smooth: bool = False       # smooth_softmax: a sink logit of 0
+    sink_std: float = 0.0      # > 0: head_sink ~ N(0, sink_std^2) per query head
 
     def synth(self) -> synth.Synth:
         return synth.Synth(self.seed, self.Hq, self.Hkv, self.D, self.dtype,
@@ -39,7 +41,16 @@ class Cfg:
     def params(self, S: int, total: int, B: int | None = None):
         return oracle.make_params(self.B if B is None else B, S, self.Hq,
                                   self.Hkv, self.D, self.C, self.W, total,
-                                  self.dtype, self.scale, self.softcap)
+                                  self.dtype, self.scale, self.softcap,
+                                  smooth_softmax=int(self.smooth))
+
+    def head_sink(self):
+        """head_sink in storage form (Hq elements), or None."""
+        if self.sink_std <= 0.0:
+            return None
+        rng = np.random.default_rng(self.seed + 7919)
+        return synth.to_storage(rng.normal(0.0, self.sink_std, self.Hq).astype(np.float32),
+                                self.dtype)
 
 
 def nan_array(shape, dtype):
@@ -112,7 +123,8 @@ class OracleBackend:
         total = int(seqlens.max()) + 1 if total is None else total
         p = self.cfg.params(S, total, B=len(seqlens))
         p.bias_dim0_is_batch, p.bias_dim1_is_heads = bias_bcast
-        st, out, plan = oracle.forward(p, q, k, v, self.K, self.V, seqlens, bias)
+        st, out, plan = oracle.forward(p, q, k, v, self.K, self.V, seqlens, bias,
+                                       head_sink=self.cfg.head_sink())
         return st, out, plan
 
     def snapshot(self):

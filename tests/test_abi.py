@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout():
-    assert ctypes.sizeof(sw.Params) == 13 * 4
+    assert ctypes.sizeof(sw.Params) == 14 * 4
     assert ctypes.sizeof(sw.PlanEntry) == 64
 
 
@@ -94,7 +94,7 @@ def test_host_validation_without_gpu():
     seq = np.zeros(1, np.int32).ctypes.data
 
     def call(p, past=ptr, present=ptr, ws_bytes=4096):
-        return lib.swgqa_forward(ctypes.byref(p), ptr, ptr, ptr, past, past, seq, None,
+        return lib.swgqa_forward(ctypes.byref(p), ptr, ptr, ptr, past, past, seq, None, None,
                                  ptr, present, present, ptr, ws_bytes, None)
 
     assert call(sw.make_params(1, 1, 3, 2, 8, 6, 4, 8)) == sw.ERR_ARG
@@ -106,6 +106,7 @@ def test_host_validation_without_gpu():
     p = sw.make_params(1, 1, 2, 2, 8, 6, 4, 8)
     assert call(p, past=ptr + 64, present=ptr + 128) == sw.ERR_ALIAS
     assert call(p, ws_bytes=8) == sw.ERR_ARG
+    assert call(sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, smooth_softmax=2)) == sw.ERR_ARG
     assert lib.swgqa_plan(ctypes.byref(sw.make_params(1, 1, 3, 2, 8, 6, 4, 8)), ptr, ptr, None) == sw.ERR_ARG
     for s in range(6):
         assert sw.status_string(s)

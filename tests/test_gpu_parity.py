@@ -324,3 +324,44 @@ def test_chunk_key_splits_long_window():
         run.step(P, S)
         P = P + S
     say(f"  worst scaled error {run.worst:.3g}")
+
+
+# ---------------------------------------------------------------------------
+# Softmax sink (head_sink per query head, or smooth_softmax's logit 0) on
+# every output path: whole-slice decode and MFMA chunks (fp32, bf16), the
+# generic split kernel (D = 256), and key splits merged by the step tail.
+SINK = [
+    Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=41, sink_std=1.0),
+    Cfg(B=2, Hq=16, Hkv=2, D=128, C=70, W=64, seed=42, dtype=synth.BF16, softcap=30.0,
+        smooth=True),
+    Cfg(B=1, Hq=4, Hkv=4, D=256, C=20, W=17, seed=43, dtype=synth.F16, sink_std=2.0),
+]
+
+
+@pytest.mark.parametrize("cfg", SINK, ids=lambda c: f"D{c.D}t{c.dtype}smooth{int(c.smooth)}")
+def test_softmax_sink_random_steps(cfg):
+    say(f"softmax sink {cfg}")
+    rng = np.random.default_rng(cfg.seed)
+    run = Lockstep(cfg)
+    T = 0
+    for _ in range(12):
+        S = int(rng.choice([1, 1, 1, 2, 8, int(rng.integers(1, 2 * cfg.C + 2))]))
+        run.step([T] * cfg.B, S)
+        T += S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+def test_softmax_sink_key_splits():
+    cfg = Cfg(B=1, Hq=4, Hkv=1, D=128, C=1600, W=1500, seed=44, dtype=synth.BF16,
+              sink_std=1.0)
+    say("softmax sink with key splits")
+    syn = cfg.synth()
+    vers = Versions(1)
+    P0 = np.array([1700])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S in [64, 1, 1, 40]:
+        run.step(P, S)
+        P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")

@@ -501,6 +501,55 @@ def test_p8_softcap_limits():
 
 
 # ---------------------------------------------------------------------------
+# P12. Softmax sink (Investigation Report 1.1 / 1.3 name head_sink, one value
+# per query head, and smooth_softmax; reading: one more logit joins the
+# denominator with a zero value row).  Zero query: all n visible scores are 0,
+# so with V[..., 0] = absolute position each output is
+# n (lo + p) / 2 / (n + e^sink); smooth_softmax alone is sink = 0.
+@pytest.mark.parametrize("smooth,sink_std", [(True, 0.0), (False, 1.5), (True, 0.7)])
+def test_p12_sink_zero_query_closed_form(smooth, sink_std):
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=8, C=6, W=4, seed=121, v_pos=True, zero_q=True,
+              smooth=smooth, sink_std=sink_std)
+    sink = cfg.head_sink()
+    sig = np.zeros(cfg.Hq) if sink is None else synth.from_storage(sink, cfg.dtype)
+    outs, _ = run_sequence(cfg, [8, 1, 3, 1, 13, 1])
+    for (b, p), row in outs.items():
+        lo = max(0, p - cfg.W + 1)
+        n = p - lo + 1
+        want = n * (lo + p) / 2.0 / (n + np.exp(sig))
+        got = row.reshape(cfg.Hq, cfg.D)[:, 0].astype(np.float64)
+        assert np.all(np.abs(got - want) <= 2**-22 * np.abs(want) + 1e-30), (p, got, want)
+
+
+def test_p12_sink_limits():
+    base = Cfg(B=2, Hq=4, Hkv=2, D=8, C=7, W=5, seed=122)
+    o_none, _ = run_sequence(base, [9, 1, 2, 4])
+    # a sink logit far below every score changes nothing, bit for bit
+    deep = Cfg(**{**base.__dict__, "sink_std": 1.0})
+    sink = -1e30 * np.ones(base.Hq, np.float32)
+    deep.head_sink = lambda: sink
+    o_deep, _ = run_sequence(deep, [9, 1, 2, 4])
+    for key in o_none:
+        assert np.array_equal(o_none[key], o_deep[key])
+    # a sink logit far above every score drives every output towards 0
+    high = Cfg(**{**base.__dict__, "sink_std": 1.0})
+    hsink = 60.0 * np.ones(base.Hq, np.float32)
+    high.head_sink = lambda: hsink
+    o_high, _ = run_sequence(high, [9, 1, 2, 4])
+    for key in o_none:
+        assert np.all(np.abs(o_high[key]) <= np.abs(o_none[key]).max() * 1e-20)
+    # smooth_softmax is exactly a zero sink logit on every head
+    o_smooth, _ = run_sequence(Cfg(**{**base.__dict__, "smooth": True}), [9, 1, 2, 4])
+    zero = Cfg(**{**base.__dict__, "sink_std": 1.0})
+    zsink = np.zeros(base.Hq, np.float32)
+    zero.head_sink = lambda: zsink
+    o_zero, _ = run_sequence(zero, [9, 1, 2, 4])
+    for key in o_none:
+        assert np.array_equal(o_smooth[key], o_zero[key])
+        assert not np.array_equal(o_smooth[key], o_none[key])
+
+
+# ---------------------------------------------------------------------------
 # P9. GQA grouping (Investigation Report 1.3: num_heads Q heads share
 # kv_num_heads K/V heads): with a zero query each Q head averages its KV
 # head's V rows; MHA (Hq == Hkv) is the identity grouping.
@@ -617,6 +666,8 @@ def test_argument_errors():
     part = big[4:]                                   # partial overlap
     st = oracle.lib().swgqa_oracle_forward(
         p, z.ctypes.data, z.ctypes.data, z.ctypes.data, big.ctypes.data,
-        big.ctypes.data, np.array([0], np.int32).ctypes.data, None,
+        big.ctypes.data, np.array([0], np.int32).ctypes.data, None, None,
         z.ctypes.data, part.ctypes.data, part.ctypes.data, None)
     assert st == 3
+    p = oracle.make_params(1, 1, 2, 2, 4, 6, 4, 8, smooth_softmax=3)
+    assert oracle.forward(p, z, z, z, z, z, np.array([0], np.int32))[0] == 1
