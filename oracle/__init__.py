@@ -26,7 +26,7 @@ def build(force: bool = True, sanitize: bool = False, out: str | None = None) ->
     """Compile the oracle with g++ (optionally under ASan/UBSan)."""
     target = out or _LIB
     if force or not os.path.exists(target):
-        cmd = ["g++", "-std=c++17", "-O2", "-fPIC", "-shared", "-fopenmp",
+        cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp",
                "-Wall", "-Wextra"]
         if sanitize:
             cmd += ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
@@ -52,6 +52,9 @@ class Params(ctypes.Structure):
         ("bias_dim0_is_batch", ctypes.c_int32),
         ("bias_dim1_is_heads", ctypes.c_int32),
         ("smooth_softmax", ctypes.c_int32),
+        ("do_rotary", ctypes.c_int32),
+        ("rotary_interleaved", ctypes.c_int32),
+        ("rotary_cache_rows", ctypes.c_int32),
     ]
 
 
@@ -71,7 +74,7 @@ def lib():
         L.swgqa_oracle_plan.restype = ctypes.c_int
         L.swgqa_oracle_plan.argtypes = [ctypes.POINTER(Params), vp, vp]
         L.swgqa_oracle_forward.restype = ctypes.c_int
-        L.swgqa_oracle_forward.argtypes = [ctypes.POINTER(Params)] + [vp] * 12
+        L.swgqa_oracle_forward.argtypes = [ctypes.POINTER(Params)] + [vp] * 15
         L.swgqa_oracle_forward_compact_first.restype = ctypes.c_int
         L.swgqa_oracle_forward_compact_first.argtypes = [ctypes.POINTER(Params)] + [vp] * 9
         L.swgqa_oracle_decode.restype = ctypes.c_double
@@ -85,9 +88,11 @@ def lib():
 
 
 def make_params(B, S, Hq, Hkv, D, C, W, total, dtype=F32, scale=0.0,
-                softcap=0.0, bias_batch=1, bias_heads=1, smooth_softmax=0) -> Params:
+                softcap=0.0, bias_batch=1, bias_heads=1, smooth_softmax=0,
+                do_rotary=0, rotary_interleaved=0, rotary_cache_rows=0) -> Params:
     return Params(B, S, Hq, Hkv, D, C, W, total, scale, softcap, dtype,
-                  bias_batch, bias_heads, smooth_softmax)
+                  bias_batch, bias_heads, smooth_softmax, do_rotary, rotary_interleaved,
+                  rotary_cache_rows)
 
 
 def _ptr(a):
@@ -117,7 +122,8 @@ def plan(p: Params, seqlens_k: np.ndarray):
 
 
 def forward(p: Params, query, key, value, past_key, past_value, seqlens_k,
-            bias=None, present_key=None, present_value=None, output=None, head_sink=None):
+            bias=None, present_key=None, present_value=None, output=None, head_sink=None,
+            cos_cache=None, sin_cache=None, position_ids=None):
     """Runs one step.  present_* default to past_* (in place: the arrays are
     modified).  Returns (status, output, plan)."""
     seqlens_k = np.ascontiguousarray(seqlens_k, dtype=np.int32)
@@ -130,9 +136,12 @@ def forward(p: Params, query, key, value, past_key, past_value, seqlens_k,
     if output is None:
         output = np.empty_like(query)
     planbuf = np.zeros((p.batch_size, 8), dtype=np.int64)
+    if position_ids is not None:
+        position_ids = np.ascontiguousarray(position_ids, dtype=np.int64)
     st = lib().swgqa_oracle_forward(
         ctypes.byref(p), _ptr(query), _ptr(key), _ptr(value), _ptr(past_key),
-        _ptr(past_value), _ptr(seqlens_k), _ptr(bias), _ptr(head_sink), _ptr(output),
+        _ptr(past_value), _ptr(seqlens_k), _ptr(bias), _ptr(head_sink), _ptr(cos_cache),
+        _ptr(sin_cache), _ptr(position_ids), _ptr(output),
         _ptr(present_key), _ptr(present_value), _ptr(planbuf))
     return st, output, planbuf
 

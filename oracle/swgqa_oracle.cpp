@@ -35,6 +35,16 @@
 //  * seqlens_k[b]+1 < S or > total_sequence_length is an error for item b;
 //  * outputs are rounded to nearest-even from fp64; cache rows are byte
 //    copies;
+//  * rotary embedding (Investigation Report sections 1.1 and 1.3 name the
+//    inputs cos_cache / sin_cache (max_S, D/2), position_ids (B, S) and the
+//    attributes do_rotary / rotary_interleaved, without formulas): query and
+//    new key rows are rotated before attention and before they are stored;
+//    the pair (a, b) -- elements (k, k + D/2), or (2k, 2k + 1) when
+//    interleaved -- at position pos becomes (a c - b s, b c + a s) with
+//    c = cos_cache[pos][k], s = sin_cache[pos][k], each product, sum and
+//    difference rounded to binary32, then the result to the element type;
+//    pos = position_ids[b][i], or P + i without them; a position outside the
+//    caches makes the item invalid (status 4, zero output, present untouched);
 //  * softmax sink (Investigation Report sections 1.1 and 1.3 name the input
 //    head_sink, one value per query head, and the attribute smooth_softmax
 //    without defining them): one more logit -- head_sink[h] as given, or 0
@@ -186,7 +196,51 @@ int validate(const swgqa_oracle_params* p) {
   if (p->dtype < 0 || p->dtype > 2) return 2;
   if (!(p->scale >= 0.0f) || !(p->softcap >= 0.0f)) return 1;
   if (p->smooth_softmax != 0 && p->smooth_softmax != 1) return 1;
+  if (p->do_rotary != 0 && p->do_rotary != 1) return 1;
+  if (p->do_rotary && (p->head_size % 2 != 0 || p->rotary_cache_rows < 1)) return 1;
   return 0;
+}
+
+// Rotary embedding of rows [0, nrows) of a (B, S, heads, D) tensor in place
+// (a private copy of query or key).  ok[b] is cleared for an item with a
+// position outside the cos/sin caches.
+void rotate_rows(const swgqa_oracle_params* p, void* x, int64_t heads, const Plan* plans,
+                 std::vector<char>& ok, const void* cos_cache, const void* sin_cache,
+                 const int64_t* position_ids) {
+  const int64_t B = p->batch_size, S = p->sequence_length, D = p->head_size;
+  const int64_t half = D / 2;
+  for (int64_t b = 0; b < B; ++b) {
+    if (!ok[b]) continue;
+    for (int64_t i = 0; i < S; ++i) {
+      const int64_t pos = position_ids ? position_ids[b * S + i] : plans[b].P + i;
+      if (pos < 0 || pos >= p->rotary_cache_rows) {
+        ok[b] = 0;
+        break;
+      }
+    }
+  }
+  for (int64_t b = 0; b < B; ++b) {
+    if (!ok[b]) continue;
+    for (int64_t i = 0; i < S; ++i) {
+      const int64_t pos = position_ids ? position_ids[b * S + i] : plans[b].P + i;
+      for (int64_t h = 0; h < heads; ++h) {
+        const size_t row = (size_t)((b * S + i) * heads + h) * D;
+        for (int64_t k = 0; k < half; ++k) {
+          const size_t ia = row + (p->rotary_interleaved ? 2 * k : k);
+          const size_t ib = row + (p->rotary_interleaved ? 2 * k + 1 : k + half);
+          const float a = (float)load(p->dtype, x, ia);
+          const float bv = (float)load(p->dtype, x, ib);
+          const float c = (float)load(p->dtype, cos_cache, (size_t)(pos * half + k));
+          const float sn = (float)load(p->dtype, sin_cache, (size_t)(pos * half + k));
+          const float ac = a * c, bs = bv * sn, bc = bv * c, as = a * sn;
+          const float ra = ac - bs;
+          const float rb = bc + as;
+          store(p->dtype, x, ia, (double)ra);
+          store(p->dtype, x, ib, (double)rb);
+        }
+      }
+    }
+  }
 }
 
 // Buffer-sharing modes, Investigation Report section 1.2: past and present
@@ -303,8 +357,10 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
                          const void* key, const void* value,
                          const void* past_key, const void* past_value,
                          const int32_t* seqlens_k, const void* attention_bias,
-                         const void* head_sink, void* output, void* present_key,
-                         void* present_value, int64_t* plan_out) {
+                         const void* head_sink, const void* cos_cache,
+                         const void* sin_cache, const int64_t* position_ids,
+                         void* output, void* present_key, void* present_value,
+                         int64_t* plan_out) {
   const int v = validate(p);
   if (v) return v;
   const int64_t B = p->batch_size, S = p->sequence_length, Hq = p->num_heads,
@@ -331,6 +387,25 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
     if (!ok[b]) status = 4;
   }
   if (plan_out) swgqa_oracle_plan(p, seqlens_k, plan_out);
+
+  // 1b. Rotary embedding of private copies of the query and the new keys.
+  std::vector<char> qrot, krot;
+  if (p->do_rotary) {
+    if (!cos_cache || !sin_cache) return 1;
+    const size_t e0 = elem_bytes(p->dtype);
+    qrot.assign((const char*)query, (const char*)query + (size_t)(B * S * Hq * D) * e0);
+    krot.assign((const char*)key, (const char*)key + (size_t)(B * S * Hkv * D) * e0);
+    rotate_rows(p, qrot.data(), Hq, plans.data(), ok, cos_cache, sin_cache, position_ids);
+    rotate_rows(p, krot.data(), Hkv, plans.data(), ok, cos_cache, sin_cache, position_ids);
+    for (int64_t b = 0; b < B; ++b)
+      if (!ok[b]) {
+        status = 4;
+        if (plan_out)
+          for (int f = 0; f < SWGQA_ORACLE_PLAN_FIELDS; ++f) plan_out[SWGQA_ORACLE_PLAN_FIELDS * b + f] = -1;
+      }
+    query = qrot.data();
+    key = krot.data();
+  }
 
   // 2. Logical concatenation per (b, kvh): the Lb resident rows followed by
   //    the S new rows; row r holds absolute position P - Lb + r.  A separate

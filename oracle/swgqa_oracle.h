@@ -19,6 +19,8 @@
  *   head_sink (Hq) or NULL: per-head sink logit joining every softmax
  *     denominator with a zero value row (used as given); with
  *     smooth_softmax set and no head_sink, the sink logit is 0
+ *   cos_cache, sin_cache (rotary_cache_rows, D/2), used when do_rotary
+ *   position_ids int64 (B, S) or NULL (then position = P + i)
  *   output (B, S, Hq*D)
  *
  * Pins: tests/test_oracle_pins.py.  Parity unpinned: the order of softcap and
@@ -55,6 +57,9 @@ typedef struct {
   int32_t bias_dim0_is_batch;    /* bias dim 0 is B (1) or 1 (0) */
   int32_t bias_dim1_is_heads;    /* bias dim 1 is Hq (1) or 1 (0) */
   int32_t smooth_softmax;        /* 0/1: sink logit 0 when head_sink is NULL */
+  int32_t do_rotary;             /* 0/1: rotary embedding of query and new keys */
+  int32_t rotary_interleaved;    /* 0: pairs (k, k + D/2); 1: pairs (2k, 2k + 1) */
+  int32_t rotary_cache_rows;     /* rows of cos_cache / sin_cache */
 } swgqa_oracle_params;
 
 /* Eight int64 per item: T, P, Lb=L(P), La=L(T), kept=La-S,
@@ -86,8 +91,10 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p,
                          const void* query, const void* key, const void* value,
                          const void* past_key, const void* past_value,
                          const int32_t* seqlens_k, const void* attention_bias,
-                         const void* head_sink, void* output, void* present_key,
-                         void* present_value, int64_t* plan_out);
+                         const void* head_sink, const void* cos_cache,
+                         const void* sin_cache, const int64_t* position_ids,
+                         void* output, void* present_key, void* present_value,
+                         int64_t* plan_out);
 
 /* Compact-first variant (in place, cache_key/cache_value are both past and
  * present): move the surviving resident rows to the front, append the new

@@ -666,8 +666,117 @@ def test_argument_errors():
     part = big[4:]                                   # partial overlap
     st = oracle.lib().swgqa_oracle_forward(
         p, z.ctypes.data, z.ctypes.data, z.ctypes.data, big.ctypes.data,
-        big.ctypes.data, np.array([0], np.int32).ctypes.data, None, None,
+        big.ctypes.data, np.array([0], np.int32).ctypes.data, None, None, None, None, None,
         z.ctypes.data, part.ctypes.data, part.ctypes.data, None)
     assert st == 3
     p = oracle.make_params(1, 1, 2, 2, 4, 6, 4, 8, smooth_softmax=3)
     assert oracle.forward(p, z, z, z, z, z, np.array([0], np.int32))[0] == 1
+
+
+# ---------------------------------------------------------------------------
+# P13. Rotary embedding (Investigation Report 1.1 / 1.3 name cos_cache,
+# sin_cache, position_ids, do_rotary and rotary_interleaved; reading: the pair
+# (k, k + D/2) -- or (2k, 2k + 1) interleaved -- of a query or new key row at
+# position pos is rotated by the angle whose cosine and sine are
+# cos_cache[pos][k], sin_cache[pos][k]).  Observable through the stored keys
+# (present rows are rotated keys) and the outputs.
+def _rope_tables(rows, D, base=10000.0):
+    k = np.arange(D // 2)
+    ang = np.arange(rows)[:, None] * base ** (-2.0 * k[None, :] / D)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _rope_step(cfg, S, q, k, v, past_k, past_v, seq, cos, sin, interleaved=0, pos_ids=None,
+               rows=None):
+    p = oracle.make_params(cfg.B, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, int(seq.max()) + 1,
+                           cfg.dtype, do_rotary=1, rotary_interleaved=interleaved,
+                           rotary_cache_rows=cos.shape[0] if rows is None else rows)
+    K, V = past_k.copy(), past_v.copy()
+    st, out, plan = oracle.forward(p, q, k, v, K, V, seq, cos_cache=cos, sin_cache=sin,
+                                   position_ids=pos_ids)
+    return st, out, K, V
+
+
+def _rope_inputs(cfg, S, P):
+    syn = cfg.synth()
+    q, k, v = syn.step_inputs(np.array(P), S)
+    K = np.zeros((cfg.B, cfg.Hkv, cfg.C, cfg.D), np.float32)
+    V = np.zeros_like(K)
+    return q, k, v, K, V
+
+
+def test_p13_rotary_identity_table():
+    cfg = Cfg(B=2, Hq=4, Hkv=2, D=8, C=12, W=6, seed=131)
+    q, k, v, K, V = _rope_inputs(cfg, 9, [0, 0])
+    seq = np.array([8, 8], np.int32)
+    ones, zeros = np.ones((16, 4), np.float32), np.zeros((16, 4), np.float32)
+    st, out, Kr, Vr = _rope_step(cfg, 9, q, k, v, K, V, seq, ones, zeros)
+    p = cfg.params(9, 9)
+    K0, V0 = K.copy(), V.copy()
+    st0, out0, _ = oracle.forward(p, q, k, v, K0, V0, seq)
+    assert st == 0 and st0 == 0
+    assert np.array_equal(out, out0) and np.array_equal(Kr, K0) and np.array_equal(Vr, V0)
+
+
+def test_p13_rotary_is_complex_rotation():
+    """Stored keys equal (a + ib) e^{i angle}, computed by numpy's complex
+    multiplication, to binary32 rounding; values are not rotated."""
+    cfg = Cfg(B=1, Hq=2, Hkv=2, D=16, C=40, W=40, seed=132)
+    S = 20
+    q, k, v, K, V = _rope_inputs(cfg, S, [0])
+    cos, sin = _rope_tables(64, cfg.D)
+    st, _, Kr, Vr = _rope_step(cfg, S, q, k, v, K, V, np.array([S - 1], np.int32), cos, sin)
+    assert st == 0
+    kk = k.reshape(S, cfg.Hkv, cfg.D).astype(np.float64)
+    z = (kk[..., :8] + 1j * kk[..., 8:]) * (cos[:S, None, :] + 1j * sin[:S, None, :]).astype(np.complex128)
+    want = np.concatenate([z.real, z.imag], axis=-1)             # (S, Hkv, D)
+    got = Kr[0, :, :S].transpose(1, 0, 2).astype(np.float64)
+    assert np.all(np.abs(got - want) <= 4 * 2**-24 * (np.abs(kk).max(-1, keepdims=True) + 1e-30))
+    assert np.array_equal(Vr[0, :, :S].transpose(1, 0, 2), v.reshape(S, cfg.Hkv, cfg.D))
+
+
+def test_p13_interleaved_is_a_permutation_of_halves():
+    """Interleaved pairs (2k, 2k+1) on a row equal half pairs (k, k + D/2) on
+    the row with its even elements first and odd elements second."""
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=8, C=10, W=10, seed=133)
+    S = 7
+    q, k, v, K, V = _rope_inputs(cfg, S, [0])
+    cos, sin = _rope_tables(16, cfg.D)
+    seq = np.array([S - 1], np.int32)
+    perm = np.concatenate([np.arange(0, 8, 2), np.arange(1, 8, 2)])
+    _, _, Ki, _ = _rope_step(cfg, S, q, k, v, K, V, seq, cos, sin, interleaved=1)
+    kp = np.ascontiguousarray(k.reshape(1, S, 1, 8)[..., perm].reshape(k.shape))
+    qp = np.ascontiguousarray(q.reshape(1, S, 2, 8)[..., perm].reshape(q.shape))
+    _, _, Kh, _ = _rope_step(cfg, S, qp, kp, v, K, V, seq, cos, sin, interleaved=0)
+    assert np.array_equal(Ki[0, 0, :S][:, perm], Kh[0, 0, :S])
+
+
+def test_p13_relative_positions_and_position_ids():
+    """All keys rotated in one prefill step: shifting every position by a
+    constant through position_ids leaves every score, hence every output,
+    unchanged (to rounding); explicit positions P + i equal the default."""
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=16, C=30, W=9, seed=134)
+    S = 24
+    q, k, v, K, V = _rope_inputs(cfg, S, [0])
+    cos, sin = _rope_tables(128, cfg.D)
+    seq = np.array([S - 1], np.int32)
+    st, base, Kb, _ = _rope_step(cfg, S, q, k, v, K, V, seq, cos, sin)
+    st2, same, Ks, _ = _rope_step(cfg, S, q, k, v, K, V, seq, cos, sin,
+                                  pos_ids=np.arange(S)[None, :])
+    assert st == 0 and st2 == 0 and np.array_equal(base, same) and np.array_equal(Kb, Ks)
+    st3, shifted, _, _ = _rope_step(cfg, S, q, k, v, K, V, seq, cos, sin,
+                                    pos_ids=np.arange(S)[None, :] + 37)
+    assert st3 == 0
+    assert np.allclose(shifted, base, rtol=2e-4, atol=2e-5)
+    assert not np.allclose(shifted, _rope_step(cfg, S, q, k, v, K, V, seq, np.ones_like(cos),
+                                               np.zeros_like(sin))[1], rtol=1e-3)
+
+
+def test_p13_position_outside_the_tables_is_an_item_error():
+    cfg = Cfg(B=2, Hq=2, Hkv=1, D=8, C=10, W=4, seed=135)
+    q, k, v, K, V = _rope_inputs(cfg, 3, [0, 0])
+    cos, sin = _rope_tables(8, cfg.D)
+    seq = np.array([2, 2], np.int32)
+    pos = np.array([[0, 1, 2], [6, 7, 8]])          # item 1 reaches row 8 of 8
+    st, out, Kr, _ = _rope_step(cfg, 3, q, k, v, K, V, seq, cos, sin, pos_ids=pos)
+    assert st == 4 and np.all(out[1] == 0) and np.all(Kr[1] == 0) and not np.all(Kr[0] == 0)
