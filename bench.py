@@ -135,7 +135,8 @@ class DecodeLoop:
             self.args.append((ctypes.byref(self.p), vp(self.q[s].data_ptr()),
                               vp(self.k[s].data_ptr()), vp(self.v[s].data_ptr()),
                               vp(K.data_ptr()), vp(V.data_ptr()), vp(self.seq[s].data_ptr()),
-                              bp, None, vp(self.out[s].data_ptr()), vp(K.data_ptr()),
+                              bp, None, None, None, None, vp(self.out[s].data_ptr()),
+                              vp(K.data_ptr()),
                               vp(V.data_ptr()), vp(self.ws.data_ptr()),
                               ctypes.c_size_t(nbytes)))
 

@@ -33,6 +33,16 @@
  *    logical concatenation of the resident rows and the S new rows;
  *  - score = scale * q.k, then softcap*tanh(score/softcap) when softcap > 0,
  *    then + attention_bias[b|0][h|0][i][j]; softmax; weighted sum of V;
+ *  - rotary embedding (do_rotary): before attention and before they are
+ *    stored, query and new key rows are rotated pairwise -- elements
+ *    (k, k + D/2), or (2k, 2k + 1) with rotary_interleaved -- the pair (a, b)
+ *    at position pos becoming (a c - b s, b c + a s) with c, s =
+ *    cos_cache[pos][k], sin_cache[pos][k]; each product, sum and difference
+ *    is rounded to binary32, then the result to the element type (the
+ *    Investigation Report, sections 1.1 and 1.3, names these inputs and
+ *    attributes only; this is the plainest reading).  pos = position_ids[b][i],
+ *    or P + i without them; an item with a position outside the caches is
+ *    skipped like an item with out-of-range seqlens_k;
  *  - softmax sink: with head_sink given, one more logit head_sink[h] (used
  *    as given: not scaled, capped or biased) joins the softmax denominator
  *    with a zero value row -- out = sum_j e^{s_j} v_j / (e^{sink} +
@@ -98,6 +108,9 @@ typedef struct {
   int32_t bias_dim0_is_batch;    /* bias dim 0: B (1) or 1 (0) */
   int32_t bias_dim1_is_heads;    /* bias dim 1: Hq (1) or 1 (0) */
   int32_t smooth_softmax;        /* 0 or 1: a sink logit of 0 when head_sink is NULL */
+  int32_t do_rotary;             /* 0 or 1 */
+  int32_t rotary_interleaved;    /* 0: pairs (k, k + D/2); 1: pairs (2k, 2k + 1) */
+  int32_t rotary_cache_rows;     /* rows of cos_cache / sin_cache (>= 1 with do_rotary) */
 } swgqa_params;
 
 /* Plan record of one item, all int64: T, P, Lb = L(P), La = L(T),
@@ -112,7 +125,8 @@ typedef struct {
 
 /* Bytes of device workspace swgqa_forward needs for these parameters: the
  * status word in bytes [0, 4), per-(item, KV head) arrival counters in bytes
- * [256, 16384) that every call leaves at zero, then key-split partials
+ * [256, 16384) that every call leaves at zero, then key-split partials and,
+ * with do_rotary, the rotated query and key rows and the per-item lengths
  * (scratch).  0 if the parameters are invalid.  Pure host function.  A
  * workspace of at least this size serves any parameter set whose own size is
  * not larger. */
@@ -131,6 +145,8 @@ swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes,
  *   seqlens_k      int32 (B)             total length T_b = seqlens_k[b]+1
  *   attention_bias NULL or (B|1, Hq|1, S, total_sequence_length)
  *   head_sink      NULL or (Hq)          per-head sink logit
+ *   cos_cache, sin_cache (rotary_cache_rows, D/2), required with do_rotary
+ *   position_ids   NULL or int64 (B, S)  rotary positions (default P + i)
  *   output         (B, S, Hq*D)
  *   present_key/value (B, Hkv, C, D)     == past (shared buffer, in place)
  *                                        or disjoint from it
@@ -141,7 +157,8 @@ swgqa_status swgqa_forward(const swgqa_params* params, const void* query,
                            const void* past_key, const void* past_value,
                            const int32_t* seqlens_k,
                            const void* attention_bias, const void* head_sink,
-                           void* output,
+                           const void* cos_cache, const void* sin_cache,
+                           const int64_t* position_ids, void* output,
                            void* present_key, void* present_value,
                            void* workspace, size_t workspace_bytes,
                            void* stream);

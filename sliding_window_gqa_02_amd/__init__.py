@@ -49,6 +49,9 @@ class Params(ctypes.Structure):
         ("bias_dim0_is_batch", ctypes.c_int32),
         ("bias_dim1_is_heads", ctypes.c_int32),
         ("smooth_softmax", ctypes.c_int32),
+        ("do_rotary", ctypes.c_int32),
+        ("rotary_interleaved", ctypes.c_int32),
+        ("rotary_cache_rows", ctypes.c_int32),
     ]
 
 
@@ -83,7 +86,7 @@ def load(path: str = LIB_PATH):
     L.swgqa_workspace_init.restype = ctypes.c_int
     L.swgqa_workspace_init.argtypes = [vp, sz, vp]
     L.swgqa_forward.restype = ctypes.c_int
-    L.swgqa_forward.argtypes = [P] + [vp] * 12 + [sz, vp]
+    L.swgqa_forward.argtypes = [P] + [vp] * 15 + [sz, vp]
     L.swgqa_plan.restype = ctypes.c_int
     L.swgqa_plan.argtypes = [P, vp, vp, vp]
     L.swgqa_resident_length.restype = i64
@@ -105,10 +108,12 @@ def status_string(status: int) -> str:
 def make_params(batch_size, sequence_length, num_heads, kv_num_heads, head_size,
                 capacity, local_window_size, total_sequence_length, dtype=F32,
                 scale=0.0, softcap=0.0, bias_dim0_is_batch=1,
-                bias_dim1_is_heads=1, smooth_softmax=0) -> Params:
+                bias_dim1_is_heads=1, smooth_softmax=0, do_rotary=0, rotary_interleaved=0,
+                rotary_cache_rows=0) -> Params:
     return Params(batch_size, sequence_length, num_heads, kv_num_heads, head_size,
                   capacity, local_window_size, total_sequence_length, scale, softcap,
-                  dtype, bias_dim0_is_batch, bias_dim1_is_heads, smooth_softmax)
+                  dtype, bias_dim0_is_batch, bias_dim1_is_heads, smooth_softmax, do_rotary,
+                  rotary_interleaved, rotary_cache_rows)
 
 
 def _ptr(t):
@@ -135,11 +140,13 @@ def workspace_init(workspace, stream=None) -> None:
 
 def forward(p: Params, query, key, value, past_key, past_value, seqlens_k,
             attention_bias, output, present_key, present_value, workspace,
-            stream=None, head_sink=None) -> None:
+            stream=None, head_sink=None, cos_cache=None, sin_cache=None,
+            position_ids=None) -> None:
     """Enqueues one step (see include/swgqa.h).  All tensors on the GPU."""
     st = load().swgqa_forward(
         ctypes.byref(p), _ptr(query), _ptr(key), _ptr(value), _ptr(past_key),
-        _ptr(past_value), _ptr(seqlens_k), _ptr(attention_bias), _ptr(head_sink), _ptr(output),
+        _ptr(past_value), _ptr(seqlens_k), _ptr(attention_bias), _ptr(head_sink),
+        _ptr(cos_cache), _ptr(sin_cache), _ptr(position_ids), _ptr(output),
         _ptr(present_key), _ptr(present_value), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     if st != OK:
@@ -148,13 +155,15 @@ def forward(p: Params, query, key, value, past_key, past_value, seqlens_k,
 
 def forward_status(p: Params, query, key, value, past_key, past_value, seqlens_k,
                    attention_bias, output, present_key, present_value, workspace,
-                   workspace_bytes=None, stream=None, head_sink=None) -> int:
+                   workspace_bytes=None, stream=None, head_sink=None, cos_cache=None,
+                   sin_cache=None, position_ids=None) -> int:
     """Like forward() but returns the status code instead of raising."""
     nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None \
         else workspace_bytes
     return load().swgqa_forward(
         ctypes.byref(p), _ptr(query), _ptr(key), _ptr(value), _ptr(past_key),
         _ptr(past_value), _ptr(seqlens_k), _ptr(attention_bias), _ptr(head_sink),
+        _ptr(cos_cache), _ptr(sin_cache), _ptr(position_ids),
         _ptr(output), _ptr(present_key), _ptr(present_value), _ptr(workspace), nbytes,
         _stream(stream))
 

@@ -68,6 +68,9 @@ swgqa_status validate(const swgqa_params* p) {
   if (p->total_sequence_length < 1) return SWGQA_ERR_ARG;
   if (!(p->scale >= 0.0f) || !(p->softcap >= 0.0f)) return SWGQA_ERR_ARG;
   if (p->smooth_softmax != 0 && p->smooth_softmax != 1) return SWGQA_ERR_ARG;
+  if (p->do_rotary != 0 && p->do_rotary != 1) return SWGQA_ERR_ARG;
+  if (p->rotary_interleaved != 0 && p->rotary_interleaved != 1) return SWGQA_ERR_ARG;
+  if (p->do_rotary && (p->rotary_cache_rows < 1 || p->head_size % 2 != 0)) return SWGQA_ERR_ARG;
   if (p->dtype < SWGQA_F32 || p->dtype > SWGQA_BF16) return SWGQA_ERR_UNSUPPORTED;
   if (!head_size_supported(p->head_size)) return SWGQA_ERR_UNSUPPORTED;
   return SWGQA_OK;
@@ -164,6 +167,24 @@ size_t partial_bytes(const swgqa_params* p, const SplitPlan& s) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Rotary scratch (after the partials): rotated query rows, rotated key rows,
+// per-item lengths.
+struct RotaryScratch {
+  size_t q_off, k_off, seq_off, end;
+};
+
+RotaryScratch rotary_scratch(const swgqa_params* p, size_t start) {
+  RotaryScratch r{start, start, start, start};
+  if (!p->do_rotary) return r;
+  const size_t e = elem_bytes(p->dtype);
+  const size_t rows = (size_t)p->batch_size * p->sequence_length;
+  r.q_off = start;
+  r.k_off = r.q_off + align256(rows * p->num_heads * p->head_size * e);
+  r.seq_off = r.k_off + align256(rows * p->kv_num_heads * p->head_size * e);
+  r.end = r.seq_off + align256((size_t)p->batch_size * 4);
+  return r;
+}
+
 
 bool ranges_partially_overlap(const void* a, const void* b, size_t n) {
   const char* x = (const char*)a;
@@ -179,7 +200,7 @@ extern "C" {
 size_t swgqa_workspace_size(const swgqa_params* p) {
   if (validate(p) != SWGQA_OK) return 0;
   const SplitPlan s = plan_split(p);
-  return kHeaderBytes + align256(partial_bytes(p, s));
+  return rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s))).end;
 }
 
 swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -194,7 +215,8 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
                            const void* value, const void* past_key,
                            const void* past_value, const int32_t* seqlens_k,
                            const void* attention_bias, const void* head_sink,
-                           void* output,
+                           const void* cos_cache, const void* sin_cache,
+                           const int64_t* position_ids, void* output,
                            void* present_key, void* present_value, void* workspace,
                            size_t workspace_bytes, void* stream) {
   const swgqa_status v = validate(p);
@@ -218,8 +240,34 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   if (align_or & 15u) return SWGQA_ERR_ARG;
 
   const SplitPlan s = plan_split(p);
-  if (workspace_bytes < kHeaderBytes + partial_bytes(p, s)) return SWGQA_ERR_ARG;
+  const RotaryScratch rs = rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s)));
+  if (workspace_bytes < rs.end) return SWGQA_ERR_ARG;
+  if (p->do_rotary && (!cos_cache || !sin_cache)) return SWGQA_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
+  if (p->do_rotary) {
+    // rotated rows and the per-item lengths every later kernel reads
+    RotaryArgs r;
+    r.q = query;
+    r.k = key;
+    r.q_out = (char*)workspace + rs.q_off;
+    r.k_out = (char*)workspace + rs.k_off;
+    r.cos_cache = cos_cache;
+    r.sin_cache = sin_cache;
+    r.position_ids = position_ids;
+    r.seqlens = seqlens_k;
+    r.seqlens_out = (int32_t*)((char*)workspace + rs.seq_off);
+    r.B = p->batch_size;
+    r.S = p->sequence_length;
+    r.Hq = p->num_heads;
+    r.Hkv = p->kv_num_heads;
+    r.D = p->head_size;
+    r.rows = p->rotary_cache_rows;
+    r.interleaved = p->rotary_interleaved;
+    if (launch_rotary(p->dtype, r, st) != hipSuccess) return SWGQA_ERR_HIP;
+    query = r.q_out;
+    key = r.k_out;
+    seqlens_k = r.seqlens_out;
+  }
   const bool shared = present_key == past_key && present_value == past_value;
 
   AttnArgs a;

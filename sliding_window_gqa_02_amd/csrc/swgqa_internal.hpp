@@ -58,6 +58,22 @@ struct CopyArgs {
   int32_t skip_drifting;  // shared buffer and the append already fused
 };
 
+// Rotary pass (swgqa_rotary.hip): rotates q (B,S,Hq,D) and k (B,S,Hkv,D)
+// into q_out / k_out and writes the per-item lengths the step reads.
+struct RotaryArgs {
+  const void* q;
+  const void* k;
+  void* q_out;
+  void* k_out;
+  const void* cos_cache;
+  const void* sin_cache;
+  const int64_t* position_ids;  // (B, S) or NULL (then P + i)
+  const int32_t* seqlens;
+  int32_t* seqlens_out;         // seqlens, or -2 for items with bad positions
+  int32_t B, S, Hq, Hkv, D, rows, interleaved;
+};
+hipError_t launch_rotary(int dtype, const RotaryArgs& r, hipStream_t stream);
+
 // Split-K attention for short steps; returns hipSuccess or the launch error.
 hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
                              hipStream_t stream);

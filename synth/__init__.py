@@ -115,6 +115,15 @@ def elem_bytes(dtype: int) -> int:
     return 4 if dtype == F32 else 2
 
 
+def rotary_tables(rows: int, head_size: int, dtype: int, base: float = 10000.0):
+    """cos / sin tables (rows, head_size / 2) in storage form: row pos, column
+    k holds cos / sin of pos * base^(-2k / head_size), computed in float64
+    and rounded once to the element type (the usual frequency ladder)."""
+    k = np.arange(head_size // 2)
+    ang = np.arange(rows)[:, None] * base ** (-2.0 * k[None, :] / head_size)
+    return to_storage(np.cos(ang), dtype), to_storage(np.sin(ang), dtype)
+
+
 class Synth:
     """Generator bound to one seed, head counts and element type.
 

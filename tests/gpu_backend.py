@@ -116,14 +116,14 @@ class GpuBackend:
             self.V[b, :, L:].fill_(nv)
 
     def step(self, S, seqlens, q, k, v, bias=None, total=None, bias_bcast=(1, 1),
-             poison=True):
+             poison=True, position_ids=None):
         cfg = self.cfg
         seqlens = np.asarray(seqlens, dtype=np.int32)
         B = len(seqlens)
         total = int(seqlens.max()) + 1 if total is None else total
         p = sw.make_params(B, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, total,
                            cfg.dtype, cfg.scale, cfg.softcap, *bias_bcast,
-                           smooth_softmax=int(cfg.smooth))
+                           smooth_softmax=int(cfg.smooth), **cfg.rotary_params())
         if poison:
             self.poison_unspecified(seqlens.astype(np.int64) + 1 - S)
         dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
@@ -142,7 +142,12 @@ class GpuBackend:
             prk, prv = pk, pv
         sink = cfg.head_sink()
         dsink = None if sink is None else to_dev(sink)
-        sw.forward(p, dq, dk, dv, pk, pv, dseq, dbias, out, prk, prv, ws, head_sink=dsink)
+        cos, sin = cfg.rotary_tables()
+        dcos = None if cos is None else to_dev(cos)
+        dsin = None if sin is None else to_dev(sin)
+        dpos = None if position_ids is None else to_dev(np.asarray(position_ids, np.int64))
+        sw.forward(p, dq, dk, dv, pk, pv, dseq, dbias, out, prk, prv, ws, head_sink=dsink,
+                   cos_cache=dcos, sin_cache=dsin, position_ids=dpos)
         torch.cuda.synchronize()
         self.cur = nxt
         status = sw.device_status(ws, clear=True)

@@ -68,14 +68,18 @@ class Lockstep:
         self.steps = 0
 
     def step(self, P, S, bias=None, total=None, bias_bcast=(1, 1), check_regen=True,
-             q=None, k=None, v=None):
+             q=None, k=None, v=None, position_ids=None):
         cfg = self.cfg
+        # with rotary the cache holds rotated keys, not the generator's rows
+        check_regen = check_regen and cfg.rotary < 0
         P = np.asarray(P, dtype=np.int64)
         if q is None:
             q, k, v = step_inputs(cfg, self.syn, P, S, self.vers)
         seq = (P + S - 1).astype(np.int32)
-        st_g, out_g = self.gpu.step(S, seq, q, k, v, bias=bias, total=total, bias_bcast=bias_bcast)
-        st_o, out_o, plan = self.ora.step(S, seq, q, k, v, bias=bias, total=total, bias_bcast=bias_bcast)
+        st_g, out_g = self.gpu.step(S, seq, q, k, v, bias=bias, total=total, bias_bcast=bias_bcast,
+                                    position_ids=position_ids)
+        st_o, out_o, plan = self.ora.step(S, seq, q, k, v, bias=bias, total=total,
+                                          bias_bcast=bias_bcast, position_ids=position_ids)
         what = f"step {self.steps} S={S} P={list(P[:4])}"
         assert st_o == 0, what
         assert st_g == 0, what

@@ -33,6 +33,8 @@ class Cfg:
     zero_q: bool = False
     smooth: bool = False       # smooth_softmax: a sink logit of 0
     sink_std: float = 0.0      # > 0: head_sink ~ N(0, sink_std^2) per query head
+    rotary: int = -1           # -1 off; 0 pairs (k, k + D/2); 1 interleaved pairs
+    rot_rows: int = 4096       # rows of the cos / sin tables
 
     def synth(self) -> synth.Synth:
         return synth.Synth(self.seed, self.Hq, self.Hkv, self.D, self.dtype,
@@ -42,7 +44,20 @@ class Cfg:
         return oracle.make_params(self.B if B is None else B, S, self.Hq,
                                   self.Hkv, self.D, self.C, self.W, total,
                                   self.dtype, self.scale, self.softcap,
-                                  smooth_softmax=int(self.smooth))
+                                  smooth_softmax=int(self.smooth),
+                                  **self.rotary_params())
+
+    def rotary_params(self):
+        if self.rotary < 0:
+            return {}
+        return dict(do_rotary=1, rotary_interleaved=self.rotary,
+                    rotary_cache_rows=self.rot_rows)
+
+    def rotary_tables(self):
+        """(cos, sin) in storage form, or (None, None) without rotary."""
+        if self.rotary < 0:
+            return None, None
+        return synth.rotary_tables(self.rot_rows, self.D, self.dtype)
 
     def head_sink(self):
         """head_sink in storage form (Hq elements), or None."""
@@ -118,13 +133,16 @@ class OracleBackend:
         self.K = nan_array(shape, cfg.dtype) if K is None else K.copy()
         self.V = nan_array(shape, cfg.dtype) if V is None else V.copy()
 
-    def step(self, S, seqlens, q, k, v, bias=None, total=None, bias_bcast=(1, 1)):
+    def step(self, S, seqlens, q, k, v, bias=None, total=None, bias_bcast=(1, 1),
+             position_ids=None):
         seqlens = np.asarray(seqlens, dtype=np.int32)
         total = int(seqlens.max()) + 1 if total is None else total
         p = self.cfg.params(S, total, B=len(seqlens))
         p.bias_dim0_is_batch, p.bias_dim1_is_heads = bias_bcast
+        cos, sin = self.cfg.rotary_tables()
         st, out, plan = oracle.forward(p, q, k, v, self.K, self.V, seqlens, bias,
-                                       head_sink=self.cfg.head_sink())
+                                       head_sink=self.cfg.head_sink(), cos_cache=cos,
+                                       sin_cache=sin, position_ids=position_ids)
         return st, out, plan
 
     def snapshot(self):

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout():
-    assert ctypes.sizeof(sw.Params) == 14 * 4
+    assert ctypes.sizeof(sw.Params) == 17 * 4
     assert ctypes.sizeof(sw.PlanEntry) == 64
 
 
@@ -95,6 +95,7 @@ def test_host_validation_without_gpu():
 
     def call(p, past=ptr, present=ptr, ws_bytes=4096):
         return lib.swgqa_forward(ctypes.byref(p), ptr, ptr, ptr, past, past, seq, None, None,
+                                 None, None, None,
                                  ptr, present, present, ptr, ws_bytes, None)
 
     assert call(sw.make_params(1, 1, 3, 2, 8, 6, 4, 8)) == sw.ERR_ARG
@@ -107,6 +108,17 @@ def test_host_validation_without_gpu():
     assert call(p, past=ptr + 64, present=ptr + 128) == sw.ERR_ALIAS
     assert call(p, ws_bytes=8) == sw.ERR_ARG
     assert call(sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, smooth_softmax=2)) == sw.ERR_ARG
+    # rotary: flags are 0/1, the caches need rows, D must be even, and the
+    # caches must be given (checked before any launch)
+    assert call(sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, do_rotary=2, rotary_cache_rows=8)) == sw.ERR_ARG
+    assert call(sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, do_rotary=1, rotary_cache_rows=0)) == sw.ERR_ARG
+    assert call(sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, do_rotary=1, rotary_cache_rows=8,
+                               rotary_interleaved=3)) == sw.ERR_ARG
+    pr = sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, do_rotary=1, rotary_cache_rows=8)
+    need = lib.swgqa_workspace_size(ctypes.byref(pr))
+    assert need > lib.swgqa_workspace_size(ctypes.byref(p))  # rotated rows + lengths
+    assert call(pr, ws_bytes=need - 1) == sw.ERR_ARG
+    assert call(pr, ws_bytes=need) == sw.ERR_ARG           # no cos/sin caches
     assert lib.swgqa_plan(ctypes.byref(sw.make_params(1, 1, 3, 2, 8, 6, 4, 8)), ptr, ptr, None) == sw.ERR_ARG
     for s in range(6):
         assert sw.status_string(s)

@@ -365,3 +365,87 @@ def test_softmax_sink_key_splits():
         run.step(P, S)
         P = P + S
     say(f"  worst scaled error {run.worst:.3g}")
+
+
+# ---------------------------------------------------------------------------
+# Rotary embedding of the query and new key rows (cos / sin tables, default
+# positions P + i or explicit position_ids) ahead of every kernel path: whole-
+# slice decode, the generic split kernel (D = 256), MFMA chunks, and key splits
+# merged by the step tail.  The cache stores rotated keys, compared byte for
+# byte with the oracle's.
+ROTARY = [
+    Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=51, rotary=0),
+    Cfg(B=2, Hq=16, Hkv=2, D=128, C=70, W=64, seed=52, dtype=synth.BF16, rotary=1,
+        softcap=30.0),
+    Cfg(B=1, Hq=4, Hkv=4, D=256, C=20, W=17, seed=53, dtype=synth.F16, rotary=0),
+    Cfg(B=3, Hq=8, Hkv=2, D=128, C=110, W=100, seed=54, dtype=synth.F16, rotary=1,
+        sink_std=1.0),
+    Cfg(B=2, Hq=4, Hkv=1, D=32, C=48, W=40, seed=55, dtype=synth.F32, rotary=1),
+]
+
+
+@pytest.mark.parametrize("explicit", [False, True], ids=["default_pos", "position_ids"])
+@pytest.mark.parametrize("cfg", ROTARY, ids=lambda c: f"D{c.D}t{c.dtype}il{c.rotary}")
+def test_rotary_random_steps(cfg, explicit):
+    say(f"rotary {cfg} position_ids={explicit}")
+    rng = np.random.default_rng(cfg.seed)
+    run = Lockstep(cfg)
+    T = np.zeros(cfg.B, np.int64)
+    off = rng.integers(0, 9, size=cfg.B)       # per-item offset (left padding)
+    for _ in range(12):
+        S = int(rng.choice([1, 1, 2, 8, 16, 33, int(rng.integers(1, 2 * cfg.C + 2))]))
+        pos = (T[:, None] + np.arange(S)[None, :] + off[:, None]) if explicit else None
+        run.step(T, S, position_ids=pos)
+        T = T + S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+def test_rotary_chunk_key_splits():
+    cfg = Cfg(B=1, Hq=4, Hkv=1, D=128, C=1600, W=1500, seed=56, dtype=synth.BF16, rotary=0)
+    say("rotary with key splits")
+    syn = cfg.synth()
+    vers = Versions(1)
+    P0 = np.array([1700])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S in [64, 1, 40]:
+        run.step(P, S)
+        P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+def test_rotary_position_outside_tables_flags_item():
+    """An item whose position reaches past the tables is skipped like an
+    out-of-range length: flagged, zero output, its cache rows untouched; the
+    other items are computed."""
+    import sliding_window_gqa_02_amd as sw
+    from tests.gpu_backend import GpuBackend
+    from tests.scenario import OracleBackend
+    cfg = Cfg(B=3, Hq=4, Hkv=2, D=16, C=12, W=8, seed=57, rotary=0, rot_rows=16)
+    syn = cfg.synth()
+    vers = Versions(3)
+    P = np.array([5, 5, 5])
+    K, V = seeded_cache(cfg, syn, P, vers)
+    g = GpuBackend(cfg, K, V)
+    q, k, v = step_inputs(cfg, syn, P, 3, vers)
+    seq = np.array([7, 7, 7], np.int32)
+    pos = np.array([[5, 6, 7], [14, 15, 16], [-1, 0, 1]])   # items 1 and 2 invalid
+    before = g.present_host()
+    st, out = g.step(3, seq, q, k, v, total=8, poison=False, position_ids=pos)
+    assert st == sw.ERR_DEVICE_INPUT
+    assert np.all(out[1] == 0) and np.all(out[2] == 0)
+    after = g.present_host()
+    for b in (1, 2):
+        assert np.array_equal(after[0][b].view(np.uint8), before[0][b].view(np.uint8))
+        assert np.array_equal(after[1][b].view(np.uint8), before[1][b].view(np.uint8))
+    o = OracleBackend(cfg, K, V)
+    st_o, out_o, _ = o.step(3, seq, q, k, v, total=8, position_ids=pos)
+    assert st_o == 4
+    assert np.allclose(out[0], out_o[0], rtol=1e-5, atol=1e-5)
+    L = oracle.resident_length(8, cfg.C, cfg.W)
+    assert np.array_equal(after[0][0, :, :L].view(np.uint8), o.K[0, :, :L].view(np.uint8))
+    # the same step with positions inside the tables succeeds
+    st, _ = g.step(3, seq, q, k, v, total=8, poison=False,
+                   position_ids=np.array([[5, 6, 7], [5, 6, 7], [5, 6, 7]]))
+    assert st == sw.OK
