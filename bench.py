@@ -101,7 +101,7 @@ class DecodeLoop:
     staged in HBM, one C-ABI call per step with precomputed arguments."""
 
     def __init__(self, torch, sw, wl: Workload, P0: np.ndarray, nsteps: int, K, V,
-                 S: int = 1, bias=None, total: int | None = None):
+                 S: int = 1, bias=None, total: int | None = None, rotary: int = -1):
         import synth
         self.torch, self.sw, self.wl = torch, sw, wl
         self.nsteps, self.S = nsteps, S
@@ -121,8 +121,14 @@ class DecodeLoop:
         self.bias = bias
         self.T = P0[None, :] + S * (np.arange(nsteps)[:, None] + 1)
         total = int(self.T.max()) if total is None else total
+        rot = {}
+        self.tables = (None, None)
+        if rotary >= 0:  # cos / sin tables covering every position of the loop
+            rows = int(self.T.max()) + 1
+            rot = dict(do_rotary=1, rotary_interleaved=rotary, rotary_cache_rows=rows)
+            self.tables = tuple(to_dev(torch, t) for t in synth.rotary_tables(rows, wl.D, wl.dtype))
         self.p = sw.make_params(B, S, wl.Hq, wl.Hkv, wl.D, wl.C, wl.W, total, wl.dtype,
-                                wl.scale, wl.softcap)
+                                wl.scale, wl.softcap, **rot)
         nbytes = sw.workspace_size(self.p)
         self.ws = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda:0")
         sw.workspace_init(self.ws)
@@ -130,12 +136,14 @@ class DecodeLoop:
         self.fn = lib.swgqa_forward
         vp = ctypes.c_void_p
         bp = None if bias is None else vp(bias.data_ptr())
+        cp, sp = (None, None) if self.tables[0] is None else \
+            (vp(self.tables[0].data_ptr()), vp(self.tables[1].data_ptr()))
         self.args = []
         for s in range(nsteps):
             self.args.append((ctypes.byref(self.p), vp(self.q[s].data_ptr()),
                               vp(self.k[s].data_ptr()), vp(self.v[s].data_ptr()),
                               vp(K.data_ptr()), vp(V.data_ptr()), vp(self.seq[s].data_ptr()),
-                              bp, None, None, None, None, vp(self.out[s].data_ptr()),
+                              bp, None, cp, sp, None, vp(self.out[s].data_ptr()),
                               vp(K.data_ptr()),
                               vp(V.data_ptr()), vp(self.ws.data_ptr()),
                               ctypes.c_size_t(nbytes)))
@@ -425,6 +433,24 @@ def small_slack(torch, sw):
     return out
 
 
+def rotary_decode(torch, sw, prompt: int, steps: int):
+    """The headline decode with rotary embedding of the query and new key
+    rows (half-split pairs, default positions): what the rotary pass adds to
+    a step."""
+    wl = Workload("pages_decode_rotary", B=1, Hq=64, Hkv=8, D=64, C=384, W=128, dtype=0,
+                  scale=0.125, seed=1002)
+    P0 = np.array([prompt])
+    K, V = seeded_cache(torch, sw, wl, P0)
+    snap = (K.clone(), V.clone())
+    loop = DecodeLoop(torch, sw, wl, P0, steps, K, V, rotary=0)
+    loop.run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    out, _ = loop_stats(torch, loop, snap, 1)
+    out["workload"] = (f"decode after a {prompt}-token prompt, B=1, 64 Q / 8 KV heads x 64, "
+                       f"fp32, W=128, C=384, rotary on query and new keys, {steps} steps")
+    return out
+
+
 def capacity_sweep(torch, sw, slacks=(0, 4, 16, 32, 128, 256, 384), steps=800):
     """Decode step time against capacity at the pages' shape (W=128): the
     cache at T=2048 (as a 2048-token prefill leaves it), then `steps` decode
@@ -611,6 +637,8 @@ def main():
         del Ks, Vs, ssnap, sloop
 
     if not args.no_extra:
+        log("rotary decode ...")
+        result["rotary_decode"] = rotary_decode(torch, sw, args.prompt, nsteps)
         log("small-slack decode ...")
         result["small_slack"] = small_slack(torch, sw)
         log("chunked prefill and verify ...")

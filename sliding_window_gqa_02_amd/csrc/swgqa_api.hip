@@ -244,7 +244,15 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   if (workspace_bytes < rs.end) return SWGQA_ERR_ARG;
   if (p->do_rotary && (!cos_cache || !sin_cache)) return SWGQA_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
-  if (p->do_rotary) {
+  // Rotary embedding runs inside the staged decode kernel where it can (row
+  // chunks of 16 bytes, 16-byte aligned tables, the new rows of a slice no
+  // more than one per thread), else as a pass of its own before attention.
+  const bool rot_fused =
+      p->do_rotary && s.kind == Kind::kDecode && p->sequence_length <= 16 &&
+      decode_rotary_supports(p->dtype, p->head_size, s.nq) &&
+      (size_t)p->sequence_length * (p->head_size * e / 16) <= 256 &&
+      (((uintptr_t)cos_cache | (uintptr_t)sin_cache) & 15u) == 0;
+  if (p->do_rotary && !rot_fused) {
     // rotated rows and the per-item lengths every later kernel reads
     RotaryArgs r;
     r.q = query;
@@ -312,27 +320,47 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
                        (int64_t)p->batch_size * p->kv_num_heads <= kMaxSliceCounters;
   a.fuse_writeback = (shared && s.nsplit == 1 && (s.ntiles == 1 || counted)) ? 1 : 0;
   a.waves = s.waves;
-
-  const hipError_t ea =
-      s.kind == Kind::kChunk    ? launch_attn_chunk(p->dtype, p->head_size, a, st)
-      : s.kind == Kind::kDecode ? launch_attn_decode(p->dtype, p->head_size, s.nq, a, st)
-                                : launch_attn_split(p->dtype, p->head_size, s.nq, a, st);
-  if (ea != hipSuccess) return SWGQA_ERR_HIP;
-  // What the attention kernel did not finish -- the merge of key splits, the
+  // What the attention kernel does not finish -- the merge of key splits, the
   // write-back when it is not done in the attention kernel -- runs in one
   // more launch, after every read.
   const bool merge = s.nsplit > 1;
   const bool writeback = !a.fuse_writeback;
+  a.rot_cos = a.rot_sin = nullptr;
+  a.rot_pos = nullptr;
+  a.rot_rows = a.rot_interleaved = 0;
+  a.k_rot = nullptr;
+  a.seqlens_out = nullptr;
+  if (rot_fused) {
+    a.rot_cos = cos_cache;
+    a.rot_sin = sin_cache;
+    a.rot_pos = position_ids;
+    a.rot_rows = p->rotary_cache_rows;
+    a.rot_interleaved = p->rotary_interleaved;
+    if (writeback) a.k_rot = (char*)workspace + rs.k_off;
+    if (merge || writeback) a.seqlens_out = (int32_t*)((char*)workspace + rs.seq_off);
+  }
+
+  const hipError_t ea =
+      s.kind == Kind::kChunk    ? launch_attn_chunk(p->dtype, p->head_size, a, st)
+      : s.kind == Kind::kDecode
+          ? (rot_fused ? launch_attn_decode_rot(p->dtype, p->head_size, s.nq, a, st)
+                       : launch_attn_decode(p->dtype, p->head_size, s.nq, a, st))
+                                : launch_attn_split(p->dtype, p->head_size, s.nq, a, st);
+  if (ea != hipSuccess) return SWGQA_ERR_HIP;
   if (!merge && !writeback) return SWGQA_OK;
+  // with fused rotary the tail reads the rotated keys and the lengths with
+  // the position verdict that the attention kernel wrote
+  AttnArgs at = a;
+  if (rot_fused) at.seqlens = a.seqlens_out;
 
   CopyArgs c;
   c.past_k = past_key;
   c.past_v = past_value;
-  c.k = key;
+  c.k = rot_fused ? a.k_rot : key;
   c.v = value;
   c.present_k = present_key;
   c.present_v = present_value;
-  c.seqlens = seqlens_k;
+  c.seqlens = rot_fused ? a.seqlens_out : seqlens_k;
   c.B = p->batch_size;
   c.S = p->sequence_length;
   c.Hkv = p->kv_num_heads;
@@ -343,7 +371,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   c.D = p->head_size;
   c.elem_bytes = (int32_t)e;
   c.skip_drifting = shared ? 1 : 0;  // drifting appends were done by attention
-  if (launch_step_tail(p->dtype, a, c, merge, writeback, st) != hipSuccess) return SWGQA_ERR_HIP;
+  if (launch_step_tail(p->dtype, at, c, merge, writeback, st) != hipSuccess) return SWGQA_ERR_HIP;
   return SWGQA_OK;
 }
 

@@ -42,6 +42,14 @@ struct AttnArgs {
   int32_t smooth;
   int32_t fuse_writeback;  // shared buffer, one key split: write-back in the kernel
   int32_t waves;           // waves per workgroup of the staged kernel
+  // rotary embedding fused into the staged decode kernel (rot_cos non-NULL):
+  // tables (rot_rows, D/2), 16-byte aligned; positions (B, S) or NULL (P + i)
+  const void* rot_cos;
+  const void* rot_sin;
+  const int64_t* rot_pos;
+  int32_t rot_rows, rot_interleaved;
+  void* k_rot;             // rotated new keys (B, S, Hkv*D) for the step tail, or NULL
+  int32_t* seqlens_out;    // per-item lengths for the step tail (-2: bad position), or NULL
 };
 
 struct CopyArgs {
@@ -90,6 +98,10 @@ bool decode_kernel_supports(int dtype, int D, int nq);
 int decode_stage_rows(int dtype, int D, int nq);
 hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
                               hipStream_t stream);
+// The same kernel with rotary embedding fused in (head sizes 32, 64, 128).
+bool decode_rotary_supports(int dtype, int D, int nq);
+hipError_t launch_attn_decode_rot(int dtype, int D, int nq, const AttnArgs& a,
+                                  hipStream_t stream);
 // Split merge and/or cache write-back after the attention kernel, one launch.
 hipError_t launch_step_tail(int dtype, const AttnArgs& a, const CopyArgs& c, bool merge,
                             bool writeback, hipStream_t stream);

@@ -62,7 +62,8 @@ __device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w
 
 // Cache write-back of slice (b, kvh) for both K and V, shared buffer.
 __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const ItemPlan& pl,
-                                                       int b, int kvh, int D, int e) {
+                                                       int b, int kvh, int D, int e,
+                                                       const u32x4* knew) {
   const int64_t rowb = (int64_t)D * e;
   const int64_t w16 = rowb / 16;
   const int64_t off = ((int64_t)b * a.Hkv + kvh) * a.C * rowb;
@@ -80,7 +81,8 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
     for (int64_t idx = tid; idx < nw; idx += nthr) {
       const int64_t i = i0 + idx / w16, w = idx % w16;
       const int64_t src = (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb;
-      dk[(pl.kept + i) * w16 + w] = ((const u32x4*)((const char*)a.k + src))[w];
+      dk[(pl.kept + i) * w16 + w] = knew ? knew[i * w16 + w]
+                                         : ((const u32x4*)((const char*)a.k + src))[w];
       dv[(pl.kept + i) * w16 + w] = ((const u32x4*)((const char*)a.v + src))[w];
     }
   }
@@ -94,9 +96,12 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
 // happens after every read of every tile, resets the counter for the next
 // call, and rewrites the slice.  Other launch shapes rewrite the cache in a
 // separate kernel.
+//
+// knew, if not NULL, holds the step's new key rows of the slice (S rows of
+// D * e / 16 words, in LDS) to store in place of a.k's.
 template <int DT>
 __device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl, int b, int kvh,
-                                           int D) {
+                                           int D, const u32x4* knew = nullptr) {
   if (!a.fuse_writeback || pl.shift == 0) return;  // drifting: appended by tile 0
   __syncthreads();  // all reads of this slice by this workgroup are done
   if (a.ntiles > 1) {
@@ -112,7 +117,7 @@ __device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl
     __syncthreads();
     if (!s_last) return;
   }
-  slice_writeback_shared(a, pl, b, kvh, D, Elem<DT>::bytes);
+  slice_writeback_shared(a, pl, b, kvh, D, Elem<DT>::bytes, knew);
 }
 
 }  // namespace swgqa

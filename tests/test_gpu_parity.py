@@ -369,10 +369,12 @@ def test_softmax_sink_key_splits():
 
 # ---------------------------------------------------------------------------
 # Rotary embedding of the query and new key rows (cos / sin tables, default
-# positions P + i or explicit position_ids) ahead of every kernel path: whole-
-# slice decode, the generic split kernel (D = 256), MFMA chunks, and key splits
-# merged by the step tail.  The cache stores rotated keys, compared byte for
-# byte with the oracle's.
+# positions P + i or explicit position_ids) on every kernel path: fused into
+# the staged decode kernel (D = 32, 64, 128; in-kernel append and compaction,
+# or the step tail in separate-buffer mode and after key splits), and as a
+# pass of its own before the generic split kernel (D = 256) and the MFMA
+# chunks.  The cache stores rotated keys, compared byte for byte with the
+# oracle's.
 ROTARY = [
     Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=51, rotary=0),
     Cfg(B=2, Hq=16, Hkv=2, D=128, C=70, W=64, seed=52, dtype=synth.BF16, rotary=1,
@@ -381,15 +383,18 @@ ROTARY = [
     Cfg(B=3, Hq=8, Hkv=2, D=128, C=110, W=100, seed=54, dtype=synth.F16, rotary=1,
         sink_std=1.0),
     Cfg(B=2, Hq=4, Hkv=1, D=32, C=48, W=40, seed=55, dtype=synth.F32, rotary=1),
+    Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=58, dtype=synth.BF16, rotary=0),
+    Cfg(B=2, Hq=4, Hkv=2, D=32, C=30, W=20, seed=59, dtype=synth.F16, rotary=1),
 ]
 
 
+@pytest.mark.parametrize("mode", ["shared", "separate"])
 @pytest.mark.parametrize("explicit", [False, True], ids=["default_pos", "position_ids"])
 @pytest.mark.parametrize("cfg", ROTARY, ids=lambda c: f"D{c.D}t{c.dtype}il{c.rotary}")
-def test_rotary_random_steps(cfg, explicit):
-    say(f"rotary {cfg} position_ids={explicit}")
+def test_rotary_random_steps(cfg, explicit, mode):
+    say(f"rotary {cfg} position_ids={explicit} mode={mode}")
     rng = np.random.default_rng(cfg.seed)
-    run = Lockstep(cfg)
+    run = Lockstep(cfg, mode=mode)
     T = np.zeros(cfg.B, np.int64)
     off = rng.integers(0, 9, size=cfg.B)       # per-item offset (left padding)
     for _ in range(12):
@@ -415,19 +420,21 @@ def test_rotary_chunk_key_splits():
     say(f"  worst scaled error {run.worst:.3g}")
 
 
-def test_rotary_position_outside_tables_flags_item():
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("D", [16, 64], ids=["prepass", "fused"])
+def test_rotary_position_outside_tables_flags_item(D, mode):
     """An item whose position reaches past the tables is skipped like an
     out-of-range length: flagged, zero output, its cache rows untouched; the
     other items are computed."""
     import sliding_window_gqa_02_amd as sw
     from tests.gpu_backend import GpuBackend
     from tests.scenario import OracleBackend
-    cfg = Cfg(B=3, Hq=4, Hkv=2, D=16, C=12, W=8, seed=57, rotary=0, rot_rows=16)
+    cfg = Cfg(B=3, Hq=4, Hkv=2, D=D, C=12, W=8, seed=57, rotary=0, rot_rows=16)
     syn = cfg.synth()
     vers = Versions(3)
     P = np.array([5, 5, 5])
     K, V = seeded_cache(cfg, syn, P, vers)
-    g = GpuBackend(cfg, K, V)
+    g = GpuBackend(cfg, K, V, mode=mode)
     q, k, v = step_inputs(cfg, syn, P, 3, vers)
     seq = np.array([7, 7, 7], np.int32)
     pos = np.array([[5, 6, 7], [14, 15, 16], [-1, 0, 1]])   # items 1 and 2 invalid
@@ -437,8 +444,13 @@ def test_rotary_position_outside_tables_flags_item():
     assert np.all(out[1] == 0) and np.all(out[2] == 0)
     after = g.present_host()
     for b in (1, 2):
-        assert np.array_equal(after[0][b].view(np.uint8), before[0][b].view(np.uint8))
-        assert np.array_equal(after[1][b].view(np.uint8), before[1][b].view(np.uint8))
+        if mode == "shared":
+            assert np.array_equal(after[0][b].view(np.uint8), before[0][b].view(np.uint8))
+            assert np.array_equal(after[1][b].view(np.uint8), before[1][b].view(np.uint8))
+        else:  # the separate present buffer keeps the NaN it was filled with
+            from tests.scenario import as_f64
+            assert np.isnan(as_f64(after[0][b], cfg.dtype)).all()
+            assert np.isnan(as_f64(after[1][b], cfg.dtype)).all()
     o = OracleBackend(cfg, K, V)
     st_o, out_o, _ = o.step(3, seq, q, k, v, total=8, position_ids=pos)
     assert st_o == 4
