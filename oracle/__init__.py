@@ -55,6 +55,9 @@ class Params(ctypes.Structure):
         ("do_rotary", ctypes.c_int32),
         ("rotary_interleaved", ctypes.c_int32),
         ("rotary_cache_rows", ctypes.c_int32),
+        ("kv_cache_type", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -89,10 +92,11 @@ def lib():
 
 def make_params(B, S, Hq, Hkv, D, C, W, total, dtype=F32, scale=0.0,
                 softcap=0.0, bias_batch=1, bias_heads=1, smooth_softmax=0,
-                do_rotary=0, rotary_interleaved=0, rotary_cache_rows=0) -> Params:
+                do_rotary=0, rotary_interleaved=0, rotary_cache_rows=0, kv_cache_type=0,
+                k_scale=0.0, v_scale=0.0) -> Params:
     return Params(B, S, Hq, Hkv, D, C, W, total, scale, softcap, dtype,
                   bias_batch, bias_heads, smooth_softmax, do_rotary, rotary_interleaved,
-                  rotary_cache_rows)
+                  rotary_cache_rows, kv_cache_type, k_scale, v_scale)
 
 
 def _ptr(a):

@@ -49,7 +49,16 @@
 //    head_sink, one value per query head, and the attribute smooth_softmax
 //    without defining them): one more logit -- head_sink[h] as given, or 0
 //    when only smooth_softmax is set -- joins the softmax denominator with a
-//    zero value row: out = sum_j e^{s_j} v_j / (e^{sink} + sum_j e^{s_j}).
+//    zero value row: out = sum_j e^{s_j} v_j / (e^{sink} + sum_j e^{s_j});
+//  * quantized cache (the Investigation Report, section 1.1, names inputs
+//    k_scale / v_scale, "KV cache quantization scale", and a cache type
+//    T_CACHE apart from T, without formulas): with kv_cache_type = 1 the
+//    caches hold int8 codes, one scale per tensor (k_scale for keys, v_scale
+//    for values); a cache element stands for code * scale; a new row element
+//    x (after rotary) is stored as the code nearest to x / scale -- the
+//    quotient rounded to binary32, then to an integer with ties to even,
+//    then saturated to [-128, 127] -- and every key and value row the step
+//    attends to, the new ones included, is read in that dequantized form.
 
 #include "swgqa_oracle.h"
 
@@ -104,6 +113,7 @@ bool make_plan(int32_t seqlen_k, int64_t S, int64_t C, int64_t W, int64_t total,
 // ---------------------------------------------------------------------------
 // Element conversions.  fp16 = IEEE binary16, bf16 = top half of binary32.
 size_t elem_bytes(int32_t dt) { return dt == 0 ? 4 : 2; }
+
 
 double decode_f16(uint32_t h) {
   const int sign = (h >> 15) & 1;
@@ -183,6 +193,28 @@ void store(int32_t dt, void* base, size_t idx, double x) {
   std::memcpy((char*)base + 2 * idx, &h, 2);
 }
 
+// Bytes of one cache element: the element type, or one int8 code.
+size_t cache_elem_bytes(const swgqa_oracle_params* p) {
+  return p->kv_cache_type == 1 ? 1 : elem_bytes(p->dtype);
+}
+
+// The int8 code of x for a quantization scale (binary32 quotient, ties to
+// even, saturation).
+int8_t quantize_int8(double x, float scale) {
+  const float t = std::nearbyint((float)x / scale);  // default mode: ties to even
+  if (!(t > -128.0f)) return (int8_t)-128;
+  if (t > 127.0f) return (int8_t)127;
+  return (int8_t)t;
+}
+
+// Element idx of a cache row buffer (element type, or dequantized int8 code).
+double load_cache(const swgqa_oracle_params* p, const void* base, size_t idx, float scale) {
+  if (p->kv_cache_type != 1) return load(p->dtype, base, idx);
+  int8_t c;
+  std::memcpy(&c, (const char*)base + idx, 1);
+  return (double)c * (double)scale;  // exact in fp64
+}
+
 // ---------------------------------------------------------------------------
 int validate(const swgqa_oracle_params* p) {
   if (!p) return 1;
@@ -198,6 +230,11 @@ int validate(const swgqa_oracle_params* p) {
   if (p->smooth_softmax != 0 && p->smooth_softmax != 1) return 1;
   if (p->do_rotary != 0 && p->do_rotary != 1) return 1;
   if (p->do_rotary && (p->head_size % 2 != 0 || p->rotary_cache_rows < 1)) return 1;
+  if (p->kv_cache_type != 0 && p->kv_cache_type != 1) return 2;
+  if (p->kv_cache_type == 1 &&
+      !(p->k_scale > 0.0f && p->v_scale > 0.0f && std::isfinite(p->k_scale) &&
+        std::isfinite(p->v_scale)))
+    return 1;
   return 0;
 }
 
@@ -293,7 +330,7 @@ void attend_one(const swgqa_oracle_params* p, const void* qrow, size_t qoff,
   for (size_t t = 0; t < n; ++t) {
     double dot = 0.0;
     for (int64_t d = 0; d < D; ++d)
-      dot += load(p->dtype, qrow, qoff + d) * load(p->dtype, krow[t], koff[t] + d);
+      dot += load(p->dtype, qrow, qoff + d) * load_cache(p, krow[t], koff[t] + d, p->k_scale);
     s[t] = finish_score(p, dot, scale, bias, b, h, i, js[t]);
     if (s[t] > m) m = s[t];
   }
@@ -308,7 +345,7 @@ void attend_one(const swgqa_oracle_params* p, const void* qrow, size_t qoff,
   }
   for (int64_t d = 0; d < D; ++d) {
     double acc = 0.0;
-    for (size_t t = 0; t < n; ++t) acc += s[t] * load(p->dtype, vrow[t], voff[t] + d);
+    for (size_t t = 0; t < n; ++t) acc += s[t] * load_cache(p, vrow[t], voff[t] + d, p->v_scale);
     store(p->dtype, out, ooff + d, acc / l);
   }
 }
@@ -371,7 +408,8 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
       !output || !present_key || !present_value)
     return 1;
   const size_t e = elem_bytes(p->dtype);
-  const size_t cache_bytes = (size_t)(B * Hkv * C * D) * e;
+  const size_t ce = cache_elem_bytes(p);
+  const size_t cache_bytes = (size_t)(B * Hkv * C * D) * ce;
   if (partial_overlap(past_key, present_key, cache_bytes) ||
       partial_overlap(past_value, present_value, cache_bytes))
     return 3;
@@ -410,8 +448,9 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
   // 2. Logical concatenation per (b, kvh): the Lb resident rows followed by
   //    the S new rows; row r holds absolute position P - Lb + r.  A separate
   //    allocation, so writing present afterwards is safe when present==past.
+  //    New rows enter in the cache's form (int8 codes when quantized).
   std::vector<std::vector<char>> XK((size_t)(B * Hkv)), XV((size_t)(B * Hkv));
-  const size_t row = (size_t)D * e;
+  const size_t row = (size_t)D * ce;
   for (int64_t b = 0; b < B; ++b) {
     if (!ok[b]) continue;
     const Plan& pl = plans[b];
@@ -426,9 +465,20 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
         std::memcpy(xv.data(), (const char*)past_value + slice, (size_t)pl.Lb * row);
       }
       for (int64_t i = 0; i < S; ++i) {
-        const size_t src = (size_t)((b * S + i) * Hkv + g) * row;
-        std::memcpy(xk.data() + (size_t)(pl.Lb + i) * row, (const char*)key + src, row);
-        std::memcpy(xv.data() + (size_t)(pl.Lb + i) * row, (const char*)value + src, row);
+        const size_t src = (size_t)((b * S + i) * Hkv + g) * D;  // element index
+        char* dk = xk.data() + (size_t)(pl.Lb + i) * row;
+        char* dv = xv.data() + (size_t)(pl.Lb + i) * row;
+        if (p->kv_cache_type == 1) {
+          for (int64_t d = 0; d < D; ++d) {
+            const int8_t qk = quantize_int8(load(p->dtype, key, src + d), p->k_scale);
+            const int8_t qv = quantize_int8(load(p->dtype, value, src + d), p->v_scale);
+            std::memcpy(dk + d, &qk, 1);
+            std::memcpy(dv + d, &qv, 1);
+          }
+        } else {
+          std::memcpy(dk, (const char*)key + src * e, row);
+          std::memcpy(dv, (const char*)value + src * e, row);
+        }
       }
     }
   }
@@ -506,6 +556,7 @@ int swgqa_oracle_forward_compact_first(const swgqa_oracle_params* p,
                                        const void* head_sink, void* output) {
   const int v = validate(p);
   if (v) return v;
+  if (p->kv_cache_type != 0) return 2;  // only the plain cache pins the staging rule
   const int64_t B = p->batch_size, S = p->sequence_length, Hq = p->num_heads,
                 Hkv = p->kv_num_heads, D = p->head_size, C = p->capacity,
                 W = p->local_window_size;

@@ -13,7 +13,8 @@
  *
  * Layouts (row-major, innermost last):
  *   query  (B, S, Hq*D)            key/value (B, S, Hkv*D)
- *   past/present key/value (B, Hkv, C, D)    ("BNSH")
+ *   past/present key/value (B, Hkv, C, D)    ("BNSH"), element type or, with
+ *     kv_cache_type 1, int8 codes (one byte per element)
  *   seqlens_k int32 (B)            total length of item b is seqlens_k[b]+1
  *   attention_bias (B or 1, Hq or 1, S, total_sequence_length) or NULL
  *   head_sink (Hq) or NULL: per-head sink logit joining every softmax
@@ -60,6 +61,9 @@ typedef struct {
   int32_t do_rotary;             /* 0/1: rotary embedding of query and new keys */
   int32_t rotary_interleaved;    /* 0: pairs (k, k + D/2); 1: pairs (2k, 2k + 1) */
   int32_t rotary_cache_rows;     /* rows of cos_cache / sin_cache */
+  int32_t kv_cache_type;         /* 0: caches in the element type; 1: int8 codes */
+  float k_scale;                 /* with kv_cache_type 1: key cache element = code * k_scale */
+  float v_scale;                 /* with kv_cache_type 1: value cache element = code * v_scale */
 } swgqa_oracle_params;
 
 /* Eight int64 per item: T, P, Lb=L(P), La=L(T), kept=La-S,

@@ -780,3 +780,182 @@ def test_p13_position_outside_the_tables_is_an_item_error():
     pos = np.array([[0, 1, 2], [6, 7, 8]])          # item 1 reaches row 8 of 8
     st, out, Kr, _ = _rope_step(cfg, 3, q, k, v, K, V, seq, cos, sin, pos_ids=pos)
     assert st == 4 and np.all(out[1] == 0) and np.all(Kr[1] == 0) and not np.all(Kr[0] == 0)
+
+
+# ---------------------------------------------------------------------------
+# P14. Quantized cache (Investigation Report 1.1 names the inputs k_scale /
+# v_scale, "KV cache quantization scale", and a cache type T_CACHE apart from
+# T; reading: int8 codes, one scale per tensor, a cache element stands for
+# code * scale, a new element x is stored as the binary32 quotient x / scale
+# rounded to an integer with ties to even and saturated to [-128, 127]; the
+# step attends to every row in that dequantized form, new rows included).
+def _q_forward(cfg, S, q, k, v, K8, V8, seq, ks, vs, total=None):
+    total = int(np.max(seq)) + 1 if total is None else total
+    p = oracle.make_params(len(seq), S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, total, cfg.dtype,
+                           cfg.scale, cfg.softcap, kv_cache_type=1, k_scale=ks, v_scale=vs)
+    K, V = K8.copy(), V8.copy()
+    st, out, plan = oracle.forward(p, q, k, v, K, V, np.asarray(seq, np.int32))
+    return st, out, K, V
+
+
+def _grid_rows(rng, shape, step, dtype):
+    """Elements code * step for random codes in [-128, 127]: exact in every
+    element type (at most 8 significant bits)."""
+    codes = rng.integers(-128, 128, size=shape)
+    return codes.astype(np.int8), synth.to_storage((codes * step).astype(np.float32), dtype)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.F16, synth.BF16])
+def test_p14_grid_values_equal_the_plain_cache(dtype):
+    """New rows whose elements are code * scale exactly: the stored codes are
+    those codes, and every output equals the plain cache's bit for bit (the
+    dequantized rows are the original values), across a staged prefill and
+    decode steps that read int8 resident rows."""
+    cfg = Cfg(B=2, Hq=4, Hkv=2, D=8, C=10, W=6, dtype=dtype, seed=141)
+    rng = np.random.default_rng(141)
+    ks, vs = 2.0 ** -3, 2.0 ** -5
+    syn = cfg.synth()
+    K8 = np.zeros((2, cfg.Hkv, cfg.C, cfg.D), np.int8)
+    V8 = np.zeros_like(K8)
+    Kp = scenario_nan((2, cfg.Hkv, cfg.C, cfg.D), dtype)
+    Vp = scenario_nan((2, cfg.Hkv, cfg.C, cfg.D), dtype)
+    T = np.zeros(2, np.int64)
+    for S in [7, 1, 1, 3, 1, 12, 1]:
+        q, _, _ = syn.step_inputs(T, S)
+        kc, k = _grid_rows(rng, (2, S, cfg.Hkv * cfg.D), ks, dtype)
+        vc, v = _grid_rows(rng, (2, S, cfg.Hkv * cfg.D), vs, dtype)
+        seq = (T + S - 1).astype(np.int32)
+        st, out, K8, V8 = _q_forward(cfg, S, q, k, v, K8, V8, seq, ks, vs)
+        p = oracle.make_params(2, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, int(seq.max()) + 1, dtype)
+        st0, out0, plan = oracle.forward(p, q, k, v, Kp, Vp, seq)
+        assert st == 0 and st0 == 0
+        assert np.array_equal(np.asarray(out).view(np.uint8), np.asarray(out0).view(np.uint8))
+        for b in range(2):
+            La = int(plan[b, 3])
+            assert np.array_equal(as_f64(Kp[b, :, :La], dtype), K8[b, :, :La] * ks)
+            assert np.array_equal(as_f64(Vp[b, :, :La], dtype), V8[b, :, :La] * vs)
+            # the newest rows are this step's codes
+            n = min(S, La)
+            got = K8[b, :, La - n:La]                               # (Hkv, n, D)
+            want = kc[b, S - n:].reshape(n, cfg.Hkv, cfg.D).transpose(1, 0, 2)
+            assert np.array_equal(got, want)
+        T = T + S
+
+
+def scenario_nan(shape, dtype):
+    from tests.scenario import nan_array
+    return nan_array(shape, dtype)
+
+
+def test_p14_rounding_ties_to_even_and_saturation():
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=16, C=4, W=4, seed=142)
+    ks, vs = 0.25, 0.5
+    mult = np.array([2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, -1.5,
+                     1000.0, -1000.0, 127.5, -128.5, 126.5, -127.5, 0.0, 7.0])
+    want = np.array([2, 4, -2, -4, 0, 0, 2, -2, 127, -128, 127, -128, 126, -128, 0, 7], np.int8)
+    k = (mult * ks).astype(np.float32).reshape(1, 1, 16)
+    v = (mult * vs).astype(np.float32).reshape(1, 1, 16)
+    q = np.zeros((1, 1, 2 * 16), np.float32)
+    K8 = np.zeros((1, 1, 4, 16), np.int8)
+    st, _, K, V = _q_forward(cfg, 1, q, k, v, K8, K8.copy(), [0], ks, vs)
+    assert st == 0
+    assert np.array_equal(K[0, 0, 0], want) and np.array_equal(V[0, 0, 0], want)
+
+
+def test_p14_scales_multiply_the_codes():
+    """Doubling k_scale while halving the query, or doubling v_scale, moves
+    every score / output by exactly that power of two: the key scale
+    multiplies the key codes in the scores, the value scale the values."""
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=8, C=12, W=9, seed=143)
+    rng = np.random.default_rng(143)
+    K8 = rng.integers(-128, 128, size=(1, 2, 12, 8)).astype(np.int8)
+    V8 = rng.integers(-128, 128, size=(1, 2, 12, 8)).astype(np.int8)
+    q = rng.normal(size=(1, 1, 32)).astype(np.float32)
+    zero_kv = np.zeros((1, 1, 16), np.float32)       # the new row: code 0 at any scale
+    seq = [10]                                       # P = 10 resident rows
+    st, base, _, _ = _q_forward(cfg, 1, q, zero_kv, zero_kv, K8, V8, seq, 0.03, 0.07)
+    st2, same, _, _ = _q_forward(cfg, 1, q * 0.5, zero_kv, zero_kv, K8, V8, seq, 0.06, 0.07)
+    st3, dbl, _, _ = _q_forward(cfg, 1, q, zero_kv, zero_kv, K8, V8, seq, 0.03, 0.14)
+    assert st == st2 == st3 == 0
+    assert np.array_equal(base, same)
+    assert np.array_equal(dbl, base * 2)
+    st4, other, _, _ = _q_forward(cfg, 1, q, zero_kv, zero_kv, K8, V8, seq, 0.09, 0.07)
+    assert not np.allclose(other, base)                # the key scale does enter
+
+
+def test_p14_dequantized_rows_within_half_a_step():
+    """Random elements inside the code range come back within scale / 2."""
+    cfg = Cfg(B=1, Hq=2, Hkv=2, D=32, C=40, W=40, seed=144)
+    syn = cfg.synth()
+    ks, vs = 0.02, 0.03
+    q, k, v = syn.step_inputs(np.array([0]), 30)
+    K8 = np.zeros((1, 2, 40, 32), np.int8)
+    st, _, K, V = _q_forward(cfg, 30, q, k, v, K8, K8.copy(), [29], ks, vs)
+    assert st == 0
+    kk = k.reshape(30, 2, 32).transpose(1, 0, 2).astype(np.float64)
+    vv = v.reshape(30, 2, 32).transpose(1, 0, 2).astype(np.float64)
+    for x, c, sc in [(kk, K[0, :, :30], ks), (vv, V[0, :, :30], vs)]:
+        inside = np.abs(x) < 127 * sc
+        assert inside.mean() > 0.9
+        assert np.all(np.abs(c * sc - x)[inside] <= sc / 2 * (1 + 1e-6))
+
+
+def test_p14_step_split_invariance():
+    """Quantization is per element: an 8-token prefill plus a 4-token step
+    and twelve 1-token steps leave the same codes and give the same outputs."""
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=8, C=10, W=6, seed=145)
+    syn = cfg.synth()
+    ks, vs = 0.05, 0.04
+    q, k, v = syn.step_inputs(np.array([0]), 12)
+    K8 = np.zeros((1, 2, 10, 8), np.int8)
+
+    def run(parts):
+        K, V = K8.copy(), K8.copy()
+        outs, t = [], 0
+        for S in parts:
+            sl = slice(t, t + S)
+            st, out, K, V = _q_forward(cfg, S, np.ascontiguousarray(q[:, sl]),
+                                       np.ascontiguousarray(k[:, sl]),
+                                       np.ascontiguousarray(v[:, sl]), K, V, [t + S - 1], ks, vs)
+            assert st == 0
+            outs.append(out)
+            t += S
+        return np.concatenate(outs, axis=1), K, V
+
+    oa, Ka, Va = run([8, 4])
+    ob, Kb, Vb = run([1] * 12)
+    L = oracle.resident_length(12, 10, 6)
+    assert np.array_equal(oa, ob)
+    assert np.array_equal(Ka[:, :, :L], Kb[:, :, :L]) and np.array_equal(Va[:, :, :L], Vb[:, :, :L])
+
+
+def test_p14_zero_query_mean_of_dequantized_positions():
+    """Zero query, V element 0 = absolute position, v_scale 1 (positions
+    below 128 are exact codes): output element 0 is the window mean
+    (lo + p) / 2."""
+    cfg = Cfg(B=1, Hq=4, Hkv=2, D=8, C=9, W=5, seed=146, v_pos=True, zero_q=True)
+    syn = cfg.synth()
+    K8 = np.zeros((1, 2, 9, 8), np.int8)
+    V8 = np.zeros_like(K8)
+    T = 0
+    for S in [6, 1, 1, 1, 4, 1, 1]:
+        q, k, v = syn.step_inputs(np.array([T]), S)
+        st, out, K8, V8 = _q_forward(cfg, S, q, k, v, K8, V8, [T + S - 1], 0.5, 1.0)
+        assert st == 0
+        o = out.reshape(S, 4, 8)[:, :, 0]
+        for i in range(S):
+            p = T + i
+            lo = max(0, p - cfg.W + 1)
+            assert np.allclose(o[i], (lo + p) / 2.0, rtol=0, atol=1e-6)
+        T += S
+
+
+def test_p14_argument_checks():
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=8, C=4, W=4, seed=147)
+    q = np.zeros((1, 1, 16), np.float32)
+    k = np.zeros((1, 1, 8), np.float32)
+    K8 = np.zeros((1, 1, 4, 8), np.int8)
+    assert _q_forward(cfg, 1, q, k, k, K8, K8, [0], 0.0, 1.0)[0] == 1
+    assert _q_forward(cfg, 1, q, k, k, K8, K8, [0], 1.0, float("inf"))[0] == 1
+    p = oracle.make_params(1, 1, 2, 1, 8, 4, 4, 1, kv_cache_type=2, k_scale=1.0, v_scale=1.0)
+    assert oracle.forward(p, q, k, k, K8.copy(), K8.copy(), np.zeros(1, np.int32))[0] == 2
