@@ -52,6 +52,9 @@ class Params(ctypes.Structure):
         ("do_rotary", ctypes.c_int32),
         ("rotary_interleaved", ctypes.c_int32),
         ("rotary_cache_rows", ctypes.c_int32),
+        ("kv_cache_type", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -109,11 +112,11 @@ def make_params(batch_size, sequence_length, num_heads, kv_num_heads, head_size,
                 capacity, local_window_size, total_sequence_length, dtype=F32,
                 scale=0.0, softcap=0.0, bias_dim0_is_batch=1,
                 bias_dim1_is_heads=1, smooth_softmax=0, do_rotary=0, rotary_interleaved=0,
-                rotary_cache_rows=0) -> Params:
+                rotary_cache_rows=0, kv_cache_type=0, k_scale=0.0, v_scale=0.0) -> Params:
     return Params(batch_size, sequence_length, num_heads, kv_num_heads, head_size,
                   capacity, local_window_size, total_sequence_length, scale, softcap,
                   dtype, bias_dim0_is_batch, bias_dim1_is_heads, smooth_softmax, do_rotary,
-                  rotary_interleaved, rotary_cache_rows)
+                  rotary_interleaved, rotary_cache_rows, kv_cache_type, k_scale, v_scale)
 
 
 def _ptr(t):

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
@@ -73,12 +74,21 @@ swgqa_status validate(const swgqa_params* p) {
   if (p->do_rotary && (p->rotary_cache_rows < 1 || p->head_size % 2 != 0)) return SWGQA_ERR_ARG;
   if (p->dtype < SWGQA_F32 || p->dtype > SWGQA_BF16) return SWGQA_ERR_UNSUPPORTED;
   if (!head_size_supported(p->head_size)) return SWGQA_ERR_UNSUPPORTED;
+  if (p->kv_cache_type != 0 && p->kv_cache_type != 1) return SWGQA_ERR_UNSUPPORTED;
+  if (p->kv_cache_type == 1) {
+    if (!(p->k_scale > 0.0f && p->v_scale > 0.0f && std::isfinite(p->k_scale) &&
+          std::isfinite(p->v_scale)))
+      return SWGQA_ERR_ARG;
+    // int8 rows of whole 16-byte chunks; multi-token steps of 16 or more
+    // tokens need the matrix-core kernel, which reads only element-type caches
+    if (p->head_size < 16 || p->sequence_length >= kChunkMinTokens) return SWGQA_ERR_UNSUPPORTED;
+  }
   return SWGQA_OK;
 }
 
 // Launch geometry of the attention kernels, a pure function of the
 // parameters.
-enum class Kind { kSplit, kDecode, kChunk };
+enum class Kind { kSplit, kDecode, kChunk, kDecodeQ8 };
 
 struct SplitPlan {
   Kind kind;    // generic split / staged decode / MFMA chunk kernel
@@ -93,6 +103,35 @@ SplitPlan plan_split(const swgqa_params* p) {
   const int group = p->num_heads / p->kv_num_heads;
   const int per_kv = p->sequence_length * group;  // queries per (item, KV head)
   s.waves = 4;
+  if (p->kv_cache_type == 1) {
+    // int8 cache: every step (S < 16) on the int8 staged kernel, tiles of
+    // 2 or 4 pairs, the same whole-slice / key-split choice as below
+    s.kind = Kind::kDecodeQ8;
+    s.nq = per_kv > 2 ? 4 : 2;
+    s.ntiles = (per_kv + s.nq - 1) / s.nq;
+    const int64_t span = std::min<int64_t>(p->sequence_length, (s.nq + group - 1) / group + 1);
+    int64_t nkeys = (int64_t)p->local_window_size + span - 1;
+    if (nkeys > p->total_sequence_length) nkeys = p->total_sequence_length;
+    const int64_t base = (int64_t)p->batch_size * p->kv_num_heads * s.ntiles;
+    if (base >= kWholeSliceMinTiles || nkeys <= kWholeSliceMaxKeys) {
+      const int64_t slices = (int64_t)p->batch_size * p->kv_num_heads;
+      if (s.nq > 2 && slices * s.ntiles < kDecodeMinWorkgroups) {
+        s.nq = 2;
+        s.ntiles = (per_kv + s.nq - 1) / s.nq;
+      }
+      const int sr = decode_q8_stage_rows(p->head_size, s.nq);
+      const int64_t stages = (nkeys + sr - 1) / sr;
+      s.nsplit = 1;
+      s.waves = stages <= 4 ? 4 : 8;
+      return s;
+    }
+    int64_t ns = base > 0 ? (kTargetWorkgroups + base - 1) / base : 1;
+    const int64_t ns_max = (nkeys + kMinKeysPerSplit - 1) / kMinKeysPerSplit;
+    if (ns > ns_max) ns = ns_max;
+    if (ns < 1) ns = 1;
+    s.nsplit = (int)ns;
+    return s;
+  }
   const bool multi_token = p->sequence_length >= kChunkMinTokens ||
                            (p->sequence_length >= 2 && per_kv >= kChunkMinRows);
   if (multi_token && chunk_kernel_supports(p->dtype, p->head_size)) {
@@ -226,8 +265,9 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
       !present_key || !present_value || !workspace)
     return SWGQA_ERR_ARG;
   const size_t e = elem_bytes(p->dtype);
+  const size_t ce = p->kv_cache_type == 1 ? 1 : e;  // cache element bytes
   const size_t cache_bytes =
-      (size_t)p->batch_size * p->kv_num_heads * p->capacity * p->head_size * e;
+      (size_t)p->batch_size * p->kv_num_heads * p->capacity * p->head_size * ce;
   if (ranges_partially_overlap(past_key, present_key, cache_bytes) ||
       ranges_partially_overlap(past_value, present_value, cache_bytes))
     return SWGQA_ERR_ALIAS;
@@ -316,7 +356,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.bias_h = p->bias_dim1_is_heads ? 1 : 0;
   // in-kernel write-back: one workgroup per slice, or (staged decode) the
   // last query tile of each slice, tracked by a counter
-  const bool counted = s.kind == Kind::kDecode &&
+  const bool counted = (s.kind == Kind::kDecode || s.kind == Kind::kDecodeQ8) &&
                        (int64_t)p->batch_size * p->kv_num_heads <= kMaxSliceCounters;
   a.fuse_writeback = (shared && s.nsplit == 1 && (s.ntiles == 1 || counted)) ? 1 : 0;
   a.waves = s.waves;
@@ -325,6 +365,8 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   // more launch, after every read.
   const bool merge = s.nsplit > 1;
   const bool writeback = !a.fuse_writeback;
+  a.k_scale = p->k_scale;
+  a.v_scale = p->v_scale;
   a.rot_cos = a.rot_sin = nullptr;
   a.rot_pos = nullptr;
   a.rot_rows = a.rot_interleaved = 0;
@@ -342,6 +384,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
 
   const hipError_t ea =
       s.kind == Kind::kChunk    ? launch_attn_chunk(p->dtype, p->head_size, a, st)
+      : s.kind == Kind::kDecodeQ8 ? launch_attn_decode_q8(p->dtype, p->head_size, s.nq, a, st)
       : s.kind == Kind::kDecode
           ? (rot_fused ? launch_attn_decode_rot(p->dtype, p->head_size, s.nq, a, st)
                        : launch_attn_decode(p->dtype, p->head_size, s.nq, a, st))
@@ -369,7 +412,12 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   c.total = p->total_sequence_length;
   c.gdiv = a.gdiv;
   c.D = p->head_size;
-  c.elem_bytes = (int32_t)e;
+  c.elem_bytes = (int32_t)ce;
+  c.quant = p->kv_cache_type == 1 ? 1 : 0;
+  c.src_elem_bytes = (int32_t)e;
+  c.dtype = p->dtype;
+  c.k_scale = p->k_scale;
+  c.v_scale = p->v_scale;
   c.skip_drifting = shared ? 1 : 0;  // drifting appends were done by attention
   if (launch_step_tail(p->dtype, at, c, merge, writeback, st) != hipSuccess) return SWGQA_ERR_HIP;
   return SWGQA_OK;

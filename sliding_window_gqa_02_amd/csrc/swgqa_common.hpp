@@ -251,6 +251,36 @@ __device__ __forceinline__ void load4_elems_unaligned(uint64_t addr, float* out)
   }
 }
 
+// int8 cache codes ("GQA In-Place KV Cache: Investigation Report", section
+// 1.1, names k_scale / v_scale; reading: the code of x is the binary32
+// quotient x / scale rounded to an integer with ties to even, saturated to
+// [-128, 127], NaN going to -128).
+__device__ __forceinline__ uint32_t quant_code(float x, float scale) {
+  float t = rintf(x / scale);
+  t = fminf(fmaxf(t, -128.0f), 127.0f);
+  return (uint32_t)((int32_t)t & 0xFF);
+}
+
+// The 16 codes of elements [c0, c0 + 16) of a row of the element type (row
+// and c0 * e 16-byte aligned).
+template <int DT>
+__device__ __forceinline__ u32x4 quant_chunk16(const void* row, int64_t c0, float scale) {
+  constexpr int e = Elem<DT>::bytes;
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < e; ++i) {  // 16 * e bytes in 16-byte loads
+    const u32x4 v = *(const u32x4*)((const char*)row + c0 * e + i * 16);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) unpack_word<DT>(v[w], x + i * (16 / e) + w * (4 / e));
+  }
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    r[w] = quant_code(x[4 * w], scale) | (quant_code(x[4 * w + 1], scale) << 8) |
+           (quant_code(x[4 * w + 2], scale) << 16) | (quant_code(x[4 * w + 3], scale) << 24);
+  return r;
+}
+
 // seqlens_k[b] (uniform across the workgroup) through the scalar data cache:
 // the array is read-only for the whole launch, and one scalar fetch per CU
 // replaces a vector load from every wave.

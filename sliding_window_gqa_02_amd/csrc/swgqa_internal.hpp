@@ -50,6 +50,8 @@ struct AttnArgs {
   int32_t rot_rows, rot_interleaved;
   void* k_rot;             // rotated new keys (B, S, Hkv*D) for the step tail, or NULL
   int32_t* seqlens_out;    // per-item lengths for the step tail (-2: bad position), or NULL
+  // int8 cache (the int8 decode kernel): element = code * scale
+  float k_scale, v_scale;
 };
 
 struct CopyArgs {
@@ -62,8 +64,14 @@ struct CopyArgs {
   const int32_t* seqlens;
   int32_t B, S, Hkv, C, W, total, D;
   GapDiv gdiv;
-  int32_t elem_bytes;
+  int32_t elem_bytes;     // cache element bytes (1 for int8 codes)
   int32_t skip_drifting;  // shared buffer and the append already fused
+  // int8 cache: new rows (element type, src_elem_bytes each) are quantized
+  // with k_scale / v_scale as they are written
+  int32_t quant;
+  int32_t src_elem_bytes;
+  int32_t dtype;
+  float k_scale, v_scale;
 };
 
 // Rotary pass (swgqa_rotary.hip): rotates q (B,S,Hq,D) and k (B,S,Hkv,D)
@@ -98,6 +106,12 @@ bool decode_kernel_supports(int dtype, int D, int nq);
 int decode_stage_rows(int dtype, int D, int nq);
 hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
                               hipStream_t stream);
+// Staged decode kernel for an int8 cache (swgqa_attn_decode_q8.hip): head
+// sizes 16..256, query tiles of 2 or 4 pairs, S < 16.
+bool decode_q8_supports(int D, int nq);
+int decode_q8_stage_rows(int D, int nq);
+hipError_t launch_attn_decode_q8(int dtype, int D, int nq, const AttnArgs& a,
+                                 hipStream_t stream);
 // The same kernel with rotary embedding fused in (head sizes 32, 64, 128).
 bool decode_rotary_supports(int dtype, int D, int nq);
 hipError_t launch_attn_decode_rot(int dtype, int D, int nq, const AttnArgs& a,

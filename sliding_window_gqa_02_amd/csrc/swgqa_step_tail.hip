@@ -79,7 +79,9 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t bl
   }
 }
 
-// Write-back of one (item, KV head, K|V, column part).
+// Write-back of one (item, KV head, K|V, column part).  With an int8 cache
+// the new rows are quantized as they are written (16 codes per word).
+template <int DT>
 __device__ __forceinline__ void writeback_part(const CopyArgs& a, uint32_t idx) {
   const int64_t rowb = (int64_t)a.D * a.elem_bytes;
   const int64_t w16 = rowb / 16;  // 16-byte words per row (a power of two)
@@ -123,6 +125,17 @@ __device__ __forceinline__ void writeback_part(const CopyArgs& a, uint32_t idx) 
   // 2. New rows i in [max(0, -kept), S) -> row kept + i.
   const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
   const int64_t nw = (a.S - i0) * wn;
+  if (a.quant) {
+    const int64_t src_rowb = (int64_t)a.D * a.src_elem_bytes;
+    const float scale = which ? a.v_scale : a.k_scale;
+    for (int64_t j = tid; j < nw; j += kTailThreads) {
+      const int64_t i = i0 + (j >> wlog);
+      const int64_t w = j & (wn - 1);
+      const char* srow = fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * src_rowb;
+      dst[(pl.kept + i) * w16 + w] = quant_chunk16<DT>(srow, (col * wn + w) * 16, scale);
+    }
+    return;
+  }
   for (int64_t j = tid; j < nw; j += kTailThreads) {
     const int64_t i = i0 + (j >> wlog);
     const int64_t w = j & (wn - 1);
@@ -136,7 +149,7 @@ template <int DT>
 __global__ __launch_bounds__(kTailThreads) void step_tail_kernel(AttnArgs a, CopyArgs c,
                                                                  uint32_t merge_blocks) {
   if (blockIdx.x < merge_blocks) merge_rows<DT>(a, c.D, blockIdx.x);
-  else writeback_part(c, blockIdx.x - merge_blocks);
+  else writeback_part<DT>(c, blockIdx.x - merge_blocks);
 }
 
 }  // namespace

@@ -63,7 +63,7 @@ __device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w
 // Cache write-back of slice (b, kvh) for both K and V, shared buffer.
 __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const ItemPlan& pl,
                                                        int b, int kvh, int D, int e,
-                                                       const u32x4* knew) {
+                                                       const u32x4* knew, const u32x4* vnew) {
   const int64_t rowb = (int64_t)D * e;
   const int64_t w16 = rowb / 16;
   const int64_t off = ((int64_t)b * a.Hkv + kvh) * a.C * rowb;
@@ -83,7 +83,8 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
       const int64_t src = (((int64_t)b * a.S + i) * a.Hkv + kvh) * rowb;
       dk[(pl.kept + i) * w16 + w] = knew ? knew[i * w16 + w]
                                          : ((const u32x4*)((const char*)a.k + src))[w];
-      dv[(pl.kept + i) * w16 + w] = ((const u32x4*)((const char*)a.v + src))[w];
+      dv[(pl.kept + i) * w16 + w] = vnew ? vnew[i * w16 + w]
+                                         : ((const u32x4*)((const char*)a.v + src))[w];
     }
   }
 }
@@ -97,11 +98,12 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
 // call, and rewrites the slice.  Other launch shapes rewrite the cache in a
 // separate kernel.
 //
-// knew, if not NULL, holds the step's new key rows of the slice (S rows of
-// D * e / 16 words, in LDS) to store in place of a.k's.
-template <int DT>
-__device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl, int b, int kvh,
-                                           int D, const u32x4* knew = nullptr) {
+// ce is the cache element size in bytes; knew / vnew, if not NULL, hold the
+// step's new key / value rows of the slice in cache form (S rows of D * ce /
+// 16 words, in LDS) to store in place of a.k's / a.v's.
+__device__ __forceinline__ void slice_tail_rows(const AttnArgs& a, const ItemPlan& pl, int b,
+                                                int kvh, int D, int ce, const u32x4* knew,
+                                                const u32x4* vnew) {
   if (!a.fuse_writeback || pl.shift == 0) return;  // drifting: appended by tile 0
   __syncthreads();  // all reads of this slice by this workgroup are done
   if (a.ntiles > 1) {
@@ -117,7 +119,13 @@ __device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl
     __syncthreads();
     if (!s_last) return;
   }
-  slice_writeback_shared(a, pl, b, kvh, D, Elem<DT>::bytes, knew);
+  slice_writeback_shared(a, pl, b, kvh, D, ce, knew, vnew);
+}
+
+template <int DT>
+__device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl, int b, int kvh,
+                                           int D, const u32x4* knew = nullptr) {
+  slice_tail_rows(a, pl, b, kvh, D, Elem<DT>::bytes, knew, nullptr);
 }
 
 }  // namespace swgqa

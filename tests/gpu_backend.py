@@ -38,6 +38,14 @@ def torch_storage(dtype):
     return torch.float32 if dtype == synth.F32 else torch.int16
 
 
+INT8 = "int8"  # cache storage tag of an int8 cache
+
+
+def cache_poison(cfg: Cfg):
+    from tests.scenario import POISON8
+    return POISON8 if cfg.kv_int8 else nan_value(cfg.dtype)
+
+
 class GuardedCache:
     """A (B, Hkv, C, D) cache inside a larger allocation whose margins hold a
     canary pattern; `intact()` checks nothing was written outside."""
@@ -46,18 +54,24 @@ class GuardedCache:
 
     def __init__(self, shape, dtype):
         n = int(np.prod(shape))
-        st = torch_storage(dtype)
-        self.flat = torch.empty(n + 2 * GUARD, dtype=st, device=DEV)
-        if dtype == synth.F32:
-            self.flat.view(torch.int32).fill_(self.CANARY32)
+        if dtype == INT8:
+            self.flat = torch.empty(n + 2 * GUARD, dtype=torch.int8, device=DEV)
+            self.flat.fill_(0x5A)
         else:
-            self.flat.fill_(0x2BCD)
+            self.flat = torch.empty(n + 2 * GUARD, dtype=torch_storage(dtype), device=DEV)
+            if dtype == synth.F32:
+                self.flat.view(torch.int32).fill_(self.CANARY32)
+            else:
+                self.flat.fill_(0x2BCD)
         self.t = self.flat[GUARD:GUARD + n].view(*shape)
-        self.t.fill_(nan_value(dtype))
+        from tests.scenario import POISON8
+        self.t.fill_(POISON8 if dtype == INT8 else nan_value(dtype))
         self.dtype = dtype
 
     def intact(self) -> bool:
         g = torch.cat([self.flat[:GUARD], self.flat[-GUARD:]])
+        if self.dtype == INT8:
+            return bool((g == 0x5A).all())
         if self.dtype == synth.F32:
             return bool((g.view(torch.int32) == self.CANARY32).all())
         return bool((g == 0x2BCD).all())
@@ -73,9 +87,10 @@ class GpuBackend:
         self.B = B
         self.mode = mode
         shape = (B, cfg.Hkv, cfg.C, cfg.D)
-        self.bufs = [(GuardedCache(shape, cfg.dtype), GuardedCache(shape, cfg.dtype))]
+        ct = INT8 if cfg.kv_int8 else cfg.dtype
+        self.bufs = [(GuardedCache(shape, ct), GuardedCache(shape, ct))]
         if mode == "separate":
-            self.bufs.append((GuardedCache(shape, cfg.dtype), GuardedCache(shape, cfg.dtype)))
+            self.bufs.append((GuardedCache(shape, ct), GuardedCache(shape, ct)))
         if K is not None:
             self.bufs[0][0].t.copy_(to_dev(K))
             self.bufs[0][1].t.copy_(to_dev(V))
@@ -107,7 +122,7 @@ class GpuBackend:
     def poison_unspecified(self, P):
         """Rows [L(P_b), C) of the current cache are unspecified: NaN them so
         that a kernel reading one shows up in the outputs."""
-        nv = nan_value(self.cfg.dtype)
+        nv = cache_poison(self.cfg)
         for b, Pb in enumerate(np.asarray(P)):
             if Pb < 0:
                 continue
@@ -123,7 +138,8 @@ class GpuBackend:
         total = int(seqlens.max()) + 1 if total is None else total
         p = sw.make_params(B, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, total,
                            cfg.dtype, cfg.scale, cfg.softcap, *bias_bcast,
-                           smooth_softmax=int(cfg.smooth), **cfg.rotary_params())
+                           smooth_softmax=int(cfg.smooth), **cfg.rotary_params(),
+                           **cfg.cache_params())
         if poison:
             self.poison_unspecified(seqlens.astype(np.int64) + 1 - S)
         dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
@@ -135,8 +151,8 @@ class GpuBackend:
         if self.mode == "separate":
             nxt = 1 - self.cur
             prk, prv = self.bufs[nxt][0].t, self.bufs[nxt][1].t
-            prk.fill_(nan_value(cfg.dtype))
-            prv.fill_(nan_value(cfg.dtype))
+            prk.fill_(cache_poison(cfg))
+            prv.fill_(cache_poison(cfg))
         else:
             nxt = self.cur
             prk, prv = pk, pv
@@ -159,6 +175,8 @@ class GpuBackend:
         return self.ws is None or int(self.ws[64:4096].abs().sum().item()) == 0
 
     def present_host(self):
+        if self.cfg.kv_int8:
+            return self.K.cpu().numpy(), self.V.cpu().numpy()
         return to_host(self.K, self.cfg.dtype), to_host(self.V, self.cfg.dtype)
 
     def snapshot(self):

@@ -15,6 +15,7 @@ import oracle
 import synth
 
 NAN16 = {synth.F16: 0x7E00, synth.BF16: 0x7FC0}
+POISON8 = 127  # poison code of an int8 cache
 
 
 @dataclasses.dataclass
@@ -35,6 +36,9 @@ class Cfg:
     sink_std: float = 0.0      # > 0: head_sink ~ N(0, sink_std^2) per query head
     rotary: int = -1           # -1 off; 0 pairs (k, k + D/2); 1 interleaved pairs
     rot_rows: int = 4096       # rows of the cos / sin tables
+    kv_int8: bool = False      # int8 cache codes with per-tensor scales
+    k_scale: float = 0.05
+    v_scale: float = 0.04
 
     def synth(self) -> synth.Synth:
         return synth.Synth(self.seed, self.Hq, self.Hkv, self.D, self.dtype,
@@ -45,7 +49,19 @@ class Cfg:
                                   self.Hkv, self.D, self.C, self.W, total,
                                   self.dtype, self.scale, self.softcap,
                                   smooth_softmax=int(self.smooth),
-                                  **self.rotary_params())
+                                  **self.rotary_params(), **self.cache_params())
+
+    def cache_params(self):
+        if not self.kv_int8:
+            return {}
+        return dict(kv_cache_type=1, k_scale=self.k_scale, v_scale=self.v_scale)
+
+    def cache_array(self, shape):
+        """A cache whose every row is poison: NaN, or with int8 codes the
+        extreme code 127 (a read of it moves scores and outputs)."""
+        if self.kv_int8:
+            return np.full(shape, POISON8, dtype=np.int8)
+        return nan_array(shape, self.dtype)
 
     def rotary_params(self):
         if self.rotary < 0:
@@ -106,8 +122,18 @@ def layout_rows(cfg: Cfg, syn: synth.Synth, b: int, T: int, vers: Versions,
 
 def seeded_cache(cfg: Cfg, syn: synth.Synth, Ts, vers: Versions):
     """(B, Hkv, C, D) caches holding the contract layout for lengths Ts and
-    NaN in every unspecified row."""
+    NaN in every unspecified row.  With an int8 cache the resident rows are
+    seeded codes (uniform in [-100, 100]) and the rest poison codes."""
     shape = (len(Ts), cfg.Hkv, cfg.C, cfg.D)
+    if cfg.kv_int8:
+        rng = np.random.default_rng(cfg.seed + 8101)
+        K = cfg.cache_array(shape)
+        V = cfg.cache_array(shape)
+        for b, T in enumerate(Ts):
+            L = oracle.resident_length(int(T), cfg.C, cfg.W)
+            K[b, :, :L] = rng.integers(-100, 101, size=(cfg.Hkv, L, cfg.D))
+            V[b, :, :L] = rng.integers(-100, 101, size=(cfg.Hkv, L, cfg.D))
+        return K, V
     K = nan_array(shape, cfg.dtype)
     V = nan_array(shape, cfg.dtype)
     for b, T in enumerate(Ts):
@@ -130,8 +156,8 @@ class OracleBackend:
         B = cfg.B if B is None else B
         shape = (B, cfg.Hkv, cfg.C, cfg.D)
         self.cfg = cfg
-        self.K = nan_array(shape, cfg.dtype) if K is None else K.copy()
-        self.V = nan_array(shape, cfg.dtype) if V is None else V.copy()
+        self.K = cfg.cache_array(shape) if K is None else K.copy()
+        self.V = cfg.cache_array(shape) if V is None else V.copy()
 
     def step(self, S, seqlens, q, k, v, bias=None, total=None, bias_bcast=(1, 1),
              position_ids=None):

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout():
-    assert ctypes.sizeof(sw.Params) == 17 * 4
+    assert ctypes.sizeof(sw.Params) == 20 * 4
     assert ctypes.sizeof(sw.PlanEntry) == 64
 
 

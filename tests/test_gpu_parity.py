@@ -461,3 +461,100 @@ def test_rotary_position_outside_tables_flags_item(D, mode):
     st, _ = g.step(3, seq, q, k, v, total=8, poison=False,
                    position_ids=np.array([[5, 6, 7], [5, 6, 7], [5, 6, 7]]))
     assert st == sw.OK
+
+
+# ---------------------------------------------------------------------------
+# int8 cache (kv_cache_type 1): per-tensor scales, new rows quantized on the
+# way in, every row read dequantized.  Steps of fewer than 16 tokens on the
+# int8 staged kernel (whole slice, query tiles with the counted compaction,
+# key splits merged by the step tail), both buffer modes; cache codes
+# compared byte for byte with the oracle's.
+Q8 = [
+    Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=61, kv_int8=True),
+    Cfg(B=2, Hq=16, Hkv=2, D=128, C=70, W=64, seed=62, dtype=synth.BF16, softcap=30.0,
+        kv_int8=True, k_scale=0.03, v_scale=0.02),
+    Cfg(B=1, Hq=4, Hkv=4, D=256, C=20, W=17, seed=63, dtype=synth.F16, kv_int8=True),
+    Cfg(B=3, Hq=4, Hkv=2, D=32, C=30, W=20, seed=64, dtype=synth.F16, kv_int8=True,
+        sink_std=1.0),
+    Cfg(B=1, Hq=2, Hkv=1, D=16, C=12, W=9, seed=65, kv_int8=True, smooth=True),
+    Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=66, dtype=synth.BF16, kv_int8=True,
+        rotary=0),
+]
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("cfg", Q8, ids=lambda c: f"D{c.D}t{c.dtype}g{c.Hq // c.Hkv}rot{c.rotary}")
+def test_int8_cache_random_steps(cfg, mode):
+    say(f"int8 cache {cfg} mode={mode}")
+    rng = np.random.default_rng(cfg.seed)
+    run = Lockstep(cfg, mode=mode)
+    T = 0
+    for _ in range(16):
+        S = int(rng.choice([1, 1, 1, 2, 3, 5, 8, 15]))
+        run.step([T] * cfg.B, S)
+        T += S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+def test_int8_cache_ragged_bias_and_key_splits():
+    """Items at different lengths with an absolute-column bias, then a long
+    window over few slices (key splits, merged and written back by the step
+    tail, which quantizes the new rows)."""
+    cfg = Cfg(B=3, Hq=8, Hkv=2, D=64, C=45, W=40, seed=67, dtype=synth.F16, kv_int8=True)
+    syn = cfg.synth()
+    vers = Versions(3)
+    P0 = np.array([0, 37, 90])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S in [8, 1, 5, 1, 3]:
+        total = int((P + S).max())
+        run.step(P, S, bias=_bias_nan_outside(cfg, syn, P, S, total), total=total)
+        P = P + S
+    long = Cfg(B=1, Hq=4, Hkv=1, D=128, C=1600, W=1500, seed=68, dtype=synth.BF16,
+               kv_int8=True)
+    syn = long.synth()
+    vers = Versions(1)
+    P0 = np.array([1700])
+    K, V = seeded_cache(long, syn, P0, vers)
+    for mode in ("shared", "separate"):
+        run = Lockstep(long, mode=mode, K=K, V=V, vers=vers)
+        P = P0.copy()
+        for S in [1, 4, 1, 15]:
+            run.step(P, S)
+            P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+def test_int8_cache_ties_and_saturation():
+    """New elements on exact ties of x / scale and far outside the code
+    range: the GPU stores the oracle's codes (ties to even, saturation)."""
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=16, C=8, W=8, seed=69, kv_int8=True, k_scale=0.25,
+              v_scale=0.5)
+    mult = np.array([2.5, 3.5, -2.5, -3.5, 0.5, -0.5, 1.5, -1.5,
+                     1000.0, -1000.0, 127.5, -128.5, 126.5, -127.5, 0.0, 7.0])
+    run = Lockstep(cfg)
+    q = np.random.default_rng(69).normal(size=(1, 1, 32)).astype(np.float32)
+    k = (mult * 0.25).astype(np.float32).reshape(1, 1, 16)
+    v = (mult * 0.5).astype(np.float32).reshape(1, 1, 16)
+    run.step([0], 1, q=q, k=k, v=v)
+    gk, gv = run.gpu.present_host()
+    want = np.array([2, 4, -2, -4, 0, 0, 2, -2, 127, -128, 127, -128, 126, -128, 0, 7], np.int8)
+    assert np.array_equal(gk[0, 0, 0], want) and np.array_equal(gv[0, 0, 0], want)
+
+
+def test_int8_cache_host_errors():
+    import sliding_window_gqa_02_amd as sw
+    t = torch.zeros(8192, dtype=torch.float32, device="cuda:0")
+    ws = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+    seq = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    mk = lambda **kw: sw.make_params(1, 1, 2, 2, 64, 6, 4, 8, **kw)
+    assert sw.forward_status(mk(kv_cache_type=1, k_scale=0.0, v_scale=1.0), t, t, t, t, t, seq,
+                             None, t, t, t, ws) == sw.ERR_ARG
+    assert sw.forward_status(mk(kv_cache_type=2, k_scale=1.0, v_scale=1.0), t, t, t, t, t, seq,
+                             None, t, t, t, ws) == sw.ERR_UNSUPPORTED
+    p16 = sw.make_params(1, 16, 2, 2, 64, 32, 4, 16, kv_cache_type=1, k_scale=1.0, v_scale=1.0)
+    assert sw.forward_status(p16, t, t, t, t, t, seq, None, t, t, t, ws) == sw.ERR_UNSUPPORTED
+    p8 = sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, kv_cache_type=1, k_scale=1.0, v_scale=1.0)
+    assert sw.forward_status(p8, t, t, t, t, t, seq, None, t, t, t, ws) == sw.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
