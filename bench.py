@@ -38,8 +38,9 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published
 # library's launch planner picks them from the shapes: 2-query tiles x 4 per
 # KV head and 4 waves for the pages' shape, one 4-query tile and 8 waves per
 # slice for the batched serving decode)
-HEADLINE_KERNEL = "attn_decode_kernel<0, 64, 2, 4, 3>"
-SERVING_KERNEL = "attn_decode_kernel<2, 128, 4, 8, 3>"
+HEADLINE_KERNEL = "attn_decode_kernel<0, 64, 2, 4, 3, false>"
+SERVING_KERNEL = "attn_decode_kernel<2, 128, 4, 8, 3, false>"
+SERVING_INT8_KERNEL = "attn_decode_q8_kernel<2, 128, 4, 8>"
 
 
 def log(*a):
@@ -48,20 +49,28 @@ def log(*a):
 
 # ---------------------------------------------------------------------------
 class Workload:
-    def __init__(self, name, B, Hq, Hkv, D, C, W, dtype, scale=0.0, softcap=0.0, seed=0):
+    def __init__(self, name, B, Hq, Hkv, D, C, W, dtype, scale=0.0, softcap=0.0, seed=0,
+                 kv_int8=False, k_scale=0.0, v_scale=0.0):
         self.name, self.B, self.Hq, self.Hkv, self.D = name, B, Hq, Hkv, D
         self.C, self.W, self.dtype, self.scale, self.softcap, self.seed = C, W, dtype, scale, softcap, seed
         self.e = 4 if dtype == 0 else 2
+        self.kv_int8, self.k_scale, self.v_scale = kv_int8, k_scale, v_scale
+        self.ce = 1 if kv_int8 else self.e  # cache element bytes
+
+    def cache_params(self) -> dict:
+        return dict(kv_cache_type=1, k_scale=self.k_scale, v_scale=self.v_scale) if self.kv_int8 else {}
 
     def step_bytes(self, T: np.ndarray, S: int, sw, bias: bool = False) -> dict:
         """Algorithmic HBM bytes of one step for items with lengths T (after
         the step): distinct K/V rows the queries read, Q read, output write,
         appended rows, rows moved by block compaction (read + write), and the
         attention_bias entries of visible keys."""
-        row = self.D * self.e
+        row = self.D * self.e      # a query / output / new row
+        crow = self.D * self.ce    # a cache row
         P = T - S
         n_kv = np.minimum(T, self.W + S - 1)
-        kv_read = int(np.sum(self.Hkv * 2 * n_kv * row))
+        # resident rows from the cache, the S new rows from key / value
+        kv_read = int(np.sum(self.Hkv * 2 * ((n_kv - S) * crow + S * row)))
         qo = 2 * len(T) * S * self.Hq * row
         if bias:
             qo += int(np.sum(self.visible_keys(T, S))) * self.Hq * self.e
@@ -69,8 +78,8 @@ class Workload:
         Lb = np.array([sw.resident_length(int(p), self.C, self.W) for p in P])
         shift = Lb + S - La
         kept = La - S
-        append = int(np.sum(self.Hkv * 2 * np.minimum(S, La) * row))
-        moved = int(np.sum(np.where((shift > 0) & (kept > 0), self.Hkv * 2 * 2 * kept * row, 0)))
+        append = int(np.sum(self.Hkv * 2 * np.minimum(S, La) * crow))
+        moved = int(np.sum(np.where((shift > 0) & (kept > 0), self.Hkv * 2 * 2 * kept * crow, 0)))
         return {"kv_read": kv_read, "qo": qo, "append": append, "compaction": moved,
                 "total": kv_read + qo + append + moved}
 
@@ -128,7 +137,7 @@ class DecodeLoop:
             rot = dict(do_rotary=1, rotary_interleaved=rotary, rotary_cache_rows=rows)
             self.tables = tuple(to_dev(torch, t) for t in synth.rotary_tables(rows, wl.D, wl.dtype))
         self.p = sw.make_params(B, S, wl.Hq, wl.Hkv, wl.D, wl.C, wl.W, total, wl.dtype,
-                                wl.scale, wl.softcap, **rot)
+                                wl.scale, wl.softcap, **rot, **wl.cache_params())
         nbytes = sw.workspace_size(self.p)
         self.ws = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda:0")
         sw.workspace_init(self.ws)
@@ -235,8 +244,14 @@ def seeded_cache(torch, sw, wl: Workload, P0: np.ndarray):
     [0, L(P_b)) = regenerated positions P_b - L + r); the layout depends only
     on the length, so this equals the state a prefill + decodes would leave."""
     import synth
-    syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
     shape = (wl.B, wl.Hkv, wl.C, wl.D)
+    if wl.kv_int8:  # seeded codes, uniform in [-100, 100]
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(wl.seed)
+        K = torch.randint(-100, 101, shape, dtype=torch.int8, device="cuda:0", generator=g)
+        V = torch.randint(-100, 101, shape, dtype=torch.int8, device="cuda:0", generator=g)
+        return K, V
+    syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
     st = storage_torch_dtype(torch, wl.dtype)
     K = torch.zeros(shape, dtype=st, device="cuda:0")
     V = torch.zeros(shape, dtype=st, device="cuda:0")
@@ -430,6 +445,38 @@ def small_slack(torch, sw):
     out, _ = loop_stats(torch, loop, snap, 1)
     out["workload"] = ("decode after a 512-token prompt, B=1, 64 Q / 8 KV heads x 64, fp32, "
                        "W=128, C=136 (G=9), 400 steps")
+    return out
+
+
+def serving_int8(torch, sw, no_graph: bool):
+    """The batched-serving decode with an int8 cache (per-tensor scales): the
+    same shape, half the cache bytes of bf16."""
+    srv = Workload("batched_serving_int8", B=32, Hq=32, Hkv=8, D=128, C=4608, W=4096, dtype=2,
+                   softcap=50.0, seed=1006, kv_int8=True, k_scale=0.02, v_scale=0.02)
+    rng = np.random.default_rng(1005)
+    Ps = rng.integers(4096, 32769, size=32)
+    K, V = seeded_cache(torch, sw, srv, Ps)
+    snap = (K.clone(), V.clone())
+    loop = DecodeLoop(torch, sw, srv, Ps, 128, K, V)
+    loop.run(torch.cuda.current_stream())  # warm-up
+    torch.cuda.synchronize()
+    r = time_decode(torch, loop, snap, not no_graph)
+    byts = loop.bytes_per_step()
+    graph = bool(r.get("graph_ok") and r["graph_s"])
+    wall = r["graph_s"] if graph else r["eager_s"]
+    kms = r["graph_kernel_ms"] if graph else float(np.mean(r["step_ms"]))
+    kv = sum(b["kv_read"] for b in byts) / 128 / (kms / 1e3) / 1e9
+    out = {
+        "workload": "B=32 decode, 32 Q / 8 KV heads x 128, bf16 queries, int8 cache "
+                    "(k_scale = v_scale = 0.02), W=4096, C=4608, softcap 50, past lengths "
+                    "U[4096, 32768], 128 steps",
+        "tokens_per_s": round(32 * 128 / wall, 1),
+        "ms_per_step": round(wall / 128 * 1e3, 5),
+        "mode": "hip_graph" if graph else "eager",
+        "kv_read_GBps": round(kv, 1),
+        "roofline": roofline(byts, kms, SERVING_INT8_KERNEL),
+    }
+    del K, V, snap, loop
     return out
 
 
@@ -635,6 +682,10 @@ def main():
             "roofline": srl,
         }
         del Ks, Vs, ssnap, sloop
+
+    if not args.no_extra and not args.no_serving:
+        log("serving decode, int8 cache ...")
+        result["serving_int8"] = serving_int8(torch, sw, args.no_graph)
 
     if not args.no_extra:
         log("rotary decode ...")

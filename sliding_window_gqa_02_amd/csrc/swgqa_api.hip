@@ -107,7 +107,11 @@ SplitPlan plan_split(const swgqa_params* p) {
     // int8 cache: every step (S < 16) on the int8 staged kernel, tiles of
     // 2 or 4 pairs, the same whole-slice / key-split choice as below
     s.kind = Kind::kDecodeQ8;
+#ifdef SWGQA_Q8_NQ
+    s.nq = SWGQA_Q8_NQ;
+#else
     s.nq = per_kv > 2 ? 4 : 2;
+#endif
     s.ntiles = (per_kv + s.nq - 1) / s.nq;
     const int64_t span = std::min<int64_t>(p->sequence_length, (s.nq + group - 1) / group + 1);
     int64_t nkeys = (int64_t)p->local_window_size + span - 1;

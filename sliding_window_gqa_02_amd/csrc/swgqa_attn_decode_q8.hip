@@ -34,12 +34,23 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQ8MaxNewRows = 16;  // S < 16 on this path
 
+// Stages of K/V loads in flight per wave.
+#ifndef SWGQA_Q8_DEPTH
+#define SWGQA_Q8_DEPTH 3
+#endif
+
+#ifndef SWGQA_Q8_UMUL
+#define SWGQA_Q8_UMUL 1
+#endif
+
 template <int D, int NQ>
 struct Q8Shape {
   static constexpr int EPL = 16;                           // codes per lane per row
   static constexpr int LPR = D / 16;                       // lanes per row
   static constexpr int RPW = kWave / (LPR > 0 ? LPR : 1);  // rows per load instruction
-  static constexpr int U = (LPR / NQ) >= 1 ? (LPR / NQ) : 1;  // loads per stage
+  // loads per stage: SWGQA_Q8_UMUL x (LPR / NQ), so that a stage's fixed
+  // cost (the softmax step) is spread over more rows than a 16-bit stage
+  static constexpr int U = (SWGQA_Q8_UMUL * LPR / NQ) >= 1 ? (SWGQA_Q8_UMUL * LPR / NQ) : 1;
   static constexpr int SR = RPW * U;                       // rows per wave stage
   static constexpr int PAIRS = SR * NQ;                    // (row, query) pairs per stage
   static constexpr int PPL = PAIRS / kWave;                // pairs per lane
@@ -68,6 +79,32 @@ __device__ __forceinline__ float allreduce_q8(float x) {
   if constexpr (NQ <= 16) x = op(x, __shfl_xor(x, 16, kWave));
   if constexpr (NQ <= 32) x = op(x, __shfl_xor(x, 32, kWave));
   return x;
+}
+
+// Two codes (exact as floats) as one packed pair of the 16-bit type: the
+// upper half of each float for bf16, a conversion for fp16 (integers of at
+// most 8 bits are exact in both).
+template <int DT>
+__device__ __forceinline__ uint32_t pack_pair16(float lo, float hi) {
+  if constexpr (DT == kBF16) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+}
+
+// Packed dot of two 16-bit pairs, accumulated in fp32.
+template <int DT>
+__device__ __forceinline__ float dot2_16(uint32_t a, uint32_t b, float acc) {
+  if constexpr (DT == kBF16) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a), __builtin_bit_cast(bf2, b),
+                                           acc, false);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), acc,
+                                  false);
+  }
 }
 
 // The four signed codes of a word, as floats (exact).
@@ -116,11 +153,13 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
 
   const int nq_item = a.S * a.group;
   const int q0 = tile * NQ;
-  // Query tile in fp32: elements [sub * 16, sub * 16 + 16) of each pair,
-  // pairs walked position-major with a carry.
+  // Query tile: elements [sub * 16, sub * 16 + 16) of each pair, as 16
+  // words (fp32) or 8 packed pairs (fp16 / bf16); pairs walked
+  // position-major with a carry.
   const int i_first = q0 / a.group;
   int i_last = i_first;
-  float qf[NQ][EPL];
+  constexpr int QW = EPL * e / 4;  // words of a query chunk
+  uint32_t qw[NQ][QW];
   {
     int h = q0 - i_first * a.group;
 #pragma unroll
@@ -128,10 +167,10 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       const int64_t row = ((int64_t)b * a.S + i_last) * a.Hq + kvh * a.group + h;
       const char* qp = (const char*)a.q + (row * D + sub * EPL) * e;
 #pragma unroll
-      for (int i = 0; i < EPL * e / 16; ++i) {
+      for (int i = 0; i < QW / 4; ++i) {
         const u32x4 v = *(const u32x4*)(qp + i * 16);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) unpack_word<DT>(v[w], &qf[tq][i * 16 / e + w * (4 / e)]);
+        for (int w = 0; w < 4; ++w) qw[tq][4 * i + w] = v[w];
       }
       if (tq + 1 < NQ && q0 + tq + 1 < nq_item && ++h == a.group) {
         h = 0;
@@ -263,12 +302,19 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   auto compute_stage = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) __attribute__((always_inline)) {
     const uint32_t s0 = (uint32_t)st * SR;
     if (s0 + SR > (uint32_t)ncache) {  // uniform: the stage reaches new rows
+      // branch-free per lane: every lane reads LDS (a clamped row) and
+      // selects, so no register with a load in flight is overwritten
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t jr = min(s0 + u * RPW + rslot, (uint32_t)(nk - 1));
-        if (jr >= (uint32_t)ncache) {
-          kr[u] = s_knew[(knew0 + (int)jr) * W16 + sub];
-          vr[u] = s_vnew[(knew0 + (int)jr) * W16 + sub];
+        const bool is_new = jr >= (uint32_t)ncache;
+        const int r = is_new ? knew0 + (int)jr : 0;
+        const u32x4 kn = s_knew[r * W16 + sub];
+        const u32x4 vn = s_vnew[r * W16 + sub];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kr[u][w] = is_new ? kn[w] : kr[u][w];
+          vr[u][w] = is_new ? vn[w] : vr[u][w];
         }
       }
     }
@@ -279,15 +325,31 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       float kf[EPL];
 #pragma unroll
       for (int w = 0; w < 4; ++w) codes4(kr[u][w], kf + 4 * w);
+      if constexpr (DT == kF32) {
 #pragma unroll
-      for (int tq = 0; tq < NQ; ++tq) {
-        float d0 = 0.0f, d1 = 0.0f;
+        for (int tq = 0; tq < NQ; ++tq) {
+          float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
-        for (int k = 0; k < EPL; k += 2) {
-          d0 = fmaf(qf[tq][k], kf[k], d0);
-          d1 = fmaf(qf[tq][k + 1], kf[k + 1], d1);
+          for (int k = 0; k < EPL; k += 2) {
+            d0 = fmaf(__uint_as_float(qw[tq][k]), kf[k], d0);
+            d1 = fmaf(__uint_as_float(qw[tq][k + 1]), kf[k + 1], d1);
+          }
+          part[(tq * SR + row) * LPR + sub] = d0 + d1;
         }
-        part[(tq * SR + row) * LPR + sub] = d0 + d1;
+      } else {
+        uint32_t kp[EPL / 2];  // the codes as packed 16-bit pairs (exact)
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j) kp[j] = pack_pair16<DT>(kf[2 * j], kf[2 * j + 1]);
+#pragma unroll
+        for (int tq = 0; tq < NQ; ++tq) {
+          float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < EPL / 2; j += 2) {
+            d0 = dot2_16<DT>(qw[tq][j], kp[j], d0);
+            d1 = dot2_16<DT>(qw[tq][j + 1], kp[j + 1], d1);
+          }
+          part[(tq * SR + row) * LPR + sub] = d0 + d1;
+        }
       }
     }
     wave_lds_fence_q8();
@@ -364,8 +426,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
     wave_lds_fence_q8();
   };
 
-  // Stages of this wave: wave, wave + kWaves, ...; the next stage's loads
-  // are in flight while one is computed.
+  // Stages of this wave: wave, wave + kWaves, ...; the loads of the next
+  // DEPTH - 1 stages are in flight while one is computed.
   u32x4 k0[U], v0[U], k1[U], v1[U];
   int st = wave;
   if (nk == 0) {
@@ -375,15 +437,33 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       load_stage(wave, k0, v0);
       compute_stage(wave, k0, v0);
     }
+  } else if constexpr (SWGQA_Q8_DEPTH == 3) {
+    // whole groups of three stages, no exit between them (a stage past the
+    // end loads clamped rows and is not computed)
+    u32x4 k2[U], v2[U];
+    load_stage(st, k0, v0);
+    load_stage(st + kWaves, k1, v1);
+    const int groups = (nst - wave + 3 * kWaves - 1) / (3 * kWaves);
+    for (int g = 0; g < groups; ++g) {
+      load_stage(st + 2 * kWaves, k2, v2);
+      compute_stage(st, k0, v0);
+      st += kWaves;
+      load_stage(st + 2 * kWaves, k0, v0);
+      if (st < nst) compute_stage(st, k1, v1);
+      st += kWaves;
+      load_stage(st + 2 * kWaves, k1, v1);
+      if (st < nst) compute_stage(st, k2, v2);
+      st += kWaves;
+    }
   } else {
     load_stage(st, k0, v0);
-    while (st < nst) {
+    const int groups = (nst - wave + 2 * kWaves - 1) / (2 * kWaves);
+    for (int g = 0; g < groups; ++g) {
       load_stage(st + kWaves, k1, v1);
       compute_stage(st, k0, v0);
       st += kWaves;
-      if (st >= nst) break;
       load_stage(st + kWaves, k0, v0);
-      compute_stage(st, k1, v1);
+      if (st < nst) compute_stage(st, k1, v1);
       st += kWaves;
     }
   }
