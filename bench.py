@@ -683,7 +683,7 @@ def main():
         }
         del Ks, Vs, ssnap, sloop
 
-    if not args.no_extra and not args.no_serving:
+    if not args.no_serving:
         log("serving decode, int8 cache ...")
         result["serving_int8"] = serving_int8(torch, sw, args.no_graph)
 
