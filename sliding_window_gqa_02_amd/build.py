@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libswgqa.so")
 SOURCES = ["swgqa_api.hip", "swgqa_attn_split.hip", "swgqa_attn_decode.hip",
            "swgqa_attn_decode_rot.hip", "swgqa_attn_decode_q8.hip",
-           "swgqa_attn_chunk.hip", "swgqa_step_tail.hip", "swgqa_copy.hip",
+           "swgqa_attn_chunk.hip", "swgqa_attn_chunk_q8.hip", "swgqa_step_tail.hip", "swgqa_copy.hip",
            "swgqa_rotary.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

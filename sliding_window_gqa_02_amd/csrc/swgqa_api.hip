@@ -79,9 +79,8 @@ swgqa_status validate(const swgqa_params* p) {
     if (!(p->k_scale > 0.0f && p->v_scale > 0.0f && std::isfinite(p->k_scale) &&
           std::isfinite(p->v_scale)))
       return SWGQA_ERR_ARG;
-    // int8 rows of whole 16-byte chunks; multi-token steps of 16 or more
-    // tokens need the matrix-core kernel, which reads only element-type caches
-    if (p->head_size < 16 || p->sequence_length >= kChunkMinTokens) return SWGQA_ERR_UNSUPPORTED;
+    // int8 rows of whole 16-byte chunks
+    if (p->head_size < 16) return SWGQA_ERR_UNSUPPORTED;
   }
   return SWGQA_OK;
 }
@@ -103,9 +102,13 @@ SplitPlan plan_split(const swgqa_params* p) {
   const int group = p->num_heads / p->kv_num_heads;
   const int per_kv = p->sequence_length * group;  // queries per (item, KV head)
   s.waves = 4;
-  if (p->kv_cache_type == 1) {
-    // int8 cache: every step (S < 16) on the int8 staged kernel, tiles of
-    // 2 or 4 pairs, the same whole-slice / key-split choice as below
+  const bool multi_token = p->sequence_length >= kChunkMinTokens ||
+                           (p->sequence_length >= 2 && per_kv >= kChunkMinRows);
+  if (p->kv_cache_type == 1 && !(p->sequence_length >= kChunkMinTokens &&
+                                 chunk_kernel_supports(p->dtype, p->head_size))) {
+    // int8 cache: steps of S < 16 on the int8 staged kernel, tiles of 2 or 4
+    // pairs, the same whole-slice / key-split choice as below (longer steps
+    // take the matrix-core kernel, with codes)
     s.kind = Kind::kDecodeQ8;
 #ifdef SWGQA_Q8_NQ
     s.nq = SWGQA_Q8_NQ;
@@ -136,8 +139,6 @@ SplitPlan plan_split(const swgqa_params* p) {
     s.nsplit = (int)ns;
     return s;
   }
-  const bool multi_token = p->sequence_length >= kChunkMinTokens ||
-                           (p->sequence_length >= 2 && per_kv >= kChunkMinRows);
   if (multi_token && chunk_kernel_supports(p->dtype, p->head_size)) {
     // multi-token step on the matrix cores
     s.kind = Kind::kChunk;
@@ -214,10 +215,18 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // per-item lengths.
 struct RotaryScratch {
   size_t q_off, k_off, seq_off, end;
+  size_t kq_off, vq_off;  // int8 codes of the new rows (chunk kernel over an int8 cache)
 };
 
-RotaryScratch rotary_scratch(const swgqa_params* p, size_t start) {
-  RotaryScratch r{start, start, start, start};
+RotaryScratch rotary_scratch(const swgqa_params* p, size_t start, const SplitPlan& s) {
+  RotaryScratch r{start, start, start, start, start, start};
+  if (p->kv_cache_type == 1 && s.kind == Kind::kChunk) {
+    const size_t n = (size_t)p->batch_size * p->sequence_length * p->kv_num_heads * p->head_size;
+    r.kq_off = start;
+    r.vq_off = r.kq_off + align256(n);
+    start = r.vq_off + align256(n);
+    r.q_off = r.k_off = r.seq_off = r.end = start;
+  }
   if (!p->do_rotary) return r;
   const size_t e = elem_bytes(p->dtype);
   const size_t rows = (size_t)p->batch_size * p->sequence_length;
@@ -243,7 +252,7 @@ extern "C" {
 size_t swgqa_workspace_size(const swgqa_params* p) {
   if (validate(p) != SWGQA_OK) return 0;
   const SplitPlan s = plan_split(p);
-  return rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s))).end;
+  return rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s)), s).end;
 }
 
 swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
@@ -284,7 +293,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   if (align_or & 15u) return SWGQA_ERR_ARG;
 
   const SplitPlan s = plan_split(p);
-  const RotaryScratch rs = rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s)));
+  const RotaryScratch rs = rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s)), s);
   if (workspace_bytes < rs.end) return SWGQA_ERR_ARG;
   if (p->do_rotary && (!cos_cache || !sin_cache)) return SWGQA_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
@@ -321,6 +330,20 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
     seqlens_k = r.seqlens_out;
   }
   const bool shared = present_key == past_key && present_value == past_value;
+  // int8 cache on the matrix-core kernel: the new rows as codes first
+  const bool chunk_q8 = p->kv_cache_type == 1 && s.kind == Kind::kChunk;
+  const void* key_rows = key;    // the new rows as the element type (rotated)
+  const void* value_rows = value;
+  if (chunk_q8) {
+    uint8_t* kq = (uint8_t*)workspace + rs.kq_off;
+    uint8_t* vq = (uint8_t*)workspace + rs.vq_off;
+    const size_t n = (size_t)p->batch_size * p->sequence_length * p->kv_num_heads * p->head_size;
+    if (launch_quant_rows(p->dtype, key, value, kq, vq, n, p->k_scale, p->v_scale, st) !=
+        hipSuccess)
+      return SWGQA_ERR_HIP;
+    key = kq;
+    value = vq;
+  }
 
   AttnArgs a;
   a.q = query;
@@ -387,7 +410,8 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   }
 
   const hipError_t ea =
-      s.kind == Kind::kChunk    ? launch_attn_chunk(p->dtype, p->head_size, a, st)
+      s.kind == Kind::kChunk    ? (chunk_q8 ? launch_attn_chunk_q8(p->dtype, p->head_size, a, st)
+                                            : launch_attn_chunk(p->dtype, p->head_size, a, st))
       : s.kind == Kind::kDecodeQ8 ? launch_attn_decode_q8(p->dtype, p->head_size, s.nq, a, st)
       : s.kind == Kind::kDecode
           ? (rot_fused ? launch_attn_decode_rot(p->dtype, p->head_size, s.nq, a, st)
@@ -403,8 +427,8 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   CopyArgs c;
   c.past_k = past_key;
   c.past_v = past_value;
-  c.k = rot_fused ? a.k_rot : key;
-  c.v = value;
+  c.k = rot_fused ? a.k_rot : key_rows;  // element-type rows (quantized as written)
+  c.v = value_rows;
   c.present_k = present_key;
   c.present_v = present_value;
   c.seqlens = rot_fused ? a.seqlens_out : seqlens_k;

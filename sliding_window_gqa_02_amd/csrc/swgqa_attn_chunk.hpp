@@ -1,0 +1,628 @@
+// swgqa_attn_chunk.hpp -- grouped-query attention for multi-token steps
+// (prefill, chunked prefill, S >= 16) over a windowed KV cache, on the CDNA4
+// matrix cores.  Instantiated for element-type caches in
+// swgqa_attn_chunk.hip and for int8 caches in swgqa_attn_chunk_q8.hip.
+//
+// Same contract as the decode kernels: query i of item b at absolute
+// position p = P + i attends to keys p - W < j <= p of [resident rows | S
+// new rows] ("Specify GroupQueryAttention windowed KV cache layout
+// contract", Description; causal rule of "Fix CPU Attention causal mask
+// ..."), keys below P read from cache row j - (P - Lb), the rest straight
+// from the new rows, so a step that evicts history it still reads needs no
+// staging copy ("[CPU] Add windowed kv cache for GQA", staging).
+//
+// A workgroup (4 waves) owns 64 consecutive (position, head) query rows of
+// one KV head's group and walks the key band [p_first - W + 1, p_last] in
+// blocks of 32 keys staged in LDS -- every K/V row staged is used by all the
+// heads of the group.  Per block each wave (16 query rows):
+//   S^T = K . Q^T   16 keys x 16 queries per MFMA (Q^T is the B operand, held
+//                   in registers for the whole band);
+//   softmax         each lane owns one query column, so max / sum need only
+//                   in-lane work plus two cross-lane steps, and every
+//                   (query, key) score is transformed exactly once;
+//   O^T += V^T . P^T  the S^T accumulator registers are the P^T operand as
+//                   they stand (keys on the reduction axis), and O^T keeps
+//                   the same one-query-per-lane-column layout as the softmax
+//                   state, so rescaling needs no shuffles.
+// fp32 uses v_mfma_f32_16x16x4_f32 (full fp32 products); fp16 / bf16 use the
+// 16x16x16 forms.  P enters the PV product rounded to fp16 (the normaliser
+// sums the rounded P, so the result is an exact weighted mean of V), or for
+// bf16 as a hi + lo pair of bf16 values (8 significant bits alone would move
+// a mean of few keys by ~2^-9).
+// The next block's K/V are loaded into registers while the current block is
+// computed.
+//
+// With an int8 cache (Q8; the Investigation Report, section 1.1, names
+// k_scale / v_scale; reading: element = code * scale, new elements quantized
+// with ties to even and saturation) every key row is read as codes -- the
+// cache rows, and the step's new rows from a workspace copy the quantization
+// pass wrote -- 16 / e codes where an element-type row has 16 bytes; the
+// codes enter LDS converted to the element type (integers of at most 8 bits
+// are exact in fp32, fp16 and bf16), k_scale joins the score scale and
+// v_scale the output.
+#pragma once
+
+#include "swgqa_common.hpp"
+#include "swgqa_internal.hpp"
+#include "swgqa_tail.hpp"
+
+#include <math.h>
+
+namespace swgqa {
+
+namespace {
+
+// A workgroup of NW waves (4 or 8) owns 16 NW query rows.
+constexpr int BN = 32;   // keys per block
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+
+template <int DT, int D, int NW>
+struct ChunkShape {
+  static constexpr int kThreads = NW * kWave;
+  static constexpr int e = Elem<DT>::bytes;
+  // LDS row strides (elements), chosen so the MFMA operand reads of 16 lanes
+  // on 16 different rows fall in distinct banks
+  static constexpr int KS = (DT == kF32) ? D + 2 : D + 8;   // K rows: [key][d]
+  static constexpr int VS = (DT == kF32) ? D + 4 : BN + 4;  // fp32 V [key][d]; 16-bit V^T [d][key]
+  static constexpr int KELEMS = BN * KS;
+  static constexpr int VELEMS = (DT == kF32) ? BN * VS : D * VS;
+  static constexpr int CHUNKS = BN * D * e / 16;           // 16-byte chunks per block per tensor
+  static constexpr int CPT = (CHUNKS + kThreads - 1) / kThreads;  // per thread
+  static constexpr int DSTEPS = (DT == kF32) ? D / 4 : D / 16;  // S^T MFMA steps
+  static constexpr int DT16 = D / 16;                      // O^T tiles
+  static constexpr bool ok = D >= 16 && D % 16 == 0 && D * e <= 512;
+};
+
+template <int DT> struct LdsT { using T = float; };
+template <> struct LdsT<kF16> { using T = uint16_t; };
+template <> struct LdsT<kBF16> { using T = uint16_t; };
+
+// Key swizzle of row d of the transposed V tile (16-bit types): XOR of key
+// bits 2..4 with d / 8, so groups of 4 consecutive keys stay contiguous.
+__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) << 2; }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  union { _Float16 h; uint16_t u; } c;
+  c.h = (_Float16)x;
+  return c.u;
+}
+
+// BIAS: attention_bias present (a separate instantiation, so that the loads
+// of a block are the same on every path and the compiler can wait for
+// exactly the block it stages).
+// 16 / e codes (4 bytes for fp32, 8 for fp16 / bf16) at a global address, in
+// the low words of a chunk register.
+template <int DT>
+__device__ __forceinline__ u32x4 load_codes(uint64_t addr) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if constexpr (DT == kF32) {
+    r[0] = *(const uint32_t __attribute__((address_space(1)))*)addr;
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = *(const u32x2 __attribute__((address_space(1)))*)addr;
+    r[0] = v[0];
+    r[1] = v[1];
+  }
+  return r;
+}
+
+// Codes (low words of c) as the element type, one 16-byte chunk: exact.
+template <int DT>
+__device__ __forceinline__ u32x4 codes_to_elems(const u32x4& c) {
+  u32x4 r;
+  auto f = [](uint32_t w, int i) { return (float)(int32_t)(int8_t)((w >> (8 * i)) & 0xFFu); };
+  if constexpr (DT == kF32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(f(c[0], i));
+  } else {
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float lo = f(c[w], 2 * h), hi = f(c[w], 2 * h + 1);
+        if constexpr (DT == kBF16)
+          r[2 * w + h] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+        else
+          r[2 * w + h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+      }
+  }
+  return r;
+}
+
+template <int DT, int D, bool BIAS, int NW, bool Q8>
+__global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
+  using Sh = ChunkShape<DT, D, NW>;
+  constexpr int kThreads = Sh::kThreads;
+  constexpr int BQ = 16 * NW;  // query rows per workgroup
+  using LT = typename LdsT<DT>::T;
+  constexpr int e = Sh::e, KS = Sh::KS, VS = Sh::VS, CPT = Sh::CPT, DSTEPS = Sh::DSTEPS;
+  constexpr int DT16 = Sh::DT16;
+  constexpr int CPR = D * e / 16;  // 16-byte element chunks per row
+  constexpr int CE = Q8 ? 1 : e;   // bytes of a cache (or new-row copy) element
+  constexpr int CPRC = D * CE / 16;  // 16-byte chunks per cache row
+  static_assert(Sh::ok, "unsupported chunk shape");
+  static_assert(!Q8 || D >= 16, "int8 rows of whole 16-byte chunks");
+
+  __shared__ LT sK[Sh::KELEMS];
+  __shared__ LT sV[Sh::VELEMS];
+
+  // work item P of the launch: slice P / T, item (tile, split) P % T
+  const uint32_t T = gridDim.x;  // ntiles * nsplit
+  const uint32_t P = xcd_contiguous(blockIdx.x + T * (blockIdx.y + gridDim.y * blockIdx.z),
+                                    T * gridDim.y * gridDim.z);
+  const uint32_t slice = div_gap(P, a.tdiv);
+  const uint32_t t = P - slice * T;
+  const int b = (int)div_gap(slice, a.hdiv);
+  const int kvh = (int)slice - b * a.Hkv;
+  const int tile = (int)t / a.nsplit;
+  const int split = (int)t % a.nsplit;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int lq = lane % 16;   // query column of this lane
+  const int lg = lane / 16;   // lane group (0..3)
+
+  // seqlens_k first: the plan and every K/V address wait on it
+  const int32_t seqlen = load_seqlen(a.seqlens, b);
+  const int nq_item = a.S * a.group;
+  const int q0 = tile * BQ;
+
+  // This lane's query (column lq of wave's 16 rows), loaded before the
+  // plan: its address does not depend on seqlens_k.
+  const int my_qi = q0 + wave * 16 + lq;
+  const bool my_ok = my_qi < nq_item;
+  const int my_qc = my_ok ? my_qi : nq_item - 1;
+  const int my_i = my_qc / a.group;
+  const int my_h = kvh * a.group + my_qc % a.group;
+  const int i_first = q0 / a.group;
+  const int i_last = (min(q0 + BQ, nq_item) - 1) / a.group;
+
+  // Q^T operand: fp32 step s holds Q[q][4s + lg]; 16-bit step s holds
+  // Q[q][16s + 4lg .. +3].
+  const char* qrow = (const char*)a.q + ((((int64_t)b * a.S + my_i) * a.Hq + my_h) * D) * e;
+  float qf[DT == kF32 ? DSTEPS : 1];
+  uint32_t qh[DT == kF32 ? 1 : DSTEPS][2];
+  if constexpr (DT == kF32) {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) qf[s] = ((const float*)qrow)[4 * s + lg];
+  } else {
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) {
+      const uint2 v = *(const uint2*)(qrow + (16 * s + 4 * lg) * 2);
+      qh[s][0] = v.x;
+      qh[s][1] = v.y;
+    }
+  }
+
+  const ItemPlan pl = plan_item(seqlen, a.S, a.C, a.gdiv, a.total);
+  const int64_t my_pos = pl.P + my_i;
+
+  if (!pl.ok) {
+    if (tid == 0 && tile == 0 && split == 0 && kvh == 0) flag_status(a.status, kStatusBadItem);
+    for (int idx = tid; idx < BQ * D; idx += kThreads) {
+      const int t = idx / D, d = idx % D;
+      const int qi = q0 + t;
+      if (qi >= nq_item) continue;
+      const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+      const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
+      if (a.nsplit == 1) {
+        if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = 0.0f;
+        else ((uint16_t*)a.out)[row * D + d] = 0;
+      } else {
+        a.opart[(row * a.nsplit + split) * D + d] = 0.0f;
+        if (d == 0) {
+          a.ml[(row * a.nsplit + split) * 2 + 0] = -INFINITY;
+          a.ml[(row * a.nsplit + split) * 2 + 1] = 0.0f;
+        }
+      }
+    }
+    return;
+  }
+
+  // Key band of the tile and this split's part of it.
+  const int64_t p_first = pl.P + i_first;
+  const int64_t p_last = pl.P + i_last;
+  const int64_t lo = p_first - a.W + 1 > 0 ? p_first - a.W + 1 : 0;
+  const int64_t nkeys = p_last - lo + 1;
+  const int64_t per = ((nkeys + a.nsplit - 1) / a.nsplit + BN - 1) / BN * BN;
+  const int64_t kb = lo + split * per;
+  const int64_t ke = kb + per < p_last + 1 ? kb + per : p_last + 1;
+
+  const int64_t base = pl.P - pl.Lb;
+  // (with Q8, a.k / a.v hold the new rows' codes)
+  const uint64_t ck = (uint64_t)((const char*)a.past_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * CE);
+  const uint64_t cv = (uint64_t)((const char*)a.past_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * CE);
+  const uint64_t nk = (uint64_t)((const char*)a.k + (((int64_t)b * a.S) * a.Hkv + kvh) * D * CE);
+  const uint64_t nv = (uint64_t)((const char*)a.v + (((int64_t)b * a.S) * a.Hkv + kvh) * D * CE);
+  const int64_t new_stride = (int64_t)a.Hkv * D * CE;
+
+  const bool has_cap = a.softcap > 0.0f;
+  const float cap = a.softcap;
+  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
+  constexpr bool has_bias = BIAS;
+  const int64_t bias_row = has_bias
+      ? ((((a.bias_b ? (int64_t)b : 0) * (a.bias_h ? a.Hq : 1) + (a.bias_h ? my_h : 0)) * a.S + my_i) *
+         (int64_t)a.total)
+      : 0;
+
+  // Block loads into registers, issued unconditionally (so the compiler can
+  // wait for exactly the loads it needs): chunk c of the block = key c / CPR,
+  // 16-byte part c % CPR; keys past the band's end are clamped to its last
+  // key (finite data the mask removes); chunks past the block repeat the last
+  // one and are not stored.  The attention_bias entries this lane scores in
+  // the block (keys j0 + 16 kt + 4 lg + r) come with them.
+  struct BlockRegs {
+    u32x4 k[CPT], v[CPT];
+    float bias[8];
+  };
+  // Per-lane parts of the addresses: chunk u of a block is key kc + j0,
+  // 16-byte part pc; blocks made only of cache rows (nearly all) add j0 rows
+  // to these, the rest take the two-segment select with clamping.
+  constexpr int kRowB = D * CE;
+  constexpr int kPartB = Q8 ? 16 / e : 16;  // bytes of a chunk's part of a row
+  uint64_t kc_lane[CPT], vc_lane[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
+    const uint64_t off = (uint64_t)(((int64_t)(c / CPR) - base) * kRowB + (c % CPR) * kPartB);
+    kc_lane[u] = ck + off;
+    vc_lane[u] = cv + off;
+  }
+  const uint64_t bias_lane =
+      BIAS ? (uint64_t)a.bias + (uint64_t)((bias_row + 4 * lg) * e) : 0;
+  const int64_t cache_end = pl.P < ke ? pl.P : ke;  // keys below this are cache rows
+  auto load_block = [&](int64_t j0, BlockRegs& rg) __attribute__((always_inline)) {
+    if (j0 + BN <= cache_end) {  // uniform
+      const uint64_t boff = (uint64_t)(j0 * kRowB);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        if constexpr (Q8) {
+          rg.k[u] = load_codes<DT>(kc_lane[u] + boff);
+          rg.v[u] = load_codes<DT>(vc_lane[u] + boff);
+        } else {
+          rg.k[u] = load16_global<false>(kc_lane[u] + boff);
+          rg.v[u] = load16_global<false>(vc_lane[u] + boff);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
+        const int key = c / CPR, part = c % CPR;
+        const int64_t j = min(j0 + key, ke - 1);
+        const bool in_cache = j < pl.P;
+        const uint64_t msk = 0ull - (uint64_t)in_cache;
+        const uint64_t off_c = (uint64_t)((j - base) * kRowB + part * kPartB);
+        const uint64_t off_n = (uint64_t)((j - pl.P) * new_stride + part * kPartB);
+        const uint64_t ka = ((ck + off_c) & msk) | ((nk + off_n) & ~msk);
+        const uint64_t va = ((cv + off_c) & msk) | ((nv + off_n) & ~msk);
+        if constexpr (Q8) {
+          rg.k[u] = load_codes<DT>(ka);
+          rg.v[u] = load_codes<DT>(va);
+        } else {
+          rg.k[u] = load16_global<false>(ka);
+          rg.v[u] = load16_global<false>(va);
+        }
+      }
+    }
+    if constexpr (BIAS) {
+      if (j0 + BN <= ke) {  // uniform
+        // keys j0 + 16 kt + 4 lg + [0, 4): one 4-element load per tile, at
+        // element (not vector) alignment -- global memory takes unaligned
+        // vector loads on this target
+        const uint64_t bb = bias_lane + (uint64_t)(j0 * e);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) load4_elems_unaligned<DT>(bb + kt * 16 * e, &rg.bias[kt * 4]);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            rg.bias[kt * 4 + r] =
+                load_elem_global<DT>((uint64_t)a.bias +
+                                     (uint64_t)((bias_row + min(j0 + kt * 16 + 4 * lg + r, ke - 1)) * e));
+      }
+    }
+  };
+  auto store_block = [&](const BlockRegs& rg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * kThreads;
+      if constexpr (Sh::CHUNKS % kThreads != 0)
+        if (c >= Sh::CHUNKS) continue;
+      const int key = c / CPR, part = c % CPR;
+      const int d0 = part * (16 / e);
+      const u32x4 kw = Q8 ? codes_to_elems<DT>(rg.k[u]) : rg.k[u];
+      const u32x4 vw = Q8 ? codes_to_elems<DT>(rg.v[u]) : rg.v[u];
+      if constexpr (DT == kF32) {
+        float* kd = (float*)sK + key * KS + d0;
+        float* vd = (float*)sV + key * VS + d0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kd[w] = __uint_as_float(kw[w]);
+          vd[w] = __uint_as_float(vw[w]);
+        }
+      } else {
+        // K rows are 16-byte aligned: one store per chunk
+        *(u32x4*)((uint16_t*)sK + key * KS + d0) = kw;
+        // V transposed, sV[d][key ^ swz(d)]: the 16 parts of a key row land
+        // on rows 8 apart, which the swizzle spreads over the banks
+        const int kx = key ^ vt_swizzle(d0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          ((uint16_t*)sV)[(d0 + 2 * w) * VS + kx] = (uint16_t)(vw[w] & 0xFFFFu);
+          ((uint16_t*)sV)[(d0 + 2 * w + 1) * VS + kx] = (uint16_t)(vw[w] >> 16);
+        }
+      }
+    }
+  };
+
+  // visibility of key kb + jr for this lane's query, as 32-bit bounds on jr
+  const int64_t vlo = my_pos - a.W + 1 - kb;
+  const int64_t vhi = (my_pos < ke - 1 ? my_pos : ke - 1) - kb;
+  const int32_t vis_lo = my_ok ? (int32_t)(vlo < -(int64_t)0x7fffffff ? -0x7fffffff : vlo) : 1;
+  const int32_t vis_hi = my_ok ? (int32_t)vhi : 0;
+
+  float m_run = -INFINITY;  // log2 units, per query (same in all 4 lane groups)
+  float l_run = 0.0f;       // this lane's share of the sum
+  f4 o[DT16];               // O^T tiles: d = 16 dt + 4 lg + r, query lq
+#pragma unroll
+  for (int t = 0; t < DT16; ++t) o[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nblocks = ke > kb ? (int)((ke - kb + BN - 1) / BN) : 0;
+  const float qk_scale = Q8 ? a.scale * a.k_scale : a.scale;
+  // One block: scores, online softmax, PV, from the block staged in LDS.
+  auto compute_block = [&](int blk, const float* bias_blk) __attribute__((always_inline)) {
+    // S^T for the two 16-key tiles of the block
+    f4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (DT == kF32) {
+        const float* kr = (const float*)sK + (kt * 16 + lq) * KS + lg;
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[4 * s], qf[s], acc, 0, 0, 0);
+      } else {
+        const uint16_t* kr = (const uint16_t*)sK + (kt * 16 + lq) * KS + 4 * lg;
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+          const uint2 kv = *(const uint2*)(kr + 16 * s);
+          if constexpr (DT == kF16) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(h4, make_uint2(kv.x, kv.y)),
+                __builtin_bit_cast(h4, make_uint2(qh[s][0], qh[s][1])), acc, 0, 0, 0);
+          } else {
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s4, make_uint2(kv.x, kv.y)),
+                __builtin_bit_cast(s4, make_uint2(qh[s][0], qh[s][1])), acc, 0, 0, 0);
+          }
+        }
+      }
+      sc[kt] = acc;
+    }
+
+    // Scores: key j = j0 + 16 kt + 4 lg + r, query lq.
+    float smax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t jr = blk * BN + kt * 16 + 4 * lg + r;
+        const bool vis = jr >= vis_lo && jr <= vis_hi;
+        float x = sc[kt][r] * qk_scale;
+        if (has_cap) {
+          const float y = x * inv_cap;
+          if constexpr (DT == kF32) {
+            x = cap * tanhf(y);
+          } else {
+            const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(
+                                       __builtin_amdgcn_exp2f(2.0f * kLog2e * fabsf(y)) + 1.0f);
+            x = cap * copysignf(t, y);
+          }
+        }
+        if (has_bias) x += bias_blk[kt * 4 + r];
+        x = vis ? x * kLog2e : -INFINITY;
+        sc[kt][r] = x;
+        smax = fmaxf(smax, x);
+      }
+    smax = fmaxf(smax, __shfl_xor(smax, 16, kWave));
+    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+    const float m_new = fmaxf(m_run, smax);
+    const float corr = (m_run == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.0f;
+    uint32_t p16[2][2] = {{0u, 0u}, {0u, 0u}};  // fp16: P as the PV operand, packed
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = (sc[kt][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sc[kt][r] - m_new);
+        if constexpr (DT == kF16) {
+          // the normaliser sums P as rounded for the product
+          const uint32_t h = f32_to_f16_bits(p);
+          p16[kt][r / 2] |= h << (16 * (r % 2));
+          p = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+        }
+        sc[kt][r] = p;
+        psum += p;
+      }
+    l_run = l_run * corr + psum;
+    // rescale only when some query's maximum moved: after the first blocks
+    // the maxima settle and this is skipped
+    if (__any(corr != 1.0f)) {
+#pragma unroll
+      for (int t = 0; t < DT16; ++t) o[t] *= corr;
+    }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if constexpr (DT == kF32) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const float* vr = (const float*)sV + (kt * 16 + 4 * lg + t4) * VS + lq;
+#pragma unroll
+          for (int dt = 0; dt < DT16; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * dt], sc[kt][t4], o[dt], 0, 0, 0);
+        }
+      } else {
+        uint32_t pw[2], pl2[2];
+        if constexpr (DT == kF16) {
+          pw[0] = p16[kt][0];
+          pw[1] = p16[kt][1];
+        } else {
+          // bf16 keeps 8 significant bits, too few for P: P = hi + lo, both
+          // bf16, and two products (relative error ~2^-17)
+          uint16_t hi[4], lo[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            hi[r] = f32_to_bf16(sc[kt][r]);
+            lo[r] = f32_to_bf16(sc[kt][r] - __uint_as_float((uint32_t)hi[r] << 16));
+          }
+          pw[0] = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+          pw[1] = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+          pl2[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+          pl2[1] = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) {
+          const uint2 vv = *(const uint2*)((const uint16_t*)sV + (16 * dt + lq) * VS +
+                                           ((kt * 16 + 4 * lg) ^ vt_swizzle(16 * dt + lq)));
+          if constexpr (DT == kF16) {
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(h4, vv), __builtin_bit_cast(h4, make_uint2(pw[0], pw[1])), o[dt],
+                0, 0, 0);
+          } else {
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s4, vv), __builtin_bit_cast(s4, make_uint2(pw[0], pw[1])), o[dt],
+                0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s4, vv), __builtin_bit_cast(s4, make_uint2(pl2[0], pl2[1])), o[dt],
+                0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  // A block's K/V/bias loads are issued three blocks ahead (register ring of
+  // three), so two blocks of loads stay in flight while one is computed;
+  // blocks past the band's end reload its last block.
+  auto block_start = [&](int blk) { return kb + (int64_t)min(blk, nblocks - 1) * BN; };
+  auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
+    __syncthreads();  // the previous block's LDS reads are done
+    store_block(rg);
+    float bias_blk[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) bias_blk[r] = has_bias ? rg.bias[r] : 0.0f;
+    __syncthreads();
+    load_block(block_start(blk + 3), rg);
+    compute_block(blk, bias_blk);
+  };
+  if (nblocks > 0) {
+    BlockRegs r0, r1, r2;
+    load_block(block_start(0), r0);
+    load_block(block_start(1), r1);
+    load_block(block_start(2), r2);
+    for (int blk = 0; blk < nblocks;) {
+      step(blk, r0);
+      if (++blk >= nblocks) break;
+      step(blk, r1);
+      if (++blk >= nblocks) break;
+      step(blk, r2);
+      ++blk;
+    }
+  }
+
+  // Sum of P over the four lane groups; write O (or the split partial).
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (my_ok) {
+    const int64_t row = ((int64_t)b * a.S + my_i) * a.Hq + my_h;
+    if (a.nsplit == 1) {
+      float m_fin = m_run;
+      const float inv = fold_sink<DT>(a.sink, a.smooth, my_h, m_fin, l_run) / l_run *
+                        (Q8 ? a.v_scale : 1.0f);
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt) {
+        const int d0 = 16 * dt + 4 * lg;
+        if constexpr (DT == kF32) {
+          *(f4*)((float*)a.out + row * D + d0) = o[dt] * inv;
+        } else {
+          uint32_t w0, w1;
+          if constexpr (DT == kF16) {
+            w0 = (uint32_t)f32_to_f16_bits(o[dt][0] * inv) | ((uint32_t)f32_to_f16_bits(o[dt][1] * inv) << 16);
+            w1 = (uint32_t)f32_to_f16_bits(o[dt][2] * inv) | ((uint32_t)f32_to_f16_bits(o[dt][3] * inv) << 16);
+          } else {
+            w0 = (uint32_t)f32_to_bf16(o[dt][0] * inv) | ((uint32_t)f32_to_bf16(o[dt][1] * inv) << 16);
+            w1 = (uint32_t)f32_to_bf16(o[dt][2] * inv) | ((uint32_t)f32_to_bf16(o[dt][3] * inv) << 16);
+          }
+          *(uint2*)((uint16_t*)a.out + row * D + d0) = make_uint2(w0, w1);
+        }
+      }
+    } else {
+      float* op = a.opart + (row * a.nsplit + split) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt)
+        *(f4*)(op + 16 * dt + 4 * lg) = Q8 ? o[dt] * a.v_scale : o[dt];
+      if (lg == 0) {
+        a.ml[(row * a.nsplit + split) * 2 + 0] = m_run;
+        a.ml[(row * a.nsplit + split) * 2 + 1] = l_run;
+      }
+    }
+  }
+  // Appends on drifting steps with a shared buffer: rows [Lb, Lb + S) lie
+  // beyond every cache row attention reads, so they are written last.
+  if (a.present_k && pl.shift == 0 && tile == 0 && split == 0) {
+    char* pk = (char*)a.present_k + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * CE;
+    char* pv = (char*)a.present_v + ((int64_t)(b * a.Hkv + kvh) * a.C) * D * CE;
+    for (int idx = tid; idx < a.S * CPRC; idx += kThreads) {
+      const int i = idx / CPRC, w = idx % CPRC;
+      const int64_t src = ((int64_t)(b * a.S + i) * a.Hkv + kvh) * D * CE + w * 16;
+      const int64_t dst = (pl.Lb + i) * (int64_t)D * CE + w * 16;
+      *(u32x4*)(pk + dst) = *(const u32x4*)((const char*)a.k + src);
+      *(u32x4*)(pv + dst) = *(const u32x4*)((const char*)a.v + src);
+    }
+  }
+
+  slice_tail_rows(a, pl, b, kvh, D, CE, nullptr, nullptr);
+}
+
+template <int DT, int D, int NW, bool Q8>
+hipError_t launch_w(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
+  if (a.bias)
+    attn_chunk_kernel<DT, D, true, NW, Q8><<<grid, NW * kWave, 0, st>>>(a);
+  else
+    attn_chunk_kernel<DT, D, false, NW, Q8><<<grid, NW * kWave, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int DT, int D, bool Q8>
+hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
+  if constexpr (ChunkShape<DT, D, 4>::ok) {
+    return a.waves == 8 ? launch_w<DT, D, 8, Q8>(a, st) : launch_w<DT, D, 4, Q8>(a, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int DT, bool Q8>
+hipError_t launch_t(int D, const AttnArgs& a, hipStream_t st) {
+  switch (D) {
+    case 16: return launch_d<DT, 16, Q8>(a, st);
+    case 32: return launch_d<DT, 32, Q8>(a, st);
+    case 64: return launch_d<DT, 64, Q8>(a, st);
+    case 128: return launch_d<DT, 128, Q8>(a, st);
+    case 256: return launch_d<DT, 256, Q8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+}  // namespace swgqa

@@ -29,6 +29,24 @@ __global__ void plan_kernel(const int32_t* seqlens, int32_t B, int32_t S,
   o[7] = pl.kept < need ? 1 : 0;
 }
 
+// int8 codes of the step's new key and value rows (four elements a thread
+// and pass), for the chunk kernel over an int8 cache.
+template <int DT>
+__global__ void quant_rows_kernel(const void* k, const void* v, uint32_t* kq, uint32_t* vq,
+                                  size_t nwords, float ks, float vs) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords;
+       i += (size_t)gridDim.x * blockDim.x) {
+    uint32_t ck = 0u, cv = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ck |= quant_code(load_one<DT>(k, (int64_t)(4 * i + j)), ks) << (8 * j);
+      cv |= quant_code(load_one<DT>(v, (int64_t)(4 * i + j)), vs) << (8 * j);
+    }
+    kq[i] = ck;
+    vq[i] = cv;
+  }
+}
+
 __global__ void zero_words_kernel(uint32_t* words, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -42,6 +60,30 @@ hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
   const int threads = 64;
   plan_kernel<<<(B + threads - 1) / threads, threads, 0, st>>>(
       seqlens, B, S, C, W, make_gap_div((uint32_t)(C - W + 1)), total, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(int dtype, const void* k, const void* v, uint8_t* kq, uint8_t* vq,
+                             size_t n, float k_scale, float v_scale, hipStream_t st) {
+  const size_t nwords = n / 4;
+  if (nwords == 0) return hipSuccess;
+  size_t blocks = (nwords + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  switch (dtype) {
+    case kF32:
+      quant_rows_kernel<kF32><<<(unsigned)blocks, 256, 0, st>>>(k, v, (uint32_t*)kq, (uint32_t*)vq,
+                                                               nwords, k_scale, v_scale);
+      break;
+    case kF16:
+      quant_rows_kernel<kF16><<<(unsigned)blocks, 256, 0, st>>>(k, v, (uint32_t*)kq, (uint32_t*)vq,
+                                                               nwords, k_scale, v_scale);
+      break;
+    case kBF16:
+      quant_rows_kernel<kBF16><<<(unsigned)blocks, 256, 0, st>>>(k, v, (uint32_t*)kq, (uint32_t*)vq,
+                                                                nwords, k_scale, v_scale);
+      break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -99,6 +99,12 @@ bool chunk_kernel_supports(int dtype, int D);
 int chunk_rows_per_workgroup(int waves);  // 4 or 8 waves
 int chunk_keys_per_block();
 hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t stream);
+// The same kernel over an int8 cache (swgqa_attn_chunk_q8.hip); a.k / a.v
+// hold the step's new rows as codes (launch_quant_rows).
+hipError_t launch_attn_chunk_q8(int dtype, int D, const AttnArgs& a, hipStream_t stream);
+// int8 codes of n elements of k and v (element type dtype), n % 4 == 0.
+hipError_t launch_quant_rows(int dtype, const void* k, const void* v, uint8_t* kq, uint8_t* vq,
+                             size_t n, float k_scale, float v_scale, hipStream_t stream);
 // Staged decode kernel (swgqa_attn_decode.hip): supports row sizes up to
 // 256 bytes and NQ * (16 / element bytes) <= 64.
 bool decode_kernel_supports(int dtype, int D, int nq);

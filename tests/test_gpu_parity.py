@@ -490,7 +490,7 @@ def test_int8_cache_random_steps(cfg, mode):
     run = Lockstep(cfg, mode=mode)
     T = 0
     for _ in range(16):
-        S = int(rng.choice([1, 1, 1, 2, 3, 5, 8, 15]))
+        S = int(rng.choice([1, 1, 1, 2, 3, 5, 8, 15, 16, 33, int(rng.integers(1, 2 * cfg.C + 2))]))
         run.step([T] * cfg.B, S)
         T += S
     say(f"  worst scaled error {run.worst:.3g}")
@@ -526,6 +526,35 @@ def test_int8_cache_ragged_bias_and_key_splits():
     say(f"  worst scaled error {run.worst:.3g}")
 
 
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+def test_int8_cache_multi_token_steps(mode):
+    """Steps of 16 or more tokens over an int8 cache take the matrix-core
+    kernel on codes: a staged prefill (S > C), chunks with a bias, verify
+    steps, then a long window over few slices (key splits)."""
+    cfg = Cfg(B=3, Hq=8, Hkv=2, D=64, C=110, W=100, seed=71, dtype=synth.BF16, kv_int8=True,
+              softcap=20.0)
+    syn = cfg.synth()
+    vers = Versions(3)
+    run = Lockstep(cfg, mode=mode, vers=vers)
+    P = np.zeros(3, np.int64)
+    for S, with_bias in [(150, False), (32, True), (17, False), (8, True), (48, True), (1, False)]:
+        total = int((P + S).max())
+        bias = _bias_nan_outside(cfg, syn, P, S, total) if with_bias else None
+        run.step(P, S, bias=bias, total=total)
+        P = P + S
+    long = Cfg(B=1, Hq=4, Hkv=1, D=128, C=1600, W=1500, seed=72, dtype=synth.F16, kv_int8=True)
+    syn = long.synth()
+    vers = Versions(1)
+    P0 = np.array([1700])
+    K, V = seeded_cache(long, syn, P0, vers)
+    run = Lockstep(long, mode=mode, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S in [64, 1, 40]:
+        run.step(P, S)
+        P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
 def test_int8_cache_ties_and_saturation():
     """New elements on exact ties of x / scale and far outside the code
     range: the GPU stores the oracle's codes (ties to even, saturation)."""
@@ -553,8 +582,6 @@ def test_int8_cache_host_errors():
                              None, t, t, t, ws) == sw.ERR_ARG
     assert sw.forward_status(mk(kv_cache_type=2, k_scale=1.0, v_scale=1.0), t, t, t, t, t, seq,
                              None, t, t, t, ws) == sw.ERR_UNSUPPORTED
-    p16 = sw.make_params(1, 16, 2, 2, 64, 32, 4, 16, kv_cache_type=1, k_scale=1.0, v_scale=1.0)
-    assert sw.forward_status(p16, t, t, t, t, t, seq, None, t, t, t, ws) == sw.ERR_UNSUPPORTED
     p8 = sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, kv_cache_type=1, k_scale=1.0, v_scale=1.0)
     assert sw.forward_status(p8, t, t, t, t, t, seq, None, t, t, t, ws) == sw.ERR_UNSUPPORTED
     torch.cuda.synchronize()
