@@ -84,6 +84,10 @@ def lib():
         L.swgqa_oracle_decode.argtypes = [i32, ctypes.c_uint32]
         L.swgqa_oracle_encode.restype = ctypes.c_uint32
         L.swgqa_oracle_encode.argtypes = [i32, ctypes.c_double]
+        L.swgqa_oracle_quantize_e4m3.restype = ctypes.c_uint32
+        L.swgqa_oracle_quantize_e4m3.argtypes = [ctypes.c_double, ctypes.c_float]
+        L.swgqa_oracle_decode_e4m3.restype = ctypes.c_double
+        L.swgqa_oracle_decode_e4m3.argtypes = [ctypes.c_uint32]
         L.swgqa_oracle_set_threads.restype = ctypes.c_int
         L.swgqa_oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -158,6 +162,14 @@ def forward_compact_first(p: Params, query, key, value, cache_key, cache_value,
         ctypes.byref(p), _ptr(query), _ptr(key), _ptr(value), _ptr(cache_key),
         _ptr(cache_value), _ptr(seqlens_k), _ptr(bias), _ptr(head_sink), _ptr(output))
     return st, output
+
+
+def quantize_e4m3(x: float, scale: float) -> int:
+    return lib().swgqa_oracle_quantize_e4m3(x, scale)
+
+
+def decode_e4m3(code: int) -> float:
+    return lib().swgqa_oracle_decode_e4m3(code)
 
 
 def decode(dtype: int, bits: int) -> float:

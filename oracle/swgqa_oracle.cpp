@@ -58,7 +58,11 @@
 //    x (after rotary) is stored as the code nearest to x / scale -- the
 //    quotient rounded to binary32, then to an integer with ties to even,
 //    then saturated to [-128, 127] -- and every key and value row the step
-//    attends to, the new ones included, is read in that dequantized form.
+//    attends to, the new ones included, is read in that dequantized form;
+//    with kv_cache_type = 2 the codes are fp8 E4M3 (OCP "FN": bias 7, no
+//    infinities, 0x7F / 0xFF NaN, largest finite 448): the quotient rounded to
+//    the nearest E4M3 value, ties to the even code, magnitudes of 448 or more
+//    saturated to 448, NaN to 0x7F.
 
 #include "swgqa_oracle.h"
 
@@ -195,7 +199,7 @@ void store(int32_t dt, void* base, size_t idx, double x) {
 
 // Bytes of one cache element: the element type, or one int8 code.
 size_t cache_elem_bytes(const swgqa_oracle_params* p) {
-  return p->kv_cache_type == 1 ? 1 : elem_bytes(p->dtype);
+  return p->kv_cache_type != 0 ? 1 : elem_bytes(p->dtype);
 }
 
 // The int8 code of x for a quantization scale (binary32 quotient, ties to
@@ -207,12 +211,45 @@ int8_t quantize_int8(double x, float scale) {
   return (int8_t)t;
 }
 
-// Element idx of a cache row buffer (element type, or dequantized int8 code).
+// Value of an fp8 E4M3 ("FN") code: sign, 4 exponent bits (bias 7), 3
+// mantissa bits; exponent 0 is subnormal (m * 2^-9); 0x7F / 0xFF are NaN.
+double decode_e4m3(uint8_t c) {
+  if ((c & 0x7F) == 0x7F) return NAN;
+  const int e = (c >> 3) & 15, m = c & 7;
+  const double mag = e == 0 ? std::ldexp((double)m, -9) : std::ldexp(8.0 + m, e - 10);
+  return (c & 0x80) ? -mag : mag;
+}
+
+// The fp8 E4M3 code of x for a quantization scale: the binary32 quotient
+// rounded to the nearest finite code value by search over all codes (ties to
+// the even code), saturated at 448, NaN to 0x7F.
+uint8_t quantize_e4m3(double x, float scale) {
+  const float t = (float)x / scale;
+  if (t != t) return 0x7F;
+  const double a = std::fabs((double)t);
+  uint8_t best = 0;
+  if (a >= 448.0) {
+    best = 0x7E;
+  } else {
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+      const double d = std::fabs(decode_e4m3((uint8_t)c) - a);
+      if (d < bd || (d == bd && (c & 1) == 0)) {
+        bd = d;
+        best = (uint8_t)c;
+      }
+    }
+  }
+  return (uint8_t)(best | (t < 0.0f && best != 0 ? 0x80 : 0));
+}
+
+// Element idx of a cache row buffer (element type, or a dequantized code).
 double load_cache(const swgqa_oracle_params* p, const void* base, size_t idx, float scale) {
-  if (p->kv_cache_type != 1) return load(p->dtype, base, idx);
-  int8_t c;
+  if (p->kv_cache_type == 0) return load(p->dtype, base, idx);
+  uint8_t c;
   std::memcpy(&c, (const char*)base + idx, 1);
-  return (double)c * (double)scale;  // exact in fp64
+  if (p->kv_cache_type == 2) return decode_e4m3(c) * (double)scale;  // exact in fp64
+  return (double)(int8_t)c * (double)scale;
 }
 
 // ---------------------------------------------------------------------------
@@ -230,8 +267,8 @@ int validate(const swgqa_oracle_params* p) {
   if (p->smooth_softmax != 0 && p->smooth_softmax != 1) return 1;
   if (p->do_rotary != 0 && p->do_rotary != 1) return 1;
   if (p->do_rotary && (p->head_size % 2 != 0 || p->rotary_cache_rows < 1)) return 1;
-  if (p->kv_cache_type != 0 && p->kv_cache_type != 1) return 2;
-  if (p->kv_cache_type == 1 &&
+  if (p->kv_cache_type < 0 || p->kv_cache_type > 2) return 2;
+  if (p->kv_cache_type != 0 &&
       !(p->k_scale > 0.0f && p->v_scale > 0.0f && std::isfinite(p->k_scale) &&
         std::isfinite(p->v_scale)))
     return 1;
@@ -475,6 +512,13 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
             std::memcpy(dk + d, &qk, 1);
             std::memcpy(dv + d, &qv, 1);
           }
+        } else if (p->kv_cache_type == 2) {
+          for (int64_t d = 0; d < D; ++d) {
+            const uint8_t qk = quantize_e4m3(load(p->dtype, key, src + d), p->k_scale);
+            const uint8_t qv = quantize_e4m3(load(p->dtype, value, src + d), p->v_scale);
+            std::memcpy(dk + d, &qk, 1);
+            std::memcpy(dv + d, &qv, 1);
+          }
         } else {
           std::memcpy(dk, (const char*)key + src * e, row);
           std::memcpy(dv, (const char*)value + src * e, row);
@@ -616,6 +660,10 @@ int swgqa_oracle_forward_compact_first(const swgqa_oracle_params* p,
   }
   return status;
 }
+
+uint32_t swgqa_oracle_quantize_e4m3(double x, float scale) { return quantize_e4m3(x, scale); }
+
+double swgqa_oracle_decode_e4m3(uint32_t code) { return decode_e4m3((uint8_t)code); }
 
 double swgqa_oracle_decode(int32_t dtype, uint32_t bits) {
   if (dtype == 0) {

@@ -61,7 +61,7 @@ typedef struct {
   int32_t do_rotary;             /* 0/1: rotary embedding of query and new keys */
   int32_t rotary_interleaved;    /* 0: pairs (k, k + D/2); 1: pairs (2k, 2k + 1) */
   int32_t rotary_cache_rows;     /* rows of cos_cache / sin_cache */
-  int32_t kv_cache_type;         /* 0: caches in the element type; 1: int8 codes */
+  int32_t kv_cache_type;         /* 0: caches in the element type; 1: int8 codes; 2: fp8 E4M3 codes */
   float k_scale;                 /* with kv_cache_type 1: key cache element = code * k_scale */
   float v_scale;                 /* with kv_cache_type 1: value cache element = code * v_scale */
 } swgqa_oracle_params;
@@ -113,6 +113,11 @@ int swgqa_oracle_forward_compact_first(const swgqa_oracle_params* p,
                                        const int32_t* seqlens_k,
                                        const void* attention_bias,
                                        const void* head_sink, void* output);
+
+/* fp8 E4M3 code of x / scale (binary32 quotient, nearest, ties to even,
+ * saturated at 448, NaN -> 0x7F) and the value of a code, for the pins. */
+uint32_t swgqa_oracle_quantize_e4m3(double x, float scale);
+double swgqa_oracle_decode_e4m3(uint32_t code);
 
 /* Element conversions the oracle uses, exported so that tests can pin them
  * against independent routines.  dtype as above; bits in the low 16/32 bits. */

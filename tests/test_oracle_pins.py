@@ -957,5 +957,101 @@ def test_p14_argument_checks():
     K8 = np.zeros((1, 1, 4, 8), np.int8)
     assert _q_forward(cfg, 1, q, k, k, K8, K8, [0], 0.0, 1.0)[0] == 1
     assert _q_forward(cfg, 1, q, k, k, K8, K8, [0], 1.0, float("inf"))[0] == 1
-    p = oracle.make_params(1, 1, 2, 1, 8, 4, 4, 1, kv_cache_type=2, k_scale=1.0, v_scale=1.0)
+    p = oracle.make_params(1, 1, 2, 1, 8, 4, 4, 1, kv_cache_type=3, k_scale=1.0, v_scale=1.0)
     assert oracle.forward(p, q, k, k, K8.copy(), K8.copy(), np.zeros(1, np.int32))[0] == 2
+
+
+# ---------------------------------------------------------------------------
+# P15. fp8 E4M3 cache codes (kv_cache_type 2; the same reading as P14 with
+# OCP E4M3 "FN" codes: nearest value, ties to the even code, magnitudes of 448
+# or more saturated to 448, NaN to 0x7F, results of zero coded +0).
+def test_p15_e4m3_values_equal_torch_float8():
+    """Every one of the 256 codes decodes to torch's float8_e4m3fn value (an
+    independent implementation of the OCP format), and the printed facts of
+    the format hold: 448 largest, 2^-6 smallest normal, 2^-9 smallest
+    subnormal, 0x7F / 0xFF NaN."""
+    torch = pytest.importorskip("torch")
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = np.array([oracle.decode_e4m3(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)])
+    assert oracle.decode_e4m3(0x7E) == 448.0 and oracle.decode_e4m3(0x08) == 2.0 ** -6
+    assert oracle.decode_e4m3(0x01) == 2.0 ** -9 and np.isnan(oracle.decode_e4m3(0x7F))
+    assert np.isnan(ours).sum() == 2
+
+
+def test_p15_e4m3_rounding_against_torch():
+    """Inside the range the code equals torch's float8 cast (nearest, ties to
+    even) for random values, all midpoints between neighbouring codes and
+    the codes themselves; saturation and +0 for results of zero are the
+    reading's own (torch gives NaN and -0 there)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(151)
+    vals = np.concatenate([
+        rng.normal(0, 30, 3000), rng.normal(0, 0.01, 1000),
+        np.exp(rng.uniform(-12, 6, 1000)) * rng.choice([-1, 1], 1000)])
+    table = np.array([oracle.decode_e4m3(c) for c in range(0x7F)])      # 0 .. 448
+    mids = (table[1:] + table[:-1]) / 2
+    vals = np.concatenate([vals, table, mids, -mids]).astype(np.float32)
+    vals = vals[np.abs(vals) < 448]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(int)
+    ours = np.array([oracle.quantize_e4m3(float(v), 1.0) for v in vals])
+    ref = np.where(ref == 0x80, 0, ref)                                   # -0 -> +0
+    assert np.array_equal(ours, ref)
+    assert oracle.quantize_e4m3(1000.0, 1.0) == 0x7E and oracle.quantize_e4m3(-1e30, 1.0) == 0xFE
+    assert oracle.quantize_e4m3(float("nan"), 1.0) == 0x7F
+    assert oracle.quantize_e4m3(-2.0 ** -11, 1.0) == 0
+
+
+def test_p15_fp8_grid_values_equal_the_plain_cache():
+    """New elements that are E4M3 values times the scale: the stored codes
+    decode to them and the outputs equal the plain cache's bit for bit."""
+    cfg = Cfg(B=2, Hq=4, Hkv=2, D=8, C=10, W=6, dtype=synth.F32, seed=152)
+    rng = np.random.default_rng(152)
+    ks, vs = 2.0 ** -4, 2.0 ** -3
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    vals = np.array([oracle.decode_e4m3(int(c)) for c in finite])
+    syn = cfg.synth()
+    K8 = np.zeros((2, cfg.Hkv, cfg.C, cfg.D), np.uint8)
+    V8 = np.zeros_like(K8)
+    Kp = scenario_nan((2, cfg.Hkv, cfg.C, cfg.D), cfg.dtype)
+    Vp = scenario_nan((2, cfg.Hkv, cfg.C, cfg.D), cfg.dtype)
+    T = np.zeros(2, np.int64)
+    for S in [7, 1, 3, 1, 12, 1]:
+        q, _, _ = syn.step_inputs(T, S)
+        k = (rng.choice(vals, size=(2, S, cfg.Hkv * cfg.D)) * ks).astype(np.float32)
+        v = (rng.choice(vals, size=(2, S, cfg.Hkv * cfg.D)) * vs).astype(np.float32)
+        seq = (T + S - 1).astype(np.int32)
+        p8 = oracle.make_params(2, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, int(seq.max()) + 1,
+                                cfg.dtype, kv_cache_type=2, k_scale=ks, v_scale=vs)
+        st, out, _ = oracle.forward(p8, q, k, v, K8, V8, seq)
+        p = oracle.make_params(2, S, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, int(seq.max()) + 1, cfg.dtype)
+        st0, out0, plan = oracle.forward(p, q, k, v, Kp, Vp, seq)
+        assert st == 0 and st0 == 0
+        assert np.array_equal(out.view(np.uint8), out0.view(np.uint8))
+        dec = np.vectorize(oracle.decode_e4m3)
+        for b in range(2):
+            La = int(plan[b, 3])
+            assert np.array_equal(dec(K8[b, :, :La]) * ks, Kp[b, :, :La].astype(np.float64))
+            assert np.array_equal(dec(V8[b, :, :La]) * vs, Vp[b, :, :La].astype(np.float64))
+        T = T + S
+
+
+def test_p15_fp8_relative_error_and_saturation():
+    """Normal-range elements come back within 2^-4 relative (half a step of
+    the 3-bit mantissa); far values saturate to +-448 * scale."""
+    cfg = Cfg(B=1, Hq=2, Hkv=2, D=32, C=40, W=40, seed=153)
+    syn = cfg.synth()
+    q, k, v = syn.step_inputs(np.array([0]), 30)
+    k[0, 0, :4] = [1e6, -1e6, 5e3, -5e3]
+    p = oracle.make_params(1, 30, 2, 2, 32, 40, 40, 30, kv_cache_type=2, k_scale=0.01, v_scale=0.02)
+    K8 = np.zeros((1, 2, 40, 32), np.uint8)
+    V8 = np.zeros_like(K8)
+    st, _, _ = oracle.forward(p, q, k, v, K8, V8, np.array([29], np.int32))
+    assert st == 0
+    assert list(K8[0, 0, 0, :4]) == [0x7E, 0xFE, 0x7E, 0xFE]
+    dec = np.vectorize(oracle.decode_e4m3)
+    vv = v.reshape(30, 2, 32).transpose(1, 0, 2).astype(np.float64)
+    got = dec(V8[0, :, :30]) * 0.02
+    normal = np.abs(vv) >= 2.0 ** -6 * 0.02
+    assert np.all(np.abs(got - vv)[normal] <= 2.0 ** -4 * np.abs(vv)[normal] * (1 + 1e-9))
