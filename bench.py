@@ -40,7 +40,8 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published
 # slice for the batched serving decode)
 HEADLINE_KERNEL = "attn_decode_kernel<0, 64, 2, 4, 3, false>"
 SERVING_KERNEL = "attn_decode_kernel<2, 128, 4, 8, 3, false>"
-SERVING_INT8_KERNEL = "attn_decode_q8_kernel<2, 128, 4, 8>"
+SERVING_INT8_KERNEL = "attn_decode_q8_kernel<2, 128, 4, 8, 1>"
+SERVING_FP8_KERNEL = "attn_decode_q8_kernel<2, 128, 4, 8, 2>"
 
 
 def log(*a):
@@ -50,15 +51,18 @@ def log(*a):
 # ---------------------------------------------------------------------------
 class Workload:
     def __init__(self, name, B, Hq, Hkv, D, C, W, dtype, scale=0.0, softcap=0.0, seed=0,
-                 kv_int8=False, k_scale=0.0, v_scale=0.0):
+                 kv_int8=False, k_scale=0.0, v_scale=0.0, kv_fp8=False):
         self.name, self.B, self.Hq, self.Hkv, self.D = name, B, Hq, Hkv, D
         self.C, self.W, self.dtype, self.scale, self.softcap, self.seed = C, W, dtype, scale, softcap, seed
         self.e = 4 if dtype == 0 else 2
-        self.kv_int8, self.k_scale, self.v_scale = kv_int8, k_scale, v_scale
-        self.ce = 1 if kv_int8 else self.e  # cache element bytes
+        self.kv_int8, self.kv_fp8, self.k_scale, self.v_scale = kv_int8, kv_fp8, k_scale, v_scale
+        self.ce = 1 if (kv_int8 or kv_fp8) else self.e  # cache element bytes
 
     def cache_params(self) -> dict:
-        return dict(kv_cache_type=1, k_scale=self.k_scale, v_scale=self.v_scale) if self.kv_int8 else {}
+        if not (self.kv_int8 or self.kv_fp8):
+            return {}
+        return dict(kv_cache_type=2 if self.kv_fp8 else 1, k_scale=self.k_scale,
+                    v_scale=self.v_scale)
 
     def step_bytes(self, T: np.ndarray, S: int, sw, bias: bool = False) -> dict:
         """Algorithmic HBM bytes of one step for items with lengths T (after
@@ -245,11 +249,21 @@ def seeded_cache(torch, sw, wl: Workload, P0: np.ndarray):
     on the length, so this equals the state a prefill + decodes would leave."""
     import synth
     shape = (wl.B, wl.Hkv, wl.C, wl.D)
-    if wl.kv_int8:  # seeded codes, uniform in [-100, 100]
+    if wl.kv_int8 or wl.kv_fp8:
+        # seeded codes: int8 uniform in [-100, 100]; fp8 E4M3 with random sign,
+        # exponent field 0..9 and mantissa (finite values up to 7.5)
         g = torch.Generator(device="cuda:0")
         g.manual_seed(wl.seed)
-        K = torch.randint(-100, 101, shape, dtype=torch.int8, device="cuda:0", generator=g)
-        V = torch.randint(-100, 101, shape, dtype=torch.int8, device="cuda:0", generator=g)
+        if wl.kv_int8:
+            K = torch.randint(-100, 101, shape, dtype=torch.int8, device="cuda:0", generator=g)
+            V = torch.randint(-100, 101, shape, dtype=torch.int8, device="cuda:0", generator=g)
+        else:
+            def codes():
+                c = (torch.randint(0, 2, shape, device="cuda:0", generator=g) << 7) | \
+                    (torch.randint(0, 10, shape, device="cuda:0", generator=g) << 3) | \
+                    torch.randint(0, 8, shape, device="cuda:0", generator=g)
+                return c.to(torch.uint8).view(torch.int8)
+            K, V = codes(), codes()
         return K, V
     syn = synth.Synth(wl.seed, wl.Hq, wl.Hkv, wl.D, wl.dtype)
     st = storage_torch_dtype(torch, wl.dtype)
@@ -448,11 +462,13 @@ def small_slack(torch, sw):
     return out
 
 
-def serving_int8(torch, sw, no_graph: bool):
-    """The batched-serving decode with an int8 cache (per-tensor scales): the
-    same shape, half the cache bytes of bf16."""
-    srv = Workload("batched_serving_int8", B=32, Hq=32, Hkv=8, D=128, C=4608, W=4096, dtype=2,
-                   softcap=50.0, seed=1006, kv_int8=True, k_scale=0.02, v_scale=0.02)
+def serving_int8(torch, sw, no_graph: bool, fp8: bool = False):
+    """The batched-serving decode with an 8-bit cache (int8, or fp8 E4M3 with
+    fp8=True; per-tensor scales): the same shape, half the cache bytes of
+    bf16."""
+    srv = Workload("batched_serving_fp8" if fp8 else "batched_serving_int8", B=32, Hq=32, Hkv=8,
+                   D=128, C=4608, W=4096, dtype=2, softcap=50.0, seed=1006, kv_int8=not fp8,
+                   kv_fp8=fp8, k_scale=0.02, v_scale=0.02)
     rng = np.random.default_rng(1005)
     Ps = rng.integers(4096, 32769, size=32)
     K, V = seeded_cache(torch, sw, srv, Ps)
@@ -467,14 +483,15 @@ def serving_int8(torch, sw, no_graph: bool):
     kms = r["graph_kernel_ms"] if graph else float(np.mean(r["step_ms"]))
     kv = sum(b["kv_read"] for b in byts) / 128 / (kms / 1e3) / 1e9
     out = {
-        "workload": "B=32 decode, 32 Q / 8 KV heads x 128, bf16 queries, int8 cache "
+        "workload": f"B=32 decode, 32 Q / 8 KV heads x 128, bf16 queries, "
+                    f"{'fp8 E4M3' if fp8 else 'int8'} cache "
                     "(k_scale = v_scale = 0.02), W=4096, C=4608, softcap 50, past lengths "
                     "U[4096, 32768], 128 steps",
         "tokens_per_s": round(32 * 128 / wall, 1),
         "ms_per_step": round(wall / 128 * 1e3, 5),
         "mode": "hip_graph" if graph else "eager",
         "kv_read_GBps": round(kv, 1),
-        "roofline": roofline(byts, kms, SERVING_INT8_KERNEL),
+        "roofline": roofline(byts, kms, SERVING_FP8_KERNEL if fp8 else SERVING_INT8_KERNEL),
     }
     del K, V, snap, loop
     return out
@@ -686,6 +703,8 @@ def main():
     if not args.no_serving:
         log("serving decode, int8 cache ...")
         result["serving_int8"] = serving_int8(torch, sw, args.no_graph)
+        log("serving decode, fp8 cache ...")
+        result["serving_fp8"] = serving_int8(torch, sw, args.no_graph, fp8=True)
 
     if not args.no_extra:
         log("rotary decode ...")

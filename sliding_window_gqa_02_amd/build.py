@@ -15,8 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libswgqa.so")
 SOURCES = ["swgqa_api.hip", "swgqa_attn_split.hip", "swgqa_attn_decode.hip",
-           "swgqa_attn_decode_rot.hip", "swgqa_attn_decode_q8.hip",
-           "swgqa_attn_chunk.hip", "swgqa_attn_chunk_q8.hip", "swgqa_step_tail.hip", "swgqa_copy.hip",
+           "swgqa_attn_decode_rot.hip", "swgqa_attn_decode_q8.hip", "swgqa_attn_decode_f8.hip",
+           "swgqa_attn_chunk.hip", "swgqa_attn_chunk_q8.hip", "swgqa_attn_chunk_f8.hip", "swgqa_step_tail.hip", "swgqa_copy.hip",
            "swgqa_rotary.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

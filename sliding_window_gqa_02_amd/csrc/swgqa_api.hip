@@ -74,8 +74,8 @@ swgqa_status validate(const swgqa_params* p) {
   if (p->do_rotary && (p->rotary_cache_rows < 1 || p->head_size % 2 != 0)) return SWGQA_ERR_ARG;
   if (p->dtype < SWGQA_F32 || p->dtype > SWGQA_BF16) return SWGQA_ERR_UNSUPPORTED;
   if (!head_size_supported(p->head_size)) return SWGQA_ERR_UNSUPPORTED;
-  if (p->kv_cache_type != 0 && p->kv_cache_type != 1) return SWGQA_ERR_UNSUPPORTED;
-  if (p->kv_cache_type == 1) {
+  if (p->kv_cache_type < 0 || p->kv_cache_type > 2) return SWGQA_ERR_UNSUPPORTED;
+  if (p->kv_cache_type != 0) {
     if (!(p->k_scale > 0.0f && p->v_scale > 0.0f && std::isfinite(p->k_scale) &&
           std::isfinite(p->v_scale)))
       return SWGQA_ERR_ARG;
@@ -104,7 +104,7 @@ SplitPlan plan_split(const swgqa_params* p) {
   s.waves = 4;
   const bool multi_token = p->sequence_length >= kChunkMinTokens ||
                            (p->sequence_length >= 2 && per_kv >= kChunkMinRows);
-  if (p->kv_cache_type == 1 && !(p->sequence_length >= kChunkMinTokens &&
+  if (p->kv_cache_type != 0 && !(p->sequence_length >= kChunkMinTokens &&
                                  chunk_kernel_supports(p->dtype, p->head_size))) {
     // int8 cache: steps of S < 16 on the int8 staged kernel, tiles of 2 or 4
     // pairs, the same whole-slice / key-split choice as below (longer steps
@@ -220,7 +220,7 @@ struct RotaryScratch {
 
 RotaryScratch rotary_scratch(const swgqa_params* p, size_t start, const SplitPlan& s) {
   RotaryScratch r{start, start, start, start, start, start};
-  if (p->kv_cache_type == 1 && s.kind == Kind::kChunk) {
+  if (p->kv_cache_type != 0 && s.kind == Kind::kChunk) {
     const size_t n = (size_t)p->batch_size * p->sequence_length * p->kv_num_heads * p->head_size;
     r.kq_off = start;
     r.vq_off = r.kq_off + align256(n);
@@ -278,7 +278,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
       !present_key || !present_value || !workspace)
     return SWGQA_ERR_ARG;
   const size_t e = elem_bytes(p->dtype);
-  const size_t ce = p->kv_cache_type == 1 ? 1 : e;  // cache element bytes
+  const size_t ce = p->kv_cache_type != 0 ? 1 : e;  // cache element bytes
   const size_t cache_bytes =
       (size_t)p->batch_size * p->kv_num_heads * p->capacity * p->head_size * ce;
   if (ranges_partially_overlap(past_key, present_key, cache_bytes) ||
@@ -331,14 +331,15 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   }
   const bool shared = present_key == past_key && present_value == past_value;
   // int8 cache on the matrix-core kernel: the new rows as codes first
-  const bool chunk_q8 = p->kv_cache_type == 1 && s.kind == Kind::kChunk;
+  const bool chunk_q8 = p->kv_cache_type != 0 && s.kind == Kind::kChunk;
+  const int ct = p->kv_cache_type == 2 ? kCodeFp8 : kCodeInt8;  // code type, if quantized
   const void* key_rows = key;    // the new rows as the element type (rotated)
   const void* value_rows = value;
   if (chunk_q8) {
     uint8_t* kq = (uint8_t*)workspace + rs.kq_off;
     uint8_t* vq = (uint8_t*)workspace + rs.vq_off;
     const size_t n = (size_t)p->batch_size * p->sequence_length * p->kv_num_heads * p->head_size;
-    if (launch_quant_rows(p->dtype, key, value, kq, vq, n, p->k_scale, p->v_scale, st) !=
+    if (launch_quant_rows(p->dtype, ct, key, value, kq, vq, n, p->k_scale, p->v_scale, st) !=
         hipSuccess)
       return SWGQA_ERR_HIP;
     key = kq;
@@ -410,9 +411,13 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   }
 
   const hipError_t ea =
-      s.kind == Kind::kChunk    ? (chunk_q8 ? launch_attn_chunk_q8(p->dtype, p->head_size, a, st)
-                                            : launch_attn_chunk(p->dtype, p->head_size, a, st))
-      : s.kind == Kind::kDecodeQ8 ? launch_attn_decode_q8(p->dtype, p->head_size, s.nq, a, st)
+      s.kind == Kind::kChunk
+          ? (!chunk_q8          ? launch_attn_chunk(p->dtype, p->head_size, a, st)
+             : ct == kCodeFp8   ? launch_attn_chunk_f8(p->dtype, p->head_size, a, st)
+                                : launch_attn_chunk_q8(p->dtype, p->head_size, a, st))
+      : s.kind == Kind::kDecodeQ8
+          ? (ct == kCodeFp8 ? launch_attn_decode_f8(p->dtype, p->head_size, s.nq, a, st)
+                            : launch_attn_decode_q8(p->dtype, p->head_size, s.nq, a, st))
       : s.kind == Kind::kDecode
           ? (rot_fused ? launch_attn_decode_rot(p->dtype, p->head_size, s.nq, a, st)
                        : launch_attn_decode(p->dtype, p->head_size, s.nq, a, st))
@@ -441,7 +446,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   c.gdiv = a.gdiv;
   c.D = p->head_size;
   c.elem_bytes = (int32_t)ce;
-  c.quant = p->kv_cache_type == 1 ? 1 : 0;
+  c.quant = p->kv_cache_type != 0 ? ct : 0;
   c.src_elem_bytes = (int32_t)e;
   c.dtype = p->dtype;
   c.k_scale = p->k_scale;

@@ -15,9 +15,9 @@ int chunk_keys_per_block() { return BN; }
 
 hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t st) {
   switch (dtype) {
-    case kF32: return launch_t<kF32, false>(D, a, st);
-    case kF16: return launch_t<kF16, false>(D, a, st);
-    case kBF16: return launch_t<kBF16, false>(D, a, st);
+    case kF32: return launch_t<kF32, 0>(D, a, st);
+    case kF16: return launch_t<kF16, 0>(D, a, st);
+    case kBF16: return launch_t<kBF16, 0>(D, a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -110,31 +110,38 @@ __device__ __forceinline__ u32x4 load_codes(uint64_t addr) {
   return r;
 }
 
-// Codes (low words of c) as the element type, one 16-byte chunk: exact.
-template <int DT>
+// Codes (low words of c) as the element type, one 16-byte chunk: exact
+// (int8 integers and fp8 E4M3 values are fp32, fp16 and bf16 numbers).
+template <int DT, int CT>
 __device__ __forceinline__ u32x4 codes_to_elems(const u32x4& c) {
   u32x4 r;
-  auto f = [](uint32_t w, int i) { return (float)(int32_t)(int8_t)((w >> (8 * i)) & 0xFFu); };
   if constexpr (DT == kF32) {
+    float x[4];
+    codes4_t<CT>(c[0], x);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(f(c[0], i));
+    for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(x[i]);
   } else {
 #pragma unroll
-    for (int w = 0; w < 2; ++w)
+    for (int w = 0; w < 2; ++w) {
+      float x[4];
+      codes4_t<CT>(c[w], x);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float lo = f(c[w], 2 * h), hi = f(c[w], 2 * h + 1);
+        const float lo = x[2 * h], hi = x[2 * h + 1];
         if constexpr (DT == kBF16)
           r[2 * w + h] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
         else
           r[2 * w + h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
       }
+    }
   }
   return r;
 }
 
-template <int DT, int D, bool BIAS, int NW, bool Q8>
+// CT: 0 for a cache in the element type, else the code type of the cache.
+template <int DT, int D, bool BIAS, int NW, int CT>
 __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
+  constexpr bool Q8 = CT != 0;
   using Sh = ChunkShape<DT, D, NW>;
   constexpr int kThreads = Sh::kThreads;
   constexpr int BQ = 16 * NW;  // query rows per workgroup
@@ -336,8 +343,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
         if (c >= Sh::CHUNKS) continue;
       const int key = c / CPR, part = c % CPR;
       const int d0 = part * (16 / e);
-      const u32x4 kw = Q8 ? codes_to_elems<DT>(rg.k[u]) : rg.k[u];
-      const u32x4 vw = Q8 ? codes_to_elems<DT>(rg.v[u]) : rg.v[u];
+      const u32x4 kw = Q8 ? codes_to_elems<DT, CT>(rg.k[u]) : rg.k[u];
+      const u32x4 vw = Q8 ? codes_to_elems<DT, CT>(rg.v[u]) : rg.v[u];
       if constexpr (DT == kF32) {
         float* kd = (float*)sK + key * KS + d0;
         float* vd = (float*)sV + key * VS + d0;
@@ -592,33 +599,33 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   slice_tail_rows(a, pl, b, kvh, D, CE, nullptr, nullptr);
 }
 
-template <int DT, int D, int NW, bool Q8>
+template <int DT, int D, int NW, int CT>
 hipError_t launch_w(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
   if (a.bias)
-    attn_chunk_kernel<DT, D, true, NW, Q8><<<grid, NW * kWave, 0, st>>>(a);
+    attn_chunk_kernel<DT, D, true, NW, CT><<<grid, NW * kWave, 0, st>>>(a);
   else
-    attn_chunk_kernel<DT, D, false, NW, Q8><<<grid, NW * kWave, 0, st>>>(a);
+    attn_chunk_kernel<DT, D, false, NW, CT><<<grid, NW * kWave, 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <int DT, int D, bool Q8>
+template <int DT, int D, int CT>
 hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
   if constexpr (ChunkShape<DT, D, 4>::ok) {
-    return a.waves == 8 ? launch_w<DT, D, 8, Q8>(a, st) : launch_w<DT, D, 4, Q8>(a, st);
+    return a.waves == 8 ? launch_w<DT, D, 8, CT>(a, st) : launch_w<DT, D, 4, CT>(a, st);
   } else {
     return hipErrorInvalidValue;
   }
 }
 
-template <int DT, bool Q8>
+template <int DT, int CT>
 hipError_t launch_t(int D, const AttnArgs& a, hipStream_t st) {
   switch (D) {
-    case 16: return launch_d<DT, 16, Q8>(a, st);
-    case 32: return launch_d<DT, 32, Q8>(a, st);
-    case 64: return launch_d<DT, 64, Q8>(a, st);
-    case 128: return launch_d<DT, 128, Q8>(a, st);
-    case 256: return launch_d<DT, 256, Q8>(a, st);
+    case 16: return launch_d<DT, 16, CT>(a, st);
+    case 32: return launch_d<DT, 32, CT>(a, st);
+    case 64: return launch_d<DT, 64, CT>(a, st);
+    case 128: return launch_d<DT, 128, CT>(a, st);
+    case 256: return launch_d<DT, 256, CT>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,17 @@
+// swgqa_attn_chunk_f8.hip -- the MFMA chunk kernel of swgqa_attn_chunk.hpp
+// for fp8 E4M3 caches (codes converted to the element type as they are
+// staged).
+#include "swgqa_attn_chunk.hpp"
+
+namespace swgqa {
+
+hipError_t launch_attn_chunk_f8(int dtype, int D, const AttnArgs& a, hipStream_t st) {
+  switch (dtype) {
+    case kF32: return launch_t<kF32, kCodeFp8>(D, a, st);
+    case kF16: return launch_t<kF16, kCodeFp8>(D, a, st);
+    case kBF16: return launch_t<kBF16, kCodeFp8>(D, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace swgqa

@@ -8,9 +8,9 @@ namespace swgqa {
 
 hipError_t launch_attn_chunk_q8(int dtype, int D, const AttnArgs& a, hipStream_t st) {
   switch (dtype) {
-    case kF32: return launch_t<kF32, true>(D, a, st);
-    case kF16: return launch_t<kF16, true>(D, a, st);
-    case kBF16: return launch_t<kBF16, true>(D, a, st);
+    case kF32: return launch_t<kF32, kCodeInt8>(D, a, st);
+    case kF16: return launch_t<kF16, kCodeInt8>(D, a, st);
+    case kBF16: return launch_t<kBF16, kCodeInt8>(D, a, st);
     default: return hipErrorInvalidValue;
   }
 }

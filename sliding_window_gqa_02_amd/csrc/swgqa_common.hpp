@@ -261,9 +261,61 @@ __device__ __forceinline__ uint32_t quant_code(float x, float scale) {
   return (uint32_t)((int32_t)t & 0xFF);
 }
 
+// Code types of a quantized cache.
+constexpr int kCodeInt8 = 1;
+constexpr int kCodeFp8 = 2;  // OCP E4M3 ("FN"): bias 7, no infinities, 0x7F NaN, max 448
+
+// The fp8 E4M3 code of t: nearest value with ties to the even code (the
+// mantissa rounded to 3 bits on the float's bits), magnitudes of 448 or more
+// saturated to 448, NaN to 0x7F, results of zero coded +0.
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+  if (t != t) return 0x7Fu;
+  const uint32_t sign = (__float_as_uint(t) >> 24) & 0x80u;
+  const float a = fabsf(t);
+  uint32_t c;
+  if (a >= 448.0f) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9 (8 -> 2^-6)
+    c = (uint32_t)rintf(a * 512.0f);
+  } else {
+    const uint32_t u = __float_as_uint(a);
+    const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);  // 3 mantissa bits, ties to even
+    c = (r >> 20) - (120u << 3);                          // float exponent E -> E - 120
+  }
+  return c == 0u ? 0u : (c | sign);
+}
+
+// The code of x for a quantization scale (binary32 quotient first).
+template <int CT>
+__device__ __forceinline__ uint32_t quant_code_t(float x, float scale) {
+  if constexpr (CT == kCodeFp8) return e4m3_code(x / scale);
+  else return quant_code(x, scale);
+}
+
+// The four codes of a word as floats (exact): int8 by sign-extending
+// conversion, fp8 E4M3 by the hardware's packed conversion (OCP E4M3 on this
+// target).
+template <int CT>
+__device__ __forceinline__ void codes4_t(uint32_t w, float* out) {
+  if constexpr (CT == kCodeFp8) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    out[0] = lo[0];
+    out[1] = lo[1];
+    out[2] = hi[0];
+    out[3] = hi[1];
+  } else {
+    out[0] = (float)(int32_t)(int8_t)(w & 0xFFu);
+    out[1] = (float)(int32_t)(int8_t)((w >> 8) & 0xFFu);
+    out[2] = (float)(int32_t)(int8_t)((w >> 16) & 0xFFu);
+    out[3] = (float)(int32_t)(int8_t)(w >> 24);
+  }
+}
+
 // The 16 codes of elements [c0, c0 + 16) of a row of the element type (row
 // and c0 * e 16-byte aligned).
-template <int DT>
+template <int DT, int CT = kCodeInt8>
 __device__ __forceinline__ u32x4 quant_chunk16(const void* row, int64_t c0, float scale) {
   constexpr int e = Elem<DT>::bytes;
   float x[16];
@@ -276,8 +328,9 @@ __device__ __forceinline__ u32x4 quant_chunk16(const void* row, int64_t c0, floa
   u32x4 r;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
-    r[w] = quant_code(x[4 * w], scale) | (quant_code(x[4 * w + 1], scale) << 8) |
-           (quant_code(x[4 * w + 2], scale) << 16) | (quant_code(x[4 * w + 3], scale) << 24);
+    r[w] = quant_code_t<CT>(x[4 * w], scale) | (quant_code_t<CT>(x[4 * w + 1], scale) << 8) |
+           (quant_code_t<CT>(x[4 * w + 2], scale) << 16) |
+           (quant_code_t<CT>(x[4 * w + 3], scale) << 24);
   return r;
 }
 

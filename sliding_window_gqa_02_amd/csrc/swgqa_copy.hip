@@ -31,7 +31,7 @@ __global__ void plan_kernel(const int32_t* seqlens, int32_t B, int32_t S,
 
 // int8 codes of the step's new key and value rows (four elements a thread
 // and pass), for the chunk kernel over an int8 cache.
-template <int DT>
+template <int DT, int CT>
 __global__ void quant_rows_kernel(const void* k, const void* v, uint32_t* kq, uint32_t* vq,
                                   size_t nwords, float ks, float vs) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords;
@@ -39,8 +39,8 @@ __global__ void quant_rows_kernel(const void* k, const void* v, uint32_t* kq, ui
     uint32_t ck = 0u, cv = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ck |= quant_code(load_one<DT>(k, (int64_t)(4 * i + j)), ks) << (8 * j);
-      cv |= quant_code(load_one<DT>(v, (int64_t)(4 * i + j)), vs) << (8 * j);
+      ck |= quant_code_t<CT>(load_one<DT>(k, (int64_t)(4 * i + j)), ks) << (8 * j);
+      cv |= quant_code_t<CT>(load_one<DT>(v, (int64_t)(4 * i + j)), vs) << (8 * j);
     }
     kq[i] = ck;
     vq[i] = cv;
@@ -63,28 +63,33 @@ hipError_t launch_plan(const int32_t* seqlens, int32_t B, int32_t S, int32_t C,
   return hipGetLastError();
 }
 
-hipError_t launch_quant_rows(int dtype, const void* k, const void* v, uint8_t* kq, uint8_t* vq,
-                             size_t n, float k_scale, float v_scale, hipStream_t st) {
+namespace {
+
+template <int CT>
+hipError_t launch_quant_ct(int dtype, const void* k, const void* v, uint32_t* kq, uint32_t* vq,
+                           size_t nwords, float ks, float vs, unsigned blocks, hipStream_t st) {
+  switch (dtype) {
+    case kF32: quant_rows_kernel<kF32, CT><<<blocks, 256, 0, st>>>(k, v, kq, vq, nwords, ks, vs); break;
+    case kF16: quant_rows_kernel<kF16, CT><<<blocks, 256, 0, st>>>(k, v, kq, vq, nwords, ks, vs); break;
+    case kBF16: quant_rows_kernel<kBF16, CT><<<blocks, 256, 0, st>>>(k, v, kq, vq, nwords, ks, vs); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(int dtype, int ct, const void* k, const void* v, uint8_t* kq,
+                             uint8_t* vq, size_t n, float k_scale, float v_scale, hipStream_t st) {
   const size_t nwords = n / 4;
   if (nwords == 0) return hipSuccess;
   size_t blocks = (nwords + 255) / 256;
   if (blocks > 2048) blocks = 2048;
-  switch (dtype) {
-    case kF32:
-      quant_rows_kernel<kF32><<<(unsigned)blocks, 256, 0, st>>>(k, v, (uint32_t*)kq, (uint32_t*)vq,
-                                                               nwords, k_scale, v_scale);
-      break;
-    case kF16:
-      quant_rows_kernel<kF16><<<(unsigned)blocks, 256, 0, st>>>(k, v, (uint32_t*)kq, (uint32_t*)vq,
-                                                               nwords, k_scale, v_scale);
-      break;
-    case kBF16:
-      quant_rows_kernel<kBF16><<<(unsigned)blocks, 256, 0, st>>>(k, v, (uint32_t*)kq, (uint32_t*)vq,
-                                                                nwords, k_scale, v_scale);
-      break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (ct == kCodeFp8)
+    return launch_quant_ct<kCodeFp8>(dtype, k, v, (uint32_t*)kq, (uint32_t*)vq, nwords, k_scale,
+                                     v_scale, (unsigned)blocks, st);
+  return launch_quant_ct<kCodeInt8>(dtype, k, v, (uint32_t*)kq, (uint32_t*)vq, nwords, k_scale,
+                                    v_scale, (unsigned)blocks, st);
 }
 
 hipError_t launch_zero_words(uint32_t* words, size_t n, hipStream_t st) {

@@ -66,8 +66,9 @@ struct CopyArgs {
   GapDiv gdiv;
   int32_t elem_bytes;     // cache element bytes (1 for int8 codes)
   int32_t skip_drifting;  // shared buffer and the append already fused
-  // int8 cache: new rows (element type, src_elem_bytes each) are quantized
-  // with k_scale / v_scale as they are written
+  // quantized cache: new rows (element type, src_elem_bytes each) are
+  // quantized with k_scale / v_scale as they are written; quant is the code
+  // type (kCodeInt8, kCodeFp8) or 0
   int32_t quant;
   int32_t src_elem_bytes;
   int32_t dtype;
@@ -99,12 +100,16 @@ bool chunk_kernel_supports(int dtype, int D);
 int chunk_rows_per_workgroup(int waves);  // 4 or 8 waves
 int chunk_keys_per_block();
 hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t stream);
-// The same kernel over an int8 cache (swgqa_attn_chunk_q8.hip); a.k / a.v
-// hold the step's new rows as codes (launch_quant_rows).
+// The same kernel over an int8 / fp8 E4M3 cache (swgqa_attn_chunk_q8.hip,
+// swgqa_attn_chunk_f8.hip); a.k / a.v hold the step's new rows as codes
+// (launch_quant_rows).
 hipError_t launch_attn_chunk_q8(int dtype, int D, const AttnArgs& a, hipStream_t stream);
-// int8 codes of n elements of k and v (element type dtype), n % 4 == 0.
-hipError_t launch_quant_rows(int dtype, const void* k, const void* v, uint8_t* kq, uint8_t* vq,
-                             size_t n, float k_scale, float v_scale, hipStream_t stream);
+hipError_t launch_attn_chunk_f8(int dtype, int D, const AttnArgs& a, hipStream_t stream);
+// Codes (code type ct: kCodeInt8 / kCodeFp8) of n elements of k and v
+// (element type dtype), n % 4 == 0.
+hipError_t launch_quant_rows(int dtype, int ct, const void* k, const void* v, uint8_t* kq,
+                             uint8_t* vq, size_t n, float k_scale, float v_scale,
+                             hipStream_t stream);
 // Staged decode kernel (swgqa_attn_decode.hip): supports row sizes up to
 // 256 bytes and NQ * (16 / element bytes) <= 64.
 bool decode_kernel_supports(int dtype, int D, int nq);
@@ -117,6 +122,9 @@ hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
 bool decode_q8_supports(int D, int nq);
 int decode_q8_stage_rows(int D, int nq);
 hipError_t launch_attn_decode_q8(int dtype, int D, int nq, const AttnArgs& a,
+                                 hipStream_t stream);
+// The same kernel for fp8 E4M3 caches (swgqa_attn_decode_f8.hip).
+hipError_t launch_attn_decode_f8(int dtype, int D, int nq, const AttnArgs& a,
                                  hipStream_t stream);
 // The same kernel with rotary embedding fused in (head sizes 32, 64, 128).
 bool decode_rotary_supports(int dtype, int D, int nq);

@@ -132,7 +132,9 @@ __device__ __forceinline__ void writeback_part(const CopyArgs& a, uint32_t idx) 
       const int64_t i = i0 + (j >> wlog);
       const int64_t w = j & (wn - 1);
       const char* srow = fresh + (((int64_t)b * a.S + i) * a.Hkv + kvh) * src_rowb;
-      dst[(pl.kept + i) * w16 + w] = quant_chunk16<DT>(srow, (col * wn + w) * 16, scale);
+      dst[(pl.kept + i) * w16 + w] =
+          a.quant == kCodeFp8 ? quant_chunk16<DT, kCodeFp8>(srow, (col * wn + w) * 16, scale)
+                              : quant_chunk16<DT, kCodeInt8>(srow, (col * wn + w) * 16, scale);
     }
     return;
   }

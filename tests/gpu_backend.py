@@ -42,8 +42,7 @@ INT8 = "int8"  # cache storage tag of an int8 cache
 
 
 def cache_poison(cfg: Cfg):
-    from tests.scenario import POISON8
-    return POISON8 if cfg.kv_int8 else nan_value(cfg.dtype)
+    return cfg.poison_code if cfg.quantized else nan_value(cfg.dtype)
 
 
 class GuardedCache:
@@ -52,7 +51,7 @@ class GuardedCache:
 
     CANARY32 = 0x5A5AA5A5
 
-    def __init__(self, shape, dtype):
+    def __init__(self, shape, dtype, poison=None):
         n = int(np.prod(shape))
         if dtype == INT8:
             self.flat = torch.empty(n + 2 * GUARD, dtype=torch.int8, device=DEV)
@@ -64,8 +63,7 @@ class GuardedCache:
             else:
                 self.flat.fill_(0x2BCD)
         self.t = self.flat[GUARD:GUARD + n].view(*shape)
-        from tests.scenario import POISON8
-        self.t.fill_(POISON8 if dtype == INT8 else nan_value(dtype))
+        self.t.fill_(poison if poison is not None else nan_value(dtype))
         self.dtype = dtype
 
     def intact(self) -> bool:
@@ -87,10 +85,11 @@ class GpuBackend:
         self.B = B
         self.mode = mode
         shape = (B, cfg.Hkv, cfg.C, cfg.D)
-        ct = INT8 if cfg.kv_int8 else cfg.dtype
-        self.bufs = [(GuardedCache(shape, ct), GuardedCache(shape, ct))]
+        ct = INT8 if cfg.quantized else cfg.dtype
+        self.bufs = [(GuardedCache(shape, ct, cache_poison(cfg)), GuardedCache(shape, ct, cache_poison(cfg)))]
         if mode == "separate":
-            self.bufs.append((GuardedCache(shape, ct), GuardedCache(shape, ct)))
+            self.bufs.append((GuardedCache(shape, ct, cache_poison(cfg)),
+                              GuardedCache(shape, ct, cache_poison(cfg))))
         if K is not None:
             self.bufs[0][0].t.copy_(to_dev(K))
             self.bufs[0][1].t.copy_(to_dev(V))
@@ -175,7 +174,7 @@ class GpuBackend:
         return self.ws is None or int(self.ws[64:4096].abs().sum().item()) == 0
 
     def present_host(self):
-        if self.cfg.kv_int8:
+        if self.cfg.quantized:
             return self.K.cpu().numpy(), self.V.cpu().numpy()
         return to_host(self.K, self.cfg.dtype), to_host(self.V, self.cfg.dtype)
 

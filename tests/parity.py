@@ -71,7 +71,7 @@ class Lockstep:
              q=None, k=None, v=None, position_ids=None):
         cfg = self.cfg
         # with rotary the cache holds rotated keys, not the generator's rows
-        check_regen = check_regen and cfg.rotary < 0 and not cfg.kv_int8
+        check_regen = check_regen and cfg.rotary < 0 and not cfg.quantized
         P = np.asarray(P, dtype=np.int64)
         if q is None:
             q, k, v = step_inputs(cfg, self.syn, P, S, self.vers)
@@ -98,9 +98,8 @@ class Lockstep:
             # poisoned before the step ([Lb, C) in place, all of a separate
             # present buffer) stay NaN beyond La
             first_poisoned = max(La, int(plan[b, 2])) if self.gpu.mode == "shared" else La
-            if cfg.kv_int8:
-                from tests.scenario import POISON8
-                assert (gk[b, :, first_poisoned:] == POISON8).all(), what + " wrote beyond the resident range"
+            if cfg.quantized:
+                assert (gk[b, :, first_poisoned:] == cfg.poison_code).all(), what + " wrote beyond the resident range"
             else:
                 rest = as_f64(gk[b, :, first_poisoned:], cfg.dtype)
                 assert np.isnan(rest).all(), what + " wrote beyond the resident range"

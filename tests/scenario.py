@@ -15,7 +15,8 @@ import oracle
 import synth
 
 NAN16 = {synth.F16: 0x7E00, synth.BF16: 0x7FC0}
-POISON8 = 127  # poison code of an int8 cache
+POISON8 = 127      # poison code of an int8 cache
+POISON_FP8 = 0x7E  # poison code of an fp8 E4M3 cache (448)
 
 
 @dataclasses.dataclass
@@ -37,6 +38,7 @@ class Cfg:
     rotary: int = -1           # -1 off; 0 pairs (k, k + D/2); 1 interleaved pairs
     rot_rows: int = 4096       # rows of the cos / sin tables
     kv_int8: bool = False      # int8 cache codes with per-tensor scales
+    kv_fp8: bool = False       # fp8 E4M3 cache codes with per-tensor scales
     k_scale: float = 0.05
     v_scale: float = 0.04
 
@@ -51,16 +53,26 @@ class Cfg:
                                   smooth_softmax=int(self.smooth),
                                   **self.rotary_params(), **self.cache_params())
 
+    @property
+    def quantized(self) -> bool:
+        return self.kv_int8 or self.kv_fp8
+
     def cache_params(self):
-        if not self.kv_int8:
+        if not self.quantized:
             return {}
-        return dict(kv_cache_type=1, k_scale=self.k_scale, v_scale=self.v_scale)
+        return dict(kv_cache_type=2 if self.kv_fp8 else 1, k_scale=self.k_scale,
+                    v_scale=self.v_scale)
+
+    @property
+    def poison_code(self) -> int:
+        return POISON_FP8 if self.kv_fp8 else POISON8
 
     def cache_array(self, shape):
-        """A cache whose every row is poison: NaN, or with int8 codes the
-        extreme code 127 (a read of it moves scores and outputs)."""
-        if self.kv_int8:
-            return np.full(shape, POISON8, dtype=np.int8)
+        """A cache whose every row is poison: NaN, or with 8-bit codes an
+        extreme code (int8 127, fp8 448): a read of it moves scores and
+        outputs.  Codes are held as int8 bytes."""
+        if self.quantized:
+            return np.full(shape, self.poison_code, dtype=np.int8)
         return nan_array(shape, self.dtype)
 
     def rotary_params(self):
@@ -125,14 +137,21 @@ def seeded_cache(cfg: Cfg, syn: synth.Synth, Ts, vers: Versions):
     NaN in every unspecified row.  With an int8 cache the resident rows are
     seeded codes (uniform in [-100, 100]) and the rest poison codes."""
     shape = (len(Ts), cfg.Hkv, cfg.C, cfg.D)
-    if cfg.kv_int8:
+    if cfg.quantized:
         rng = np.random.default_rng(cfg.seed + 8101)
         K = cfg.cache_array(shape)
         V = cfg.cache_array(shape)
+
+        def codes(n):
+            if cfg.kv_int8:
+                return rng.integers(-100, 101, size=n)
+            # fp8: sign, exponent 0..9, mantissa: finite values up to 7.5
+            c = (rng.integers(0, 2, size=n) << 7) | (rng.integers(0, 10, size=n) << 3) | rng.integers(0, 8, size=n)
+            return c.astype(np.uint8).view(np.int8)
         for b, T in enumerate(Ts):
             L = oracle.resident_length(int(T), cfg.C, cfg.W)
-            K[b, :, :L] = rng.integers(-100, 101, size=(cfg.Hkv, L, cfg.D))
-            V[b, :, :L] = rng.integers(-100, 101, size=(cfg.Hkv, L, cfg.D))
+            K[b, :, :L] = codes((cfg.Hkv, L, cfg.D))
+            V[b, :, :L] = codes((cfg.Hkv, L, cfg.D))
         return K, V
     K = nan_array(shape, cfg.dtype)
     V = nan_array(shape, cfg.dtype)

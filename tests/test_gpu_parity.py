@@ -580,8 +580,64 @@ def test_int8_cache_host_errors():
     mk = lambda **kw: sw.make_params(1, 1, 2, 2, 64, 6, 4, 8, **kw)
     assert sw.forward_status(mk(kv_cache_type=1, k_scale=0.0, v_scale=1.0), t, t, t, t, t, seq,
                              None, t, t, t, ws) == sw.ERR_ARG
-    assert sw.forward_status(mk(kv_cache_type=2, k_scale=1.0, v_scale=1.0), t, t, t, t, t, seq,
+    assert sw.forward_status(mk(kv_cache_type=3, k_scale=1.0, v_scale=1.0), t, t, t, t, t, seq,
                              None, t, t, t, ws) == sw.ERR_UNSUPPORTED
     p8 = sw.make_params(1, 1, 2, 2, 8, 6, 4, 8, kv_cache_type=1, k_scale=1.0, v_scale=1.0)
     assert sw.forward_status(p8, t, t, t, t, t, seq, None, t, t, t, ws) == sw.ERR_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# fp8 E4M3 cache (kv_cache_type 2): the int8 paths with E4M3 codes (nearest,
+# ties to the even code, saturated at 448), decode and multi-token steps.
+F8 = [
+    Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=81, kv_fp8=True, k_scale=0.02, v_scale=0.03),
+    Cfg(B=2, Hq=16, Hkv=2, D=128, C=70, W=64, seed=82, dtype=synth.BF16, softcap=30.0,
+        kv_fp8=True, k_scale=0.01, v_scale=0.01),
+    Cfg(B=1, Hq=4, Hkv=4, D=256, C=20, W=17, seed=83, dtype=synth.F16, kv_fp8=True,
+        sink_std=1.0),
+    Cfg(B=3, Hq=4, Hkv=2, D=32, C=30, W=20, seed=84, dtype=synth.F16, kv_fp8=True, rotary=1),
+]
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("cfg", F8, ids=lambda c: f"D{c.D}t{c.dtype}g{c.Hq // c.Hkv}rot{c.rotary}")
+def test_fp8_cache_random_steps(cfg, mode):
+    say(f"fp8 cache {cfg} mode={mode}")
+    rng = np.random.default_rng(cfg.seed)
+    run = Lockstep(cfg, mode=mode)
+    T = 0
+    for _ in range(14):
+        S = int(rng.choice([1, 1, 1, 2, 5, 15, 16, 33, int(rng.integers(1, 2 * cfg.C + 2))]))
+        run.step([T] * cfg.B, S)
+        T += S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+def test_fp8_cache_codes_ties_saturation_and_key_splits():
+    """Exact ties and far values on the GPU give the oracle's codes; then a
+    long window over one slice (key splits) on seeded codes."""
+    cfg = Cfg(B=1, Hq=2, Hkv=1, D=16, C=8, W=8, seed=85, kv_fp8=True, k_scale=1.0, v_scale=0.5)
+    vals = np.array([1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -11, 7.5 * 2.0 ** -9,
+                     1000.0, -1000.0, 432.0, 440.0, 447.0, -0.0, 0.3, 15.5 * 2.0 ** -9, 0.0, 5.0])
+    run = Lockstep(cfg)
+    q = np.random.default_rng(85).normal(size=(1, 1, 32)).astype(np.float32)
+    k = vals.astype(np.float32).reshape(1, 1, 16)
+    v = (vals * 0.5).astype(np.float32).reshape(1, 1, 16)
+    run.step([0], 1, q=q, k=k, v=v)
+    gk, gv = run.gpu.present_host()
+    want = np.array([oracle.quantize_e4m3(float(x), 1.0) for x in vals], np.uint8)
+    assert np.array_equal(gk[0, 0, 0].view(np.uint8), want)
+    assert np.array_equal(gv[0, 0, 0].view(np.uint8), want)
+    long = Cfg(B=1, Hq=4, Hkv=1, D=128, C=1600, W=1500, seed=86, dtype=synth.BF16, kv_fp8=True,
+               k_scale=0.02, v_scale=0.02)
+    syn = long.synth()
+    vers = Versions(1)
+    P0 = np.array([1700])
+    K, V = seeded_cache(long, syn, P0, vers)
+    run = Lockstep(long, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S in [1, 64, 4]:
+        run.step(P, S)
+        P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")
