@@ -49,15 +49,18 @@
  *    sum_j e^{s_j}); with smooth_softmax != 0 and no head_sink that logit
  *    is 0 (the Investigation Report, sections 1.1 and 1.3, names head_sink
  *    and smooth_softmax without defining them; this is the plainest reading);
- *  - quantized cache (kv_cache_type 1): past/present hold int8 codes, one
- *    scale per tensor (k_scale for keys, v_scale for values); a cache
- *    element stands for code * scale, and a new element x (after rotary) is
- *    stored as the binary32 quotient x / scale rounded to an integer with
- *    ties to even and saturated to [-128, 127]; the step attends to every key
- *    and value row in that dequantized form, new rows included (the
- *    Investigation Report, section 1.1, names k_scale / v_scale and a cache
- *    type only; this is the plainest reading).  Head sizes below 16 return
- *    SWGQA_ERR_UNSUPPORTED with this cache;
+ *  - quantized cache (kv_cache_type 1: int8, 2: fp8 E4M3): past/present
+ *    hold 8-bit codes, one scale per tensor (k_scale for keys, v_scale for
+ *    values); a cache element stands for value(code) * scale, and a new
+ *    element x (after rotary) is stored as the code of the binary32 quotient
+ *    x / scale -- int8: rounded to an integer with ties to even, saturated to
+ *    [-128, 127], NaN to -128; fp8: OCP E4M3 ("FN": bias 7, no infinities,
+ *    0x7F NaN), the nearest value with ties to the even code, magnitudes of
+ *    448 or more saturated to 448, NaN to 0x7F, zero results coded +0; the
+ *    step attends to every key and value row in that dequantized form, new
+ *    rows included (the Investigation Report, section 1.1, names k_scale /
+ *    v_scale and a cache type only; this is the plainest reading).  Head
+ *    sizes below 16 return SWGQA_ERR_UNSUPPORTED with these caches;
  *  - query head h reads KV head h / (num_heads / kv_num_heads);
  *  - present rows [0, L(T)) receive the newest L(T) rows of that
  *    concatenation (byte copies); rows [L(T), C) are unspecified.
@@ -120,7 +123,7 @@ typedef struct {
   int32_t do_rotary;             /* 0 or 1 */
   int32_t rotary_interleaved;    /* 0: pairs (k, k + D/2); 1: pairs (2k, 2k + 1) */
   int32_t rotary_cache_rows;     /* rows of cos_cache / sin_cache (>= 1 with do_rotary) */
-  int32_t kv_cache_type;         /* 0: caches in dtype; 1: int8 codes (see above) */
+  int32_t kv_cache_type;         /* 0: caches in dtype; 1: int8; 2: fp8 E4M3 codes (see above) */
   float k_scale;                 /* kv_cache_type 1: key element = code * k_scale (> 0) */
   float v_scale;                 /* kv_cache_type 1: value element = code * v_scale (> 0) */
 } swgqa_params;
@@ -154,8 +157,8 @@ swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes,
  *   query          (B, S, Hq*D)
  *   key, value     (B, S, Hkv*D)         the S new rows of every item
  *   past_key/value (B, Hkv, C, D)        rows [0, L(P_b)) valid on entry;
- *                                        dtype elements, or int8 codes with
- *                                        kv_cache_type 1
+ *                                        dtype elements, or 8-bit codes with
+ *                                        kv_cache_type 1 / 2
  *   seqlens_k      int32 (B)             total length T_b = seqlens_k[b]+1
  *   attention_bias NULL or (B|1, Hq|1, S, total_sequence_length)
  *   head_sink      NULL or (Hq)          per-head sink logit
