@@ -44,6 +44,10 @@ constexpr int kQ8MaxNewRows = 16;  // S < 16 on this path
 #define SWGQA_Q8_DEPTH 3
 #endif
 
+#ifndef SWGQA_Q8_PV16
+#define SWGQA_Q8_PV16 1
+#endif
+
 #ifndef SWGQA_Q8_UMUL
 #define SWGQA_Q8_UMUL 1
 #endif
@@ -122,6 +126,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   constexpr int e = Elem<DT>::bytes;
   constexpr int W16 = D / 16;  // 16-byte chunks per cache row
   static_assert(Sh::ok, "unsupported int8 decode shape");
+  // value sums as packed fp16 dot products over row pairs (16-bit outputs)
+  constexpr bool PV16 = DT != kF32 && U % 2 == 0 && SWGQA_Q8_PV16;
 
   const uint32_t T = gridDim.x;  // ntiles * nsplit
   const uint32_t P = xcd_contiguous(blockIdx.x + T * (blockIdx.y + gridDim.y * blockIdx.z),
@@ -384,7 +390,10 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
     float psum = 0.0f;
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-      const float p = (s[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[k] - m_new);
+      float p = (s[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[k] - m_new);
+      // PV16: P enters the value sum rounded to fp16 and the normaliser sums
+      // the rounded P, so the output stays an exact weighted mean
+      if constexpr (PV16) p = (float)(_Float16)p;
       pbuf[lane + k * kWave] = p;
       psum += p;
     }
@@ -406,19 +415,45 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
 #pragma unroll
         for (int k = 0; k < EPL; ++k) acc[tq][k] *= cr[tq];
     }
+    if constexpr (PV16) {
+      // two rows at a time: (p_a, p_b) . (v_a[k], v_b[k]) as one packed fp16
+      // dot product per query and element (codes are exact in fp16)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = u * RPW + rslot;
-      float pr[NQ];
+      for (int u = 0; u < U; u += 2) {
+        const int ra = u * RPW + rslot, rb = ra + RPW;
+        uint32_t pp[NQ];
 #pragma unroll
-      for (int tq = 0; tq < NQ; ++tq) pr[tq] = pbuf[row * NQ + tq];
-      float vf[EPL];
+        for (int tq = 0; tq < NQ; ++tq)
+          pp[tq] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pbuf[ra * NQ + tq],
+                                                                           pbuf[rb * NQ + tq]));
+        float va[EPL], vb[EPL];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) codes4_t<CT>(vr[u][w], vf + 4 * w);
+        for (int w = 0; w < 4; ++w) {
+          codes4_t<CT>(vr[u][w], va + 4 * w);
+          codes4_t<CT>(vr[u + 1][w], vb + 4 * w);
+        }
 #pragma unroll
-      for (int tq = 0; tq < NQ; ++tq)
+        for (int k = 0; k < EPL; ++k) {
+          const uint32_t vp = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(va[k], vb[k]));
 #pragma unroll
-        for (int k = 0; k < EPL; ++k) acc[tq][k] = fmaf(pr[tq], vf[k], acc[tq][k]);
+          for (int tq = 0; tq < NQ; ++tq) acc[tq][k] = dot2_16<kF16>(pp[tq], vp, acc[tq][k]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int row = u * RPW + rslot;
+        float pr[NQ];
+#pragma unroll
+        for (int tq = 0; tq < NQ; ++tq) pr[tq] = pbuf[row * NQ + tq];
+        float vf[EPL];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) codes4_t<CT>(vr[u][w], vf + 4 * w);
+#pragma unroll
+        for (int tq = 0; tq < NQ; ++tq)
+#pragma unroll
+          for (int k = 0; k < EPL; ++k) acc[tq][k] = fmaf(pr[tq], vf[k], acc[tq][k]);
+      }
     }
     wave_lds_fence_q8();
   };
