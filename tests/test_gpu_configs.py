@@ -273,3 +273,66 @@ def test_batched_serving_full():
     say(f"  compaction events {events}")
     for b in range(32):
         dev.check_layout(syn, b, T[b], vers, "final")
+
+
+# ---------------------------------------------------------------------------
+# The batched serving decode over an 8-bit cache (int8 / fp8 E4M3), at the
+# full size and in the benchmark's launch configuration: seeded codes, 48
+# decode steps; four items are followed by the oracle from the same seeded
+# codes, compared at every step (outputs) and at the end (resident codes byte
+# for byte).
+@pytest.mark.parametrize("code", ["int8", "fp8"])
+def test_batched_serving_full_8bit(code):
+    from tests.gpu_backend import to_dev, to_host
+    import sliding_window_gqa_02_amd as sw
+    fp8 = code == "fp8"
+    cfg = Cfg(B=32, Hq=32, Hkv=8, D=128, C=4608, W=4096, seed=1007, dtype=synth.BF16,
+              softcap=50.0, kv_int8=not fp8, kv_fp8=fp8, k_scale=0.02, v_scale=0.02)
+    syn = cfg.synth()
+    rng = np.random.default_rng(1007)
+    P0 = rng.integers(4096, 32769, size=32)
+    shape = (32, cfg.Hkv, cfg.C, cfg.D)
+    if fp8:  # finite E4M3 codes up to 7.5
+        codes = lambda sh: ((rng.integers(0, 2, sh) << 7) | (rng.integers(0, 10, sh) << 3) |
+                            rng.integers(0, 8, sh)).astype(np.uint8).view(np.int8)
+    else:
+        codes = lambda sh: rng.integers(-100, 101, sh).astype(np.int8)
+    K0, V0 = codes(shape), codes(shape)
+    tracked = [0, 7, 19, 31]
+    oK = {b: K0[b:b + 1].copy() for b in tracked}
+    oV = {b: V0[b:b + 1].copy() for b in tracked}
+    K = torch.from_numpy(K0).to("cuda:0")
+    V = torch.from_numpy(V0).to("cuda:0")
+    del K0, V0
+    T = P0.copy()
+    ws = None
+    for s in range(48):
+        P = T.copy()
+        q, k, v = syn.step_inputs(P, 1)
+        p = sw.make_params(32, 1, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, int((P + 1).max()),
+                           cfg.dtype, cfg.scale, cfg.softcap, **cfg.cache_params())
+        if ws is None:
+            ws = torch.zeros(sw.workspace_size(p) // 4 + 64, dtype=torch.int32, device="cuda:0")
+            sw.workspace_init(ws)
+        dq = to_dev(q)
+        out = torch.empty_like(dq)
+        sw.forward(p, dq, to_dev(k), to_dev(v), K, V, to_dev(P.astype(np.int32)), None, out, K, V,
+                   ws)
+        torch.cuda.synchronize()
+        assert sw.device_status(ws, clear=True) == sw.OK
+        got = to_host(out, cfg.dtype)
+        for b in tracked:
+            po = cfg.params(1, int(P[b]) + 1, B=1)
+            st, ref, _ = oracle.forward(po, np.ascontiguousarray(q[b:b + 1]),
+                                        np.ascontiguousarray(k[b:b + 1]),
+                                        np.ascontiguousarray(v[b:b + 1]), oK[b], oV[b],
+                                        np.array([P[b]], np.int32))
+            assert st == 0
+            assert_outputs_close(got[b:b + 1], ref, cfg.dtype, f"{code} step {s} item {b}")
+        T += 1
+    say(f"  {code}: 48 steps, items {tracked} followed by the oracle")
+    gk, gv = K.cpu().numpy(), V.cpu().numpy()
+    for b in tracked:
+        L = oracle.resident_length(int(T[b]), cfg.C, cfg.W)
+        assert np.array_equal(gk[b, :, :L], oK[b][0, :, :L]), f"{code} K item {b}"
+        assert np.array_equal(gv[b, :, :L], oV[b][0, :, :L]), f"{code} V item {b}"
