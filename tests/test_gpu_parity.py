@@ -641,3 +641,65 @@ def test_fp8_cache_codes_ties_saturation_and_key_splits():
         run.step(P, S)
         P = P + S
     say(f"  worst scaled error {run.worst:.3g}")
+
+
+# ---------------------------------------------------------------------------
+# HIP graph replay: a run of steps captured once through the C ABI (the
+# slice counters of the in-kernel compaction included) and replayed three
+# times from a restored cache, with eager work between the replays; every
+# replay equals the eager run byte for byte.
+@pytest.mark.parametrize("cache", ["element", "int8"])
+def test_graph_replay_equals_eager(cache):
+    import ctypes
+    import sliding_window_gqa_02_amd as sw
+    from tests.gpu_backend import to_dev
+    cfg = Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=91, kv_int8=cache == "int8")
+    syn = cfg.synth()
+    vers = Versions(2)
+    P0 = np.array([60, 75])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    Kd, Vd = to_dev(K), to_dev(V)
+    snap = (Kd.clone(), Vd.clone())
+    n = 24
+    steps = []
+    for s in range(n):
+        P = P0 + s
+        q, k, v = step_inputs(cfg, syn, P, 1, vers)
+        steps.append((to_dev(q), to_dev(k), to_dev(v), to_dev((P).astype(np.int32))))
+    p = sw.make_params(2, 1, cfg.Hq, cfg.Hkv, cfg.D, cfg.C, cfg.W, int(P0.max()) + n, cfg.dtype,
+                       **cfg.cache_params())
+    ws = torch.zeros(sw.workspace_size(p) // 4 + 64, dtype=torch.int32, device="cuda:0")
+    sw.workspace_init(ws)
+    outs = [torch.empty_like(st[0]) for st in steps]
+
+    def run(stream):
+        for (q, k, v, seq), out in zip(steps, outs):
+            sw.forward(p, q, k, v, Kd, Vd, seq, None, out, Kd, Vd, ws, stream=stream)
+
+    torch.cuda.synchronize()
+    run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager_out = torch.stack([o.clone() for o in outs])
+    eager_K, eager_V = Kd.clone(), Vd.clone()
+    assert sw.device_status(ws) == sw.OK
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    Kd.copy_(snap[0]), Vd.copy_(snap[1])
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            run(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        Kd.copy_(snap[0]), Vd.copy_(snap[1])
+        for o in outs:
+            o.fill_(0)
+        junk = torch.randn(1 << 16, device="cuda:0").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert bool(torch.equal(torch.stack(outs), eager_out)), f"replay {rep}: outputs"
+        assert bool(torch.equal(Kd, eager_K)) and bool(torch.equal(Vd, eager_V)), f"replay {rep}: cache"
+        assert int(ws[64:4096].abs().sum().item()) == 0, f"replay {rep}: slice counters"
+    assert sw.device_status(ws) == sw.OK
+    del g, junk
