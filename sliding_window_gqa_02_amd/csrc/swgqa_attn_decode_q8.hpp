@@ -16,10 +16,20 @@
 // (swgqa_attn_decode.hpp): one workgroup per (item, KV head, query tile,
 // key split), query i of item b at p = P + i attends keys p - W < j <= p of
 // [resident rows | S new rows].  What differs:
-//  - a lane's 16-byte chunk holds 16 codes, so a row of D codes takes D / 16
-//    lanes; the query tile sits in registers as fp32, 16 elements per query;
 //  - scores are scale * k_scale * sum(q * code), the value sum is taken over
-//    codes and multiplied by v_scale once, at the end;
+//    codes and multiplied by v_scale once, at the end; codes enter the
+//    products as exact 16-bit values (integers of at most 8 bits and E4M3
+//    values are exact in fp16 and bf16);
+//  - 16-bit queries in 4-query tiles with D >= 64 (the serving shape) take
+//    both products on the matrix cores, a 16-row stage at a time: scores as
+//    K . Q^T (16 x 16 x 32 in the query type, the 4 queries repeated over the
+//    16 columns), value sums as P . V (16 x 16 x 16 in fp16, P rounded to
+//    fp16 once and the normaliser summing the rounded values);
+//  - other shapes use the vector units: a lane's 16-byte chunk holds 16
+//    codes, so a row of D codes takes D / 16 lanes, dotted with the query
+//    tile held in registers (packed 16-bit pairs for fp16 / bf16); with
+//    16-bit outputs P is rounded to fp16 and the value sum taken two rows at
+//    a time as packed fp16 dot products;
 //  - the S new rows of the slice are quantized once per workgroup into LDS
 //    (K and V codes); stages that reach them take their chunks from there
 //    (their global loads are clamped to a resident row), and so do the
@@ -51,6 +61,32 @@ constexpr int kQ8MaxNewRows = 16;  // S < 16 on this path
 #ifndef SWGQA_Q8_UMUL
 #define SWGQA_Q8_UMUL 1
 #endif
+
+// Key scores of 16-bit queries on the matrix cores (tiles of 4 queries).
+#ifndef SWGQA_Q8_MFMA
+#define SWGQA_Q8_MFMA 1
+#endif
+
+typedef float q8f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 q8h4 __attribute__((ext_vector_type(4)));
+
+// VB bytes (4, 8 or 16) at a global address, non-temporal, in the first
+// VB / 4 words.
+template <int VB>
+__device__ __forceinline__ u32x4 load_codes_global(uint64_t addr) {
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if constexpr (VB == 16) {
+    r = load16_global<1>(addr);
+  } else if constexpr (VB == 8) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 v = __builtin_nontemporal_load((const u2 __attribute__((address_space(1)))*)addr);
+    r[0] = v[0];
+    r[1] = v[1];
+  } else {
+    r[0] = __builtin_nontemporal_load((const uint32_t __attribute__((address_space(1)))*)addr);
+  }
+  return r;
+}
 
 template <int D, int NQ>
 struct Q8Shape {
@@ -91,14 +127,31 @@ __device__ __forceinline__ float allreduce_q8(float x) {
 }
 
 // Two codes (exact as floats) as one packed pair of the 16-bit type: the
-// upper half of each float for bf16, a conversion for fp16 (integers of at
-// most 8 bits are exact in both).
+// upper half of each float for bf16 (one byte permute), a conversion for fp16
+// (integers of at most 8 bits and E4M3 values are exact in both).
 template <int DT>
 __device__ __forceinline__ uint32_t pack_pair16(float lo, float hi) {
   if constexpr (DT == kBF16) {
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   } else {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+}
+
+// One 16 x 16 x 32 product of the 16-bit type on the matrix cores: lane l
+// supplies row l % 16 of A and column l % 16 of B, with 8 elements each of
+// the 32-element reduction; the result holds column l % 16 and rows
+// 4 (l / 16) + [0, 4).
+template <int DT>
+__device__ __forceinline__ q8f4 mfma16x32(const u32x4& a, const u32x4& b, q8f4 c) {
+  if constexpr (DT == kBF16) {
+    typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a),
+                                                   __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+  } else {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
+                                                  __builtin_bit_cast(h8, b), c, 0, 0, 0);
   }
 }
 
@@ -128,6 +181,24 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   static_assert(Sh::ok, "unsupported int8 decode shape");
   // value sums as packed fp16 dot products over row pairs (16-bit outputs)
   constexpr bool PV16 = DT != kF32 && U % 2 == 0 && SWGQA_Q8_PV16;
+  // Key scores on the matrix cores: a stage's 16 rows against the tile's 4
+  // queries (each repeated in 4 of the 16 columns), D / 32 products of
+  // 32 elements.  Lane l loads row l % 16, chunks (l / 16) % 4 + 4 u of it,
+  // and keeps the score of row l / 4 and query l % 4.
+  constexpr bool MK = DT != kF32 && NQ == 4 && D >= 64 && SR == 16 && SWGQA_Q8_MFMA;
+  constexpr int KM = D / 32;
+  static_assert(!MK || (U == D / 64 && PPL == 1), "matrix-core key path shape");
+  // Value sums on the matrix cores (with the key path): O[q][d] +=
+  // P[q][16 rows] . V[16 rows][d] as D / 16 products of 16 x 16 x 16 in
+  // fp16 -- A holds P (query l % 4 in row l % 16), B the codes.  Lane l
+  // loads rows 4 (l / 16) + [0, 4), bytes [VB (l % 16), VB (l % 16) + VB)
+  // of each; product t takes byte t, so the lane's result column is
+  // element VB (l % 16) + t, and every lane group holds all 4 queries.
+  // P is rounded to fp16 once and the normaliser sums the rounded values.
+  constexpr bool MV = MK;
+  constexpr int VB = D / 16;              // code bytes per lane and row
+  constexpr int UV = MV ? 4 : U;          // value loads per lane and stage
+  constexpr bool PROUND = MV || PV16;     // P rounded to fp16
 
   const uint32_t T = gridDim.x;  // ntiles * nsplit
   const uint32_t P = xcd_contiguous(blockIdx.x + T * (blockIdx.y + gridDim.y * blockIdx.z),
@@ -145,8 +216,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   const int rslot = lane / LPR;
   const int sub = lane % LPR;
 
-  __shared__ float s_part[kWaves][NQ * SR * LPR];   // [q][row][sub]
-  __shared__ float s_p[kWaves][PAIRS];              // [row][q]
+  __shared__ float s_part[kWaves][MK ? 1 : NQ * SR * LPR];   // [q][row][sub]
+  __shared__ __attribute__((aligned(16))) float s_p[kWaves][PAIRS];  // [row][q] ([q][row] on the matrix-core path)
   __shared__ float s_corr[kWaves][NQ];
   __shared__ float s_m[kWaves][NQ];
   __shared__ float s_l[kWaves][NQ];
@@ -162,23 +233,36 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   const int i_first = q0 / a.group;
   int i_last = i_first;
   constexpr int QW = EPL * e / 4;  // words of a query chunk
-  uint32_t qw[NQ][QW];
+  uint32_t qw[MK ? 1 : NQ][QW];
+  // matrix-core path: operand m holds elements 16 ((l / 16) % 4 + 4 (m / 2))
+  // + 8 (m % 2) + [0, 8) of query l % 4
+  u32x4 qb[MK ? KM : 1];
   {
     int h = q0 - i_first * a.group;
+    int64_t my_row = 0;
 #pragma unroll
     for (int tq = 0; tq < NQ; ++tq) {
       const int64_t row = ((int64_t)b * a.S + i_last) * a.Hq + kvh * a.group + h;
-      const char* qp = (const char*)a.q + (row * D + sub * EPL) * e;
+      if constexpr (MK) {
+        if ((lane & 3) == tq) my_row = row;
+      } else {
+        const char* qp = (const char*)a.q + (row * D + sub * EPL) * e;
 #pragma unroll
-      for (int i = 0; i < QW / 4; ++i) {
-        const u32x4 v = *(const u32x4*)(qp + i * 16);
+        for (int i = 0; i < QW / 4; ++i) {
+          const u32x4 v = *(const u32x4*)(qp + i * 16);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) qw[tq][4 * i + w] = v[w];
+          for (int w = 0; w < 4; ++w) qw[tq][4 * i + w] = v[w];
+        }
       }
       if (tq + 1 < NQ && q0 + tq + 1 < nq_item && ++h == a.group) {
         h = 0;
         ++i_last;
       }
+    }
+    if constexpr (MK) {
+      const char* qp = (const char*)a.q + (my_row * D + ((lane >> 4) & 3) * 16) * e;
+#pragma unroll
+      for (int m = 0; m < KM; ++m) qb[m] = *(const u32x4*)(qp + ((m >> 1) * 64 + (m & 1) * 8) * e);
     }
   }
   // The S new K and V rows, one element per thread and pass (their loads
@@ -265,8 +349,13 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   const int64_t slice_base = (int64_t)(b * a.Hkv + kvh) * a.C;
   const int64_t first_row = ncache > 0 ? kb - (pl.P - pl.Lb) : 0;
   const uint32_t last_res = ncache > 0 ? (uint32_t)(ncache - 1) : 0u;
-  const uint64_t ck_lane = (uint64_t)a.past_k + (uint64_t)((slice_base + first_row) << kRowShift) + sub * 16;
+  const uint64_t ck_base = (uint64_t)a.past_k + (uint64_t)((slice_base + first_row) << kRowShift);
+  const uint64_t ck_lane = ck_base + sub * 16;
   const uint64_t dv = (uint64_t)a.past_v - (uint64_t)a.past_k;
+  // matrix-core path: K row lane % 16, chunks (lane / 16) % 4 + 4 u
+  const int krow = lane & 15;
+  const int kchunk = (lane >> 4) & 3;
+  const uint64_t ckm_lane = ck_base + kchunk * 16;
 
   const bool has_cap = a.softcap > 0.0f;
   const float cap = a.softcap;
@@ -280,29 +369,47 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
 
   float m_run = -INFINITY;
   float l_run = 0.0f;
-  float acc[NQ][EPL];
+  float acc[MV ? 1 : NQ][EPL];
 #pragma unroll
-  for (int tq = 0; tq < NQ; ++tq)
+  for (int tq = 0; tq < (MV ? 1 : NQ); ++tq)
 #pragma unroll
     for (int k = 0; k < EPL; ++k) acc[tq][k] = 0.0f;
+  q8f4 o[MV ? VB : 1];  // matrix-core value sums: [t][query]
+#pragma unroll
+  for (int t = 0; t < (MV ? VB : 1); ++t) o[t] = q8f4{0.0f, 0.0f, 0.0f, 0.0f};
+  // matrix-core value path: rows 4 (lane / 16) + r, bytes from VB (lane % 16)
+  const int vg = lane >> 4;
+  const int vc = lane & 15;
 
   float* part = s_part[wave];
   float* pbuf = s_p[wave];
   float* cbuf = s_corr[wave];
 
   // Loads of one stage, issued unconditionally at clamped resident rows.
-  auto load_stage = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) __attribute__((always_inline)) {
+  auto load_stage = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[UV]) __attribute__((always_inline)) {
     const uint32_t s0 = (uint32_t)min(st, nst) * SR;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t jr = min(s0 + u * RPW + rslot, last_res);
       const uint64_t ka = ck_lane + ((uint64_t)jr << kRowShift);
-      kr[u] = load16_global<1>(ka);
-      vr[u] = load16_global<1>(ka + dv);
+      if constexpr (MK) {
+        const uint32_t jk = min(s0 + krow, last_res);
+        kr[u] = load16_global<1>(ckm_lane + ((uint64_t)jk << kRowShift) + u * 64);
+      } else {
+        kr[u] = load16_global<1>(ka);
+      }
+      if constexpr (!MV) vr[u] = load16_global<1>(ka + dv);
+    }
+    if constexpr (MV) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t jv = min(s0 + 4 * vg + r, last_res);
+        vr[r] = load_codes_global<VB>(ck_base + dv + ((uint64_t)jv << kRowShift) + VB * vc);
+      }
     }
   };
 
-  auto compute_stage = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[U]) __attribute__((always_inline)) {
+  auto compute_stage = [&](int st, u32x4 (&kr)[U], u32x4 (&vr)[UV]) __attribute__((always_inline)) {
     const uint32_t s0 = (uint32_t)st * SR;
     if (s0 + SR > (uint32_t)ncache) {  // uniform: the stage reaches new rows
       // branch-free per lane: every lane reads LDS (a clamped row) and
@@ -312,16 +419,55 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
         const uint32_t jr = min(s0 + u * RPW + rslot, (uint32_t)(nk - 1));
         const bool is_new = jr >= (uint32_t)ncache;
         const int r = is_new ? knew0 + (int)jr : 0;
-        const u32x4 kn = s_knew[r * W16 + sub];
-        const u32x4 vn = s_vnew[r * W16 + sub];
+        if constexpr (!MV) {
+          const u32x4 vn = s_vnew[r * W16 + sub];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          kr[u][w] = is_new ? kn[w] : kr[u][w];
-          vr[u][w] = is_new ? vn[w] : vr[u][w];
+          for (int w = 0; w < 4; ++w) vr[u][w] = is_new ? vn[w] : vr[u][w];
+        }
+        if constexpr (MK) {
+          const uint32_t jk = min(s0 + krow, (uint32_t)(nk - 1));
+          const bool k_new = jk >= (uint32_t)ncache;
+          const int rk = k_new ? knew0 + (int)jk : 0;
+          const u32x4 kn = s_knew[rk * W16 + kchunk + 4 * u];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) kr[u][w] = k_new ? kn[w] : kr[u][w];
+        } else {
+          const u32x4 kn = s_knew[r * W16 + sub];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) kr[u][w] = is_new ? kn[w] : kr[u][w];
+        }
+      }
+      if constexpr (MV) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t jv = min(s0 + 4 * vg + r, (uint32_t)(nk - 1));
+          const bool v_new = jv >= (uint32_t)ncache;
+          const int rv = v_new ? knew0 + (int)jv : 0;
+          const uint32_t* vn = (const uint32_t*)s_vnew + (rv * D + VB * vc) / 4;
+#pragma unroll
+          for (int w = 0; w < VB / 4; ++w) vr[r][w] = v_new ? vn[w] : vr[r][w];
         }
       }
     }
-    // A. partial dots over 16 codes -> LDS [q][row][sub]
+    // A. scores: matrix-core products, or partial dots over 16 codes -> LDS
+    // [q][row][sub]
+    q8f4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MK) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float kf[EPL];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) codes4_t<CT>(kr[u][w], kf + 4 * w);
+        u32x4 lo, hi;  // codes 0..7 and 8..15 of the chunk as 16-bit pairs
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lo[j] = pack_pair16<DT>(kf[2 * j], kf[2 * j + 1]);
+          hi[j] = pack_pair16<DT>(kf[8 + 2 * j], kf[9 + 2 * j]);
+        }
+        sacc = mfma16x32<DT>(lo, qb[2 * u], sacc);
+        sacc = mfma16x32<DT>(hi, qb[2 * u + 1], sacc);
+      }
+    } else {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = u * RPW + rslot;
@@ -356,6 +502,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       }
     }
     wave_lds_fence_q8();
+    }
     // B. scores, stage max, probabilities
     float s[PPL];
     float smax = -INFINITY;
@@ -363,10 +510,15 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
     for (int k = 0; k < PPL; ++k) {
       const int pid = lane + k * kWave;
       const int row = pid / NQ;
-      const float* pp = part + (my_q * SR + row) * LPR;
       float x = 0.0f;
+      if constexpr (MK) {
+        const int rs = (lane >> 2) & 3;  // row lane / 4 of the product
+        x = rs == 0 ? sacc[0] : rs == 1 ? sacc[1] : rs == 2 ? sacc[2] : sacc[3];
+      } else {
+        const float* pp = part + (my_q * SR + row) * LPR;
 #pragma unroll
-      for (int w = 0; w < LPR; ++w) x += pp[w];
+        for (int w = 0; w < LPR; ++w) x += pp[w];
+      }
       x *= qk_scale;
       const int32_t jr = st * SR + row;
       const bool vis = jr >= vis_lo && jr <= vis_hi;
@@ -393,8 +545,9 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       float p = (s[k] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[k] - m_new);
       // PV16: P enters the value sum rounded to fp16 and the normaliser sums
       // the rounded P, so the output stays an exact weighted mean
-      if constexpr (PV16) p = (float)(_Float16)p;
-      pbuf[lane + k * kWave] = p;
+      if constexpr (PROUND) p = (float)(_Float16)p;
+      if constexpr (MV) pbuf[(lane & 3) * 16 + (lane >> 2)] = p;  // [q][row]
+      else pbuf[lane + k * kWave] = p;
       psum += p;
     }
     l_run = l_run * corr + psum;
@@ -409,6 +562,31 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       cr[tq] = cbuf[tq];
       rescale |= cr[tq] != 1.0f;
     }
+    if constexpr (MV) {
+      if (rescale) {
+#pragma unroll
+        for (int t = 0; t < VB; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[t][r] *= cr[r];
+      }
+      // A: P of query lane % 4 at rows 4 (lane / 16) + [0, 4)
+      const q8f4 pv = *(const q8f4*)(pbuf + (lane & 3) * 16 + 4 * vg);
+      const uint2 pa = make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1])),
+                                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3])));
+      float vf[4][VB];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int w = 0; w < VB / 4; ++w) codes4_t<CT>(vr[r][w], vf[r] + 4 * w);
+#pragma unroll
+      for (int t = 0; t < VB; ++t) {
+        const uint2 vb = make_uint2(
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(vf[0][t], vf[1][t])),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(vf[2][t], vf[3][t])));
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(q8h4, pa),
+                                                      __builtin_bit_cast(q8h4, vb), o[t], 0, 0, 0);
+      }
+    } else {
     if (rescale) {
 #pragma unroll
       for (int tq = 0; tq < NQ; ++tq)
@@ -455,12 +633,13 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
           for (int k = 0; k < EPL; ++k) acc[tq][k] = fmaf(pr[tq], vf[k], acc[tq][k]);
       }
     }
+    }
     wave_lds_fence_q8();
   };
 
   // Stages of this wave: wave, wave + kWaves, ...; the loads of the next
   // DEPTH - 1 stages are in flight while one is computed.
-  u32x4 k0[U], v0[U], k1[U], v1[U];
+  u32x4 k0[U], v0[UV], k1[U], v1[UV];
   int st = wave;
   if (nk == 0) {
     // empty split
@@ -472,7 +651,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   } else if constexpr (SWGQA_Q8_DEPTH == 3) {
     // whole groups of three stages, no exit between them (a stage past the
     // end loads clamped rows and is not computed)
-    u32x4 k2[U], v2[U];
+    u32x4 k2[U], v2[UV];
     load_stage(st, k0, v0);
     load_stage(st + kWaves, k1, v1);
     const int groups = (nst - wave + 3 * kWaves - 1) / (3 * kWaves);
@@ -502,6 +681,14 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
 
   // Wave result, then the merge of the waves.
   const float l_tot = allreduce_q8<NQ, false>(l_run);
+  if constexpr (MV) {
+    if (lane < 16) {  // lane group 0 holds the 4 queries' sums
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < VB; ++t) s_acc[wave][r][VB * lane + t] = o[t][r];
+    }
+  } else {
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1)
 #pragma unroll
@@ -513,6 +700,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
     for (int tq = 0; tq < NQ; ++tq)
 #pragma unroll
       for (int k = 0; k < EPL; ++k) s_acc[wave][tq][sub * EPL + k] = acc[tq][k];
+  }
   }
   if (lane < NQ) {
     s_m[wave][lane] = m_run;
