@@ -139,8 +139,10 @@ SplitPlan plan_split(const swgqa_params* p) {
     s.nsplit = (int)ns;
     return s;
   }
-  if (multi_token && chunk_kernel_supports(p->dtype, p->head_size)) {
-    // multi-token step on the matrix cores
+  if (multi_token && chunk_kernel_supports(p->dtype, p->head_size) &&
+      p->total_sequence_length >= 4) {
+    // multi-token step on the matrix cores (its bias reads take rows of at
+    // least 4 entries)
     s.kind = Kind::kChunk;
     // 16-bit types: 8-wave workgroups (128 query rows) once a KV head has
     // that many rows -- twice the matrix work per staged K/V block, two

@@ -262,9 +262,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   // key (finite data the mask removes); chunks past the block repeat the last
   // one and are not stored.  The attention_bias entries this lane scores in
   // the block (keys j0 + 16 kt + 4 lg + r) come with them.
+  // The bias entries stay raw words until the block is computed: converting
+  // them where they are loaded would make every block wait for all loads in
+  // flight.
+  constexpr int BW = 8 * e / 4;  // words of the 8 bias entries
   struct BlockRegs {
     u32x4 k[CPT], v[CPT];
-    float bias[8];
+    uint32_t bias[BW];
   };
   // Per-lane parts of the addresses: chunk u of a block is key kc + j0,
   // 16-byte part pc; blocks made only of cache rows (nearly all) add j0 rows
@@ -317,21 +321,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
       }
     }
     if constexpr (BIAS) {
-      if (j0 + BN <= ke) {  // uniform
-        // keys j0 + 16 kt + 4 lg + [0, 4): one 4-element load per tile, at
-        // element (not vector) alignment -- global memory takes unaligned
-        // vector loads on this target
-        const uint64_t bb = bias_lane + (uint64_t)(j0 * e);
+      // keys j0 + 16 kt + 4 lg + [0, 4): one 4-element load per tile, at
+      // element (not vector) alignment -- global memory takes unaligned
+      // vector loads on this target.  The start is clamped to total - 4 so
+      // the load stays inside the row (a valid item has total >= T >= S, and
+      // the host sends steps of S < 16 here only when total >= 4); entries
+      // of keys past the band's end are masked, and a group moved back by the
+      // clamp is shifted into place when the block is computed (shifts of
+      // more than 3 leave only masked keys).  One path for every block, so no
+      // load waits on another.
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) load4_elems_unaligned<DT>(bb + kt * 16 * e, &rg.bias[kt * 4]);
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            rg.bias[kt * 4 + r] =
-                load_elem_global<DT>((uint64_t)a.bias +
-                                     (uint64_t)((bias_row + min(j0 + kt * 16 + 4 * lg + r, ke - 1)) * e));
+      for (int kt = 0; kt < 2; ++kt) {
+        const int64_t g0 = min(j0 + kt * 16, (int64_t)a.total - 4 - 4 * lg);
+        load4_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), &rg.bias[kt * BW / 2]);
       }
     }
   };
@@ -523,9 +525,29 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
     __syncthreads();  // the previous block's LDS reads are done
     store_block(rg);
-    float bias_blk[8];
+    float bias_blk[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (BIAS) {
+      const int64_t j0 = kb + (int64_t)blk * BN;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) bias_blk[r] = has_bias ? rg.bias[r] : 0.0f;
+      for (int kt = 0; kt < 2; ++kt) {
+        // elements the clamp moved the group back by (0 unless the group
+        // passes the end of the row)
+        const int64_t g = j0 + kt * 16 + 4 * lg;
+        const int sh = (int)min(g - min(g, (int64_t)a.total - 4), (int64_t)3);
+        const uint32_t* w = &rg.bias[kt * BW / 2];
+        float x[4];
+        if constexpr (DT == kF32) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = __uint_as_float(w[min(r + sh, 3)]);
+        } else {
+          const uint64_t v = (((uint64_t)w[1] << 32) | w[0]) >> (16 * sh);
+          unpack_word<DT>((uint32_t)v, x);
+          unpack_word<DT>((uint32_t)(v >> 32), x + 2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bias_blk[kt * 4 + r] = x[r];
+      }
+    }
     __syncthreads();
     load_block(block_start(blk + 3), rg);
     compute_block(blk, bias_blk);

@@ -20,8 +20,9 @@
 //     and writes p = 2^(s - m) and the rescale factor to LDS.
 //  C. The V rows (same lane layout as K) are accumulated with p read back
 //     from LDS as a broadcast.
-// K and V of the next stage are loaded into a second register set before
-// stage n is computed, so each wave keeps two stages of loads in flight.
+// K and V of the next DEPTH - 1 stages are loaded into further register sets
+// before stage n is computed, so their loads are in flight while it is
+// (DEPTH = 3: triple buffering).
 // LDS traffic is private to the wave and in program order, so phases only
 // need compiler ordering fences, not barriers.
 //

@@ -233,21 +233,22 @@ __device__ __forceinline__ float load_elem_global(uint64_t addr) {
 }
 
 // Four consecutive elements at a global address aligned only to the element
-// size, as floats (one vector load; AMD global memory accepts unaligned
-// vector accesses).
+// size, as raw words (4 for fp32, 2 for fp16 / bf16) for callers that convert
+// them later (one vector load; AMD global memory accepts unaligned vector
+// accesses).
 template <int DT>
-__device__ __forceinline__ void load4_elems_unaligned(uint64_t addr, float* out) {
+__device__ __forceinline__ void load4_raw_unaligned(uint64_t addr, uint32_t* out) {
   if constexpr (DT == kF32) {
     typedef u32x4 v_t __attribute__((aligned(4)));
     const v_t w = *(const v_t __attribute__((address_space(1)))*)addr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+    for (int i = 0; i < 4; ++i) out[i] = w[i];
   } else {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     typedef u32x2 v_t __attribute__((aligned(2)));
     const v_t w = *(const v_t __attribute__((address_space(1)))*)addr;
-    unpack_word<DT>(w[0], out);
-    unpack_word<DT>(w[1], out + 2);
+    out[0] = w[0];
+    out[1] = w[1];
   }
 }
 
