@@ -107,16 +107,18 @@ def as_f64(a, dtype):
 
 
 class Versions:
-    """version[b][pos]: how many times position pos of item b was re-drawn."""
+    """version[b][pos]: how many times position pos of item b was re-drawn,
+    for positions base .. base + n - 1."""
 
-    def __init__(self, B: int, n: int = 1 << 16):
+    def __init__(self, B: int, n: int = 1 << 16, base: int = 0):
         self.v = np.zeros((B, n), dtype=np.int64)
+        self.base = base
 
     def of(self, b: int, pos):
-        return self.v[b, np.asarray(pos)]
+        return self.v[b, np.asarray(pos) - self.base]
 
     def bump(self, b: int, pos):
-        self.v[b, np.asarray(pos)] += 1
+        self.v[b, np.asarray(pos) - self.base] += 1
 
 
 def layout_rows(cfg: Cfg, syn: synth.Synth, b: int, T: int, vers: Versions,

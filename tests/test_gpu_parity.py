@@ -326,6 +326,26 @@ def test_bias_rows_shorter_than_a_load_group():
     say(f"  worst scaled error {run.worst:.3g}")
 
 
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16], ids=["f32", "bf16"])
+def test_positions_near_int32_limit(dtype):
+    """Lengths up to 2^31 - 1 (seqlens_k near the int32 limit, the planner's
+    division at the top of its range): decode, short multi-token and chunked
+    steps, with compactions, from caches holding the contract layout."""
+    cfg = Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=38, dtype=dtype, softcap=20.0)
+    syn = cfg.synth()
+    top = 2**31 - 1
+    vers = Versions(cfg.B, n=4096, base=top - 4000)
+    P0 = np.array([top - 60, top - 41])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S in [1, 2, 1, 17, 1, 3, 1, 9, 1, 1]:
+        run.step(P, S, total=int((P + S).max()))
+        P = P + S
+    assert int(P.max()) <= top
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
 def test_chunk_key_splits_long_window():
     """Few (item, KV head) slices and a long window: the chunk kernel splits
     the key band across workgroups and a merge kernel combines them."""
