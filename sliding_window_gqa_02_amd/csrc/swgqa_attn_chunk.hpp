@@ -439,8 +439,9 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
         sc[kt][r] = x;
         smax = fmaxf(smax, x);
       }
-    smax = fmaxf(smax, __shfl_xor(smax, 16, kWave));
-    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+    auto fmax_op = [](float x, float y) { return fmaxf(x, y); };
+    smax = reduce_xor16(smax, fmax_op);
+    smax = reduce_xor32(smax, fmax_op);
     const float m_new = fmaxf(m_run, smax);
     const float corr = (m_run == m_new) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -568,8 +569,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   }
 
   // Sum of P over the four lane groups; write O (or the split partial).
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = reduce_xor16(l_run, add_f);
+  l_run = reduce_xor32(l_run, add_f);
   if (my_ok) {
     const int64_t row = ((int64_t)b * a.S + my_i) * a.Hq + my_h;
     if (a.nsplit == 1) {

@@ -94,8 +94,8 @@ __device__ __forceinline__ float dpp_f(float x) {
 
 // Max / sum over the lanes that share (lane % NQ): xor offsets NQ..32.
 // Offsets below 16 use DPP inside a 16-lane row (quad_perm for 1 and 2,
-// row rotations by 4 and 8, which cover the same lane classes), the rest
-// cross-row shuffles.
+// row rotations by 4 and 8, which cover the same lane classes), 16 and 32
+// row swaps between two copies (v_permlane16_swap / v_permlane32_swap).
 template <int NQ, bool MAX>
 __device__ __forceinline__ float allreduce_q(float x) {
   auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
@@ -103,8 +103,8 @@ __device__ __forceinline__ float allreduce_q(float x) {
   if constexpr (NQ <= 2) x = op(x, dpp_f<0x4E>(x));    // quad_perm [2,3,0,1]
   if constexpr (NQ <= 4) x = op(x, dpp_f<0x124>(x));   // row_ror:4
   if constexpr (NQ <= 8) x = op(x, dpp_f<0x128>(x));   // row_ror:8
-  if constexpr (NQ <= 16) x = op(x, __shfl_xor(x, 16, kWave));
-  if constexpr (NQ <= 32) x = op(x, __shfl_xor(x, 32, kWave));
+  if constexpr (NQ <= 16) x = reduce_xor16(x, op);
+  if constexpr (NQ <= 32) x = reduce_xor32(x, op);
   return x;
 }
 
@@ -712,7 +712,11 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
 #pragma unroll
     for (int t = 0; t < NQ; ++t)
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) acc[t][k] += __shfl_xor(acc[t][k], off, kWave);
+      for (int k = 0; k < EPL; ++k) {
+        if (off == 16) acc[t][k] = reduce_xor16(acc[t][k], add_f);
+        else if (off == 32) acc[t][k] = reduce_xor32(acc[t][k], add_f);
+        else acc[t][k] += __shfl_xor(acc[t][k], off, kWave);
+      }
   if (rslot == 0) {
 #pragma unroll
     for (int t = 0; t < NQ; ++t)

@@ -121,8 +121,8 @@ __device__ __forceinline__ float allreduce_q8(float x) {
   if constexpr (NQ <= 2) x = op(x, dpp_q8<0x4E>(x));    // quad_perm [2,3,0,1]
   if constexpr (NQ <= 4) x = op(x, dpp_q8<0x124>(x));   // row_ror:4
   if constexpr (NQ <= 8) x = op(x, dpp_q8<0x128>(x));   // row_ror:8
-  if constexpr (NQ <= 16) x = op(x, __shfl_xor(x, 16, kWave));
-  if constexpr (NQ <= 32) x = op(x, __shfl_xor(x, 32, kWave));
+  if constexpr (NQ <= 16) x = reduce_xor16(x, op);
+  if constexpr (NQ <= 32) x = reduce_xor32(x, op);
   return x;
 }
 
@@ -694,7 +694,11 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
 #pragma unroll
     for (int tq = 0; tq < NQ; ++tq)
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) acc[tq][k] += __shfl_xor(acc[tq][k], off, kWave);
+      for (int k = 0; k < EPL; ++k) {
+        if (off == 16) acc[tq][k] = reduce_xor16(acc[tq][k], add_f);
+        else if (off == 32) acc[tq][k] = reduce_xor32(acc[tq][k], add_f);
+        else acc[tq][k] += __shfl_xor(acc[tq][k], off, kWave);
+      }
   if (rslot == 0) {
 #pragma unroll
     for (int tq = 0; tq < NQ; ++tq)

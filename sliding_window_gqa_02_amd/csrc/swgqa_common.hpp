@@ -338,6 +338,27 @@ __device__ __forceinline__ u32x4 quant_chunk16(const void* row, int64_t c0, floa
 // seqlens_k[b] (uniform across the workgroup) through the scalar data cache:
 // the array is read-only for the whole launch, and one scalar fetch per CU
 // replaces a vector load from every wave.
+// op(x of lane l, x of lane l ^ 16) in every lane: v_permlane16_swap on two
+// copies of x exchanges rows 1 and 3 of the first with rows 0 and 2 of the
+// second, so each lane then holds its own value in one copy and its
+// partner's in the other (a VALU exchange; no LDS round trip).  Needs a
+// commutative op and every lane active.
+template <typename Op>
+__device__ __forceinline__ float reduce_xor16(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The same for lane l ^ 32 (v_permlane32_swap exchanges the upper half of
+// the first copy with the lower half of the second).
+template <typename Op>
+__device__ __forceinline__ float reduce_xor32(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float add_f(float a, float b) { return a + b; }
+
 __device__ __forceinline__ int32_t load_seqlen(const int32_t* seqlens, int b) {
   return ((const int32_t __attribute__((address_space(4)))*)seqlens)[b];
 }
