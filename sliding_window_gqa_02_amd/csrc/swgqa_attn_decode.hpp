@@ -707,16 +707,11 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
 
   // Wave result: acc summed over row slots, l over the lanes of each query.
   const float l_tot = allreduce_q<NQ, false>(l_run);
+  // (sum over the lanes that share lane % LPR: the row slots)
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1)
+  for (int t = 0; t < NQ; ++t)
 #pragma unroll
-    for (int t = 0; t < NQ; ++t)
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) {
-        if (off == 16) acc[t][k] = reduce_xor16(acc[t][k], add_f);
-        else if (off == 32) acc[t][k] = reduce_xor32(acc[t][k], add_f);
-        else acc[t][k] += __shfl_xor(acc[t][k], off, kWave);
-      }
+    for (int k = 0; k < EPL; ++k) acc[t][k] = allreduce_q<LPR, false>(acc[t][k]);
   if (rslot == 0) {
 #pragma unroll
     for (int t = 0; t < NQ; ++t)

@@ -689,16 +689,11 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
         for (int t = 0; t < VB; ++t) s_acc[wave][r][VB * lane + t] = o[t][r];
     }
   } else {
+  // (sum over the lanes that share lane % LPR: the row slots)
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1)
+  for (int tq = 0; tq < NQ; ++tq)
 #pragma unroll
-    for (int tq = 0; tq < NQ; ++tq)
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) {
-        if (off == 16) acc[tq][k] = reduce_xor16(acc[tq][k], add_f);
-        else if (off == 32) acc[tq][k] = reduce_xor32(acc[tq][k], add_f);
-        else acc[tq][k] += __shfl_xor(acc[tq][k], off, kWave);
-      }
+    for (int k = 0; k < EPL; ++k) acc[tq][k] = allreduce_q8<LPR, false>(acc[tq][k]);
   if (rslot == 0) {
 #pragma unroll
     for (int tq = 0; tq < NQ; ++tq)
