@@ -32,6 +32,8 @@ namespace swgqa {
 namespace {
 
 constexpr int kTailThreads = 256;
+constexpr int kMergeGroup = 8;  // key splits whose partials are loaded together
+constexpr int kCopyUnroll = 4;  // words per thread whose loads are issued together
 
 // Column parts per row: the workgroups of one (item, KV head, K|V) slice
 // each move a disjoint set of 16-byte words of every row, so they need no
@@ -51,20 +53,41 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t bl
   const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (pl.ok) {
+    // Splits in groups of kMergeGroup whose loads are all issued before any
+    // is used (one memory round trip per group, not per split); indices past
+    // the last split repeat it and are not summed.
     const int64_t r0 = (int64_t)row * a.nsplit;
+    const int ns = a.nsplit;
+    const float2* ml2 = (const float2*)a.ml;
     float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ml[(r0 + s) * 2]);
+    for (int s0 = 0; s0 < ns; s0 += kMergeGroup) {
+      float2 v[kMergeGroup];
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) v[j] = ml2[r0 + min(s0 + j, ns - 1)];
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) M = fmaxf(M, v[j].x);
+    }
     float L = 0.0f;
     float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.ml[(r0 + s) * 2];
-      const float c = (ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      L += a.ml[(r0 + s) * 2 + 1] * c;
-      const float4 p = *(const float4*)(a.opart + (r0 + s) * D + d);
-      A[0] += p.x * c;
-      A[1] += p.y * c;
-      A[2] += p.z * c;
-      A[3] += p.w * c;
+    for (int s0 = 0; s0 < ns; s0 += kMergeGroup) {
+      float2 v[kMergeGroup];
+      float4 p[kMergeGroup];
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        const int64_t s = r0 + min(s0 + j, ns - 1);
+        v[j] = ml2[s];
+        p[j] = *(const float4*)(a.opart + s * D + d);
+      }
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) {
+        const bool in = s0 + j < ns;
+        const float c = (v[j].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(v[j].x - M);
+        L = in ? L + v[j].y * c : L;
+        A[0] = in ? A[0] + p[j].x * c : A[0];
+        A[1] = in ? A[1] + p[j].y * c : A[1];
+        A[2] = in ? A[2] + p[j].z * c : A[2];
+        A[3] = in ? A[3] + p[j].w * c : A[3];
+      }
     }
     const float c = fold_sink<DT>(a.sink, a.smooth, (int)(row % (uint32_t)a.Hq), M, L);
 #pragma unroll
@@ -113,10 +136,20 @@ __device__ __forceinline__ void writeback_part(const CopyArgs& a, uint32_t idx) 
     if (shared) {
       move_rows_in_place(dst, nullptr, w16, wlog, pl.shift, pl.kept, tid, kTailThreads);
     } else {
+      // separate buffers: loads of kCopyUnroll words issued together
       const int64_t nw = pl.kept * wn;
-      for (int64_t i = tid; i < nw; i += kTailThreads) {
-        const int64_t r = i >> wlog, w = i & (wn - 1);
-        dst[r * w16 + w] = src[(pl.shift + r) * w16 + w];
+      for (int64_t i0 = tid; i0 < nw; i0 += kCopyUnroll * kTailThreads) {
+        u32x4 x[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int64_t i = min(i0 + (int64_t)u * kTailThreads, nw - 1);
+          x[u] = src[(pl.shift + (i >> wlog)) * w16 + (i & (wn - 1))];
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int64_t i = i0 + (int64_t)u * kTailThreads;
+          if (i < nw) dst[(i >> wlog) * w16 + (i & (wn - 1))] = x[u];
+        }
       }
     }
   }
