@@ -515,6 +515,8 @@ Q8 = [
     Cfg(B=1, Hq=2, Hkv=1, D=16, C=12, W=9, seed=65, kv_int8=True, smooth=True),
     Cfg(B=2, Hq=8, Hkv=2, D=64, C=40, W=33, seed=66, dtype=synth.BF16, kv_int8=True,
         rotary=0),
+    Cfg(B=3, Hq=8, Hkv=2, D=128, C=90, W=70, seed=67, dtype=synth.F16, softcap=40.0,
+        kv_int8=True, k_scale=0.03, v_scale=0.05),
 ]
 
 
