@@ -29,7 +29,8 @@ def build(force: bool = True, sanitize: bool = False, out: str | None = None) ->
         cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp",
                "-Wall", "-Wextra"]
         if sanitize:
-            cmd += ["-fsanitize=address,undefined", "-fno-omit-frame-pointer"]
+            cmd += ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                    "-fno-omit-frame-pointer", "-g"]
         tmp = target + ".tmp%d" % os.getpid()
         subprocess.check_call(cmd + ["-o", tmp, _SRC])
         os.replace(tmp, target)
@@ -62,11 +63,14 @@ class Params(ctypes.Structure):
 
 
 def lib():
+    """The loaded oracle library: libswgqa_oracle.so next to this file, or
+    the build named by SWGQA_ORACLE_LIB (e.g. one built with sanitize=True)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("SWGQA_ORACLE_LIB", _LIB)
+        if not os.path.exists(path):
+            build(force=False, out=path)
+        L = ctypes.CDLL(path)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         L.swgqa_oracle_resident_length.restype = i64
         L.swgqa_oracle_resident_length.argtypes = [i64, i64, i64]

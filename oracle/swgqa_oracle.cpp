@@ -533,7 +533,7 @@ int swgqa_oracle_forward(const swgqa_oracle_params* p, const void* query,
   //    PR #34226 with past = P, intersected with the local window).
 #ifdef _OPENMP
   const int nth = g_threads > 0 ? g_threads : omp_get_max_threads();
-#pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nth)
+#pragma omp parallel for collapse(2) schedule(dynamic) num_threads(nth) reduction(| : broken)
 #endif
   for (int64_t b = 0; b < B; ++b) {
     for (int64_t h = 0; h < Hq; ++h) {

@@ -735,6 +735,163 @@ def test_p13_rotary_is_complex_rotation():
     assert np.array_equal(Vr[0, :, :S].transpose(1, 0, 2), v.reshape(S, cfg.Hkv, cfg.D))
 
 
+def _decode_bits(a, dtype):
+    """Element storage -> float32 values (exact for every element type)."""
+    a = np.asarray(a)
+    if dtype == synth.F32:
+        return a.astype(np.float32)
+    if dtype == synth.F16:
+        return a.view(np.float16).astype(np.float32)
+    return (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _round_bits(x32, dtype):
+    """float32 values -> element storage, nearest-even: numpy's IEEE cast for
+    fp16, torch's cast for bf16 (neither is the oracle's encoder)."""
+    import torch
+    x32 = np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == synth.F32:
+        return x32
+    if dtype == synth.F16:
+        return x32.astype(np.float16).view(np.uint16)
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _rne_exact(x64, dtype):
+    """Values rounded once, nearest-even, from float64 straight to the
+    element type (no binary32 step): the alternative reading a pin must tell
+    apart.  frexp / ldexp / rint arithmetic, written for this test only."""
+    p, emin = {synth.F32: (24, -126), synth.F16: (11, -14), synth.BF16: (8, -126)}[dtype]
+    ax = np.abs(x64)
+    _, e = np.frexp(ax)
+    q = np.maximum(e - 1, emin) - (p - 1)
+    r = np.ldexp(np.rint(np.ldexp(ax, -q)), q)
+    return _round_bits(np.where(x64 < 0, -r, r).astype(np.float32), dtype)
+
+
+def _numpy_rotary(x, cos, sin, pos, dtype, interleaved, direct=False):
+    """(B, S, H, D) storage rotated pair by pair: each product, the difference
+    and the sum rounded to binary32 (numpy float32 ufuncs, one rounding per
+    operation), the result to the element type.  direct=True instead forms
+    each component exactly (float64 holds products of two binary32 values)
+    and rounds it once to the element type -- a fused multiply-add for fp32,
+    no binary32 step for fp16 / bf16."""
+    xf = _decode_bits(x, dtype)
+    c = _decode_bits(cos, dtype)[pos][:, :, None, :]
+    s = _decode_bits(sin, dtype)[pos][:, :, None, :]
+    half = xf.shape[-1] // 2
+    ia = np.arange(0, 2 * half, 2) if interleaved else np.arange(half)
+    ib = ia + 1 if interleaved else ia + half
+    a, b = xf[..., ia], xf[..., ib]
+    if direct:
+        a64, b64, c64, s64 = (t.astype(np.float64) for t in (a, b, c, s))
+        out = np.empty(xf.shape, np.float64)
+        out[...] = xf
+        out[..., ia] = a64 * c64 - b64 * s64
+        out[..., ib] = b64 * c64 + a64 * s64
+        return _rne_exact(out, dtype)
+    ra = np.float32(a * c) - np.float32(b * s)
+    rb = np.float32(b * c) + np.float32(a * s)
+    out = xf.copy()
+    out[..., ia] = ra
+    out[..., ib] = rb
+    return _round_bits(out, dtype)
+
+
+def _hard_fp16_rotations(n_want=24, seed=1361):
+    """fp16 quadruples (a, b, c, s) where one rotated component rounds
+    differently through binary32 than straight from the exact value (about 2
+    in 10^5 random draws; products of fp16 values are exact in binary32, so
+    only the sum or difference is rounded there)."""
+    rng = np.random.default_rng(seed)
+    found = []
+    while len(found) < n_want:
+        n = 1 << 20
+        ab = synth.to_storage(rng.normal(size=(n, 2)).astype(np.float32), synth.F16)
+        ang = rng.uniform(0.0, 100.0, size=n)
+        c = synth.to_storage(np.cos(ang), synth.F16)
+        s = synth.to_storage(np.sin(ang), synth.F16)
+        x = ab.reshape(1, n, 1, 2)
+        pos = np.arange(n)[None, :]
+        per = _numpy_rotary(x, c[:, None], s[:, None], pos, synth.F16, 0)
+        alt = _numpy_rotary(x, c[:, None], s[:, None], pos, synth.F16, 0, direct=True)
+        hit = np.nonzero((per != alt).any(-1)[0, :, 0])[0]
+        found += [(ab[i, 0], ab[i, 1], c[i], s[i]) for i in hit]
+    return np.array(found[:n_want], dtype=np.uint16)
+
+
+def _check_rotary_step(cfg, S, q, k, v, K, V, seq, cos, sin, pos, interleaved):
+    """One prefill step through the oracle with rotary: stored keys and (via
+    an un-rotated step fed the rotated rows) outputs against numpy's per-
+    operation binary32 rotation.  Returns numpy's rotated keys."""
+    dtype = cfg.dtype
+    explicit = pos if not np.array_equal(pos, np.broadcast_to(np.arange(S), pos.shape)) else None
+    st, out, Kr, Vr = _rope_step(cfg, S, q, k, v, K, V, seq, cos, sin,
+                                 interleaved=interleaved, pos_ids=explicit)
+    assert st == 0
+    k4 = k.reshape(cfg.B, S, cfg.Hkv, cfg.D)
+    want_k = _numpy_rotary(k4, cos, sin, pos, dtype, interleaved)
+    got_k = np.ascontiguousarray(Kr[:, :, :S].transpose(0, 2, 1, 3))
+    assert np.array_equal(got_k.view(np.uint8), want_k.view(np.uint8))
+    assert np.array_equal(Vr[:, :, :S].transpose(0, 2, 1, 3), v.reshape(k4.shape))
+    q4 = q.reshape(cfg.B, S, cfg.Hq, cfg.D)
+    want_q = _numpy_rotary(q4, cos, sin, pos, dtype, interleaved)
+    K0, V0 = K.copy(), V.copy()
+    st0, out0, _ = oracle.forward(cfg.params(S, S), want_q.reshape(q.shape),
+                                  want_k.reshape(k.shape), v, K0, V0, seq)
+    assert st0 == 0 and np.array_equal(out.view(np.uint8), out0.view(np.uint8))
+    return k4, want_k
+
+
+@pytest.mark.parametrize("interleaved", [0, 1])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.F16, synth.BF16])
+def test_p13_rotary_rounding_is_binary32_per_operation(dtype, interleaved):
+    """Stored keys equal, bit for bit, numpy's float32 evaluation of
+    (a c - b s, b c + a s) one operation at a time, rounded to the element
+    type; the query rotation likewise (an un-rotated step fed numpy's rotated
+    rows returns bit-identical outputs).  Default and explicit (left-padded)
+    positions.  Discrimination on these inputs: for fp32 a fused multiply-add
+    (exact component, one rounding) differs; for fp16 rounding the exact
+    component straight to fp16 differs on searched inputs; for bf16 no input
+    separates the two (products of 8-bit significands and their sums stay
+    exact in binary32 or round away from bf16 midpoints), so the per-
+    operation result must equal the exact component rounded once."""
+    cfg = Cfg(B=2, Hq=4, Hkv=2, D=64, C=300, W=300, seed=136, dtype=dtype)
+    S = 160
+    q, k, v, K, V = _rope_inputs(cfg, S, [0, 0])
+    if dtype != synth.F32:
+        K, V = K.astype(np.uint16), V.astype(np.uint16)
+    cos, sin = synth.rotary_tables(512, cfg.D, dtype, base=50.0)
+    seq = np.array([S - 1, S - 1], np.int32)
+    told_apart = False
+    for pos in (np.stack([np.arange(S), np.arange(S)]),
+                np.stack([np.arange(S) + 3, np.arange(S) + 211])):
+        k4, want_k = _check_rotary_step(cfg, S, q, k, v, K, V, seq, cos, sin, pos, interleaved)
+        alt = _numpy_rotary(k4, cos, sin, pos, dtype, interleaved, direct=True)
+        if dtype == synth.BF16:
+            assert np.array_equal(alt, want_k)
+        told_apart |= not np.array_equal(alt, want_k)
+    if dtype == synth.F16:
+        # searched inputs: pair 0 of new key row i and table row i
+        hard = _hard_fp16_rotations()
+        n = len(hard)
+        hc = Cfg(B=1, Hq=1, Hkv=1, D=8, C=n, W=n, seed=137, dtype=dtype)
+        q, k, v, K, V = _rope_inputs(hc, n, [0])
+        K, V = K.astype(np.uint16), V.astype(np.uint16)
+        k = k.reshape(1, n, 8).copy()
+        ia, ib = (0, 1) if interleaved else (0, 4)
+        k[0, :, ia], k[0, :, ib] = hard[:, 0], hard[:, 1]
+        hcos, hsin = synth.rotary_tables(n, 8, dtype)
+        hcos, hsin = hcos.copy(), hsin.copy()
+        hcos[:, 0], hsin[:, 0] = hard[:, 2], hard[:, 3]
+        pos = np.arange(n)[None, :]
+        k4, want_k = _check_rotary_step(hc, n, q, k.reshape(1, n * 1 * 8), v, K, V,
+                                        np.array([n - 1], np.int32), hcos, hsin, pos, interleaved)
+        alt = _numpy_rotary(k4, hcos, hsin, pos, dtype, interleaved, direct=True)
+        told_apart |= not np.array_equal(alt, want_k)
+    assert told_apart or dtype == synth.BF16, "these inputs cannot tell the readings apart"
+
+
 def test_p13_interleaved_is_a_permutation_of_halves():
     """Interleaved pairs (2k, 2k+1) on a row equal half pairs (k, k + D/2) on
     the row with its even elements first and odd elements second."""
