@@ -60,7 +60,8 @@
  *    step attends to every key and value row in that dequantized form, new
  *    rows included (the Investigation Report, section 1.1, names k_scale /
  *    v_scale and a cache type only; this is the plainest reading).  Head
- *    sizes below 16 return SWGQA_ERR_UNSUPPORTED with these caches;
+ *    sizes below 16 return SWGQA_ERR_UNSUPPORTED with these caches, and so
+ *    do steps of more than 16 tokens with fp32 at head size 256;
  *  - query head h reads KV head h / (num_heads / kv_num_heads);
  *  - present rows [0, L(T)) receive the newest L(T) rows of that
  *    concatenation (byte copies); rows [L(T), C) are unspecified.

@@ -81,6 +81,10 @@ swgqa_status validate(const swgqa_params* p) {
       return SWGQA_ERR_ARG;
     // int8 rows of whole 16-byte chunks
     if (p->head_size < 16) return SWGQA_ERR_UNSUPPORTED;
+    // steps longer than the 8-bit staged kernel holds need the matrix-core
+    // kernel, whose rows are at most 512 bytes (not fp32 at head size 256)
+    if (p->sequence_length > kQ8MaxNewRows && !chunk_kernel_supports(p->dtype, p->head_size))
+      return SWGQA_ERR_UNSUPPORTED;
   }
   return SWGQA_OK;
 }

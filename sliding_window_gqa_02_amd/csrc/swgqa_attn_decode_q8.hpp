@@ -47,7 +47,6 @@ namespace swgqa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kQ8MaxNewRows = 16;  // S < 16 on this path
 
 // Stages of K/V loads in flight per wave.
 #ifndef SWGQA_Q8_DEPTH
@@ -745,6 +744,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
 template <int DT, int D, int NQ, int CT>
 hipError_t launch_q8_nq(const AttnArgs& a, hipStream_t st) {
   if constexpr (Q8Shape<D, NQ>::ok) {
+    // the new rows' codes live in LDS arrays of kQ8MaxNewRows rows
+    if (a.S < 1 || a.S > kQ8MaxNewRows) return hipErrorInvalidValue;
     const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
     if (a.waves == 8)
       attn_decode_q8_kernel<DT, D, NQ, 8, CT><<<grid, 8 * kWave, 0, st>>>(a);

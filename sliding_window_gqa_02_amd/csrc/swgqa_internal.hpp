@@ -120,6 +120,9 @@ hipError_t launch_attn_decode(int dtype, int D, int nq, const AttnArgs& a,
 // Staged decode kernel for an int8 cache (swgqa_attn_decode_q8.hip): head
 // sizes 16..256, query tiles of 2 or 4 pairs, S < 16.
 bool decode_q8_supports(int D, int nq);
+// New rows per step the 8-bit staged kernel holds in LDS: the quantized new
+// rows of a step of at most this many tokens.
+constexpr int kQ8MaxNewRows = 16;
 int decode_q8_stage_rows(int D, int nq);
 hipError_t launch_attn_decode_q8(int dtype, int D, int nq, const AttnArgs& a,
                                  hipStream_t stream);

@@ -122,3 +122,29 @@ def test_host_validation_without_gpu():
     assert lib.swgqa_plan(ctypes.byref(sw.make_params(1, 1, 3, 2, 8, 6, 4, 8)), ptr, ptr, None) == sw.ERR_ARG
     for s in range(6):
         assert sw.status_string(s)
+
+
+def test_eight_bit_cache_step_limits():
+    """8-bit caches: steps of up to 16 tokens run on the 8-bit staged kernel
+    (its LDS holds 16 quantized new rows); longer steps need the matrix-core
+    kernel, whose rows are at most 512 bytes, so fp32 at head size 256 with
+    more than 16 tokens is rejected before any launch -- for both code
+    types; fp16 / bf16 at head size 256 take the matrix-core kernel."""
+    lib = sw.load()
+    buf = np.zeros(1 << 12, np.float32)
+    ptr = buf.ctypes.data
+    seq = np.zeros(1, np.int32).ctypes.data
+    for ct in (1, 2):
+        def params(S, dtype, D=256):
+            return sw.make_params(1, S, 4, 2, D, 64, 32, 64, dtype, kv_cache_type=ct,
+                                  k_scale=0.05, v_scale=0.04)
+        assert sw.workspace_size(params(16, sw.F32)) > 0
+        for S in (17, 32, 64):
+            p = params(S, sw.F32)
+            assert sw.workspace_size(p) == 0
+            assert lib.swgqa_forward(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, seq, None, None,
+                                     None, None, None, ptr, ptr, ptr, ptr, 1 << 14,
+                                     None) == sw.ERR_UNSUPPORTED
+            assert sw.workspace_size(params(S, sw.F16)) > 0
+            assert sw.workspace_size(params(S, sw.BF16)) > 0
+            assert sw.workspace_size(params(S, sw.F32, D=128)) > 0
