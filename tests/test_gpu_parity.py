@@ -197,6 +197,98 @@ def test_small_slack_400_decodes():
     say(f"  worst scaled error {run.worst:.3g}")
 
 
+# The capacity sweep's tightest points at the pages' decode shape: C = W
+# (gap 1, a compaction on every decode step) and C = W + 4 (gap 5), after a
+# 2048-token prompt, 300 decodes, every step compared ("[CPU] Add windowed kv
+# cache for GQA", Performance Results: decode latency against capacity).
+@pytest.mark.parametrize("slack", [0, 4])
+def test_pages_shape_tight_capacity(slack):
+    cfg = Cfg(B=1, Hq=64, Hkv=8, D=64, C=128 + slack, W=128, seed=1010 + slack, scale=0.125)
+    say(f"pages' shape, C = W + {slack}, prompt 2048 + 300 decodes")
+    run = Lockstep(cfg, vers=Versions(1, n=2400))
+    run.step([0], 2048)
+    events = 0
+    for T in range(2049, 2349):
+        _, _, plan = run.step([T - 1], 1, check_regen=(T % 7 == 0))
+        events += int(plan[0, 5] > 0)
+    assert events == (300 if slack == 0 else 60)
+    say(f"  worst scaled error {run.worst:.3g}, {events} compactions")
+
+
+# Rows wider than 256 bytes: fp32 at head size 128 and 256, bf16 at 256.
+# Steps of few query rows go to the generic split kernel (whole slices, and
+# key splits merged by the step tail over a long window); fp32 D = 128 and
+# bf16 D = 256 multi-token steps take the matrix-core kernel's 512-byte rows;
+# fp32 D = 256 multi-token steps stay on the split kernel.
+WIDE = [
+    Cfg(B=2, Hq=4, Hkv=2, D=128, C=40, W=33, seed=141, dtype=synth.F32),
+    Cfg(B=2, Hq=8, Hkv=2, D=256, C=30, W=24, seed=142, dtype=synth.F32, softcap=20.0),
+    Cfg(B=2, Hq=4, Hkv=1, D=256, C=36, W=30, seed=143, dtype=synth.BF16, sink_std=1.0),
+    Cfg(B=3, Hq=12, Hkv=3, D=128, C=70, W=64, seed=144, dtype=synth.F32, rotary=1),
+    Cfg(B=1, Hq=8, Hkv=8, D=256, C=20, W=17, seed=145, dtype=synth.BF16, softcap=30.0,
+        rotary=0),
+]
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("cfg", WIDE, ids=lambda c: f"D{c.D}t{c.dtype}g{c.Hq // c.Hkv}")
+def test_wide_rows_random_steps(cfg, mode):
+    say(f"wide rows {cfg} mode={mode}")
+    rng = np.random.default_rng(cfg.seed)
+    run = Lockstep(cfg, mode=mode)
+    T = 0
+    for S in [1, 3, 1, 16, 1, 2, 33, 1, 17, int(rng.integers(1, 2 * cfg.C + 2)), 1, 5,
+              2 * cfg.C + 1, 1]:
+        run.step([T] * cfg.B, S)
+        T += S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("dtype,D", [(synth.F32, 128), (synth.F32, 256), (synth.BF16, 256)],
+                         ids=["f32_128", "f32_256", "bf16_256"])
+def test_wide_rows_key_splits_with_bias(dtype, D, mode):
+    """A long window over one slice: key splits on the split kernel (short
+    steps) or the matrix-core kernel (fp32 D=128 and bf16 D=256 chunks),
+    merged by the step tail; a NaN bias outside the visible band."""
+    cfg = Cfg(B=1, Hq=4, Hkv=1, D=D, C=1600, W=1500, seed=146 + D, dtype=dtype, softcap=40.0)
+    syn = cfg.synth()
+    vers = Versions(1)
+    P0 = np.array([1700])
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, mode=mode, K=K, V=V, vers=vers)
+    P = P0.copy()
+    for S, with_bias in [(1, False), (3, True), (40, True), (1, True), (16, False)]:
+        total = int((P + S).max())
+        bias = _bias_nan_outside(cfg, syn, P, S, total) if with_bias else None
+        run.step(P, S, bias=bias, total=total)
+        P = P + S
+    say(f"  worst scaled error {run.worst:.3g}")
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("code", ["int8", "fp8"])
+def test_eight_bit_cache_fp32_head_size_256(code, mode):
+    """fp32 queries at head size 256 over an 8-bit cache: every step of up
+    to 16 tokens on the 8-bit staged kernel (16 included); longer steps are
+    refused before any launch."""
+    import sliding_window_gqa_02_amd as sw
+    cfg = Cfg(B=2, Hq=4, Hkv=2, D=256, C=40, W=33, seed=148, kv_int8=code == "int8",
+              kv_fp8=code == "fp8", k_scale=0.03, v_scale=0.02)
+    run = Lockstep(cfg, mode=mode)
+    T = 0
+    for S in [16, 1, 3, 1, 15, 1, 16, 2, 1, 8, 16, 1]:
+        run.step([T] * cfg.B, S)
+        T += S
+    say(f"  worst scaled error {run.worst:.3g}")
+    t = torch.zeros(1 << 16, dtype=torch.float32, device="cuda:0")
+    ws = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+    seq = torch.full((2,), T + 16, dtype=torch.int32, device="cuda:0")
+    p = sw.make_params(2, 17, 4, 2, 256, 40, 33, T + 17, synth.F32, **cfg.cache_params())
+    assert sw.forward_status(p, t, t, t, t, t, seq, None, t, t, t, ws) == sw.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+
+
 # One workspace, sized for a long-window key-split step (partials), then
 # reused for decode steps of a few-slice shape whose query tiles share each
 # slice and compact through the per-slice counters: the counters sit in the
