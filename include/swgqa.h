@@ -102,7 +102,9 @@ typedef enum {
   SWGQA_ERR_UNSUPPORTED = 2,  /* valid but not built: head_size, dtype */
   SWGQA_ERR_ALIAS = 3,        /* past and present overlap partially */
   SWGQA_ERR_DEVICE_INPUT = 4, /* some seqlens_k[b] out of range (device) */
-  SWGQA_ERR_HIP = 5           /* a HIP runtime call failed */
+  SWGQA_ERR_HIP = 5,          /* a HIP runtime call failed */
+  SWGQA_ERR_SCRATCH = 6       /* swgqa_forward_noalloc: the step needs more
+                                 workspace than the static scratch holds */
 } swgqa_status;
 
 /* Step parameters.  All sizes are element counts. */
@@ -180,6 +182,33 @@ swgqa_status swgqa_forward(const swgqa_params* params, const void* query,
                            void* present_key, void* present_value,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* swgqa_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same step, same kernels, same results
+ * as swgqa_forward; its workspace is a static 32 MiB device array inside the
+ * library, one per GPU, held until the process ends.  Nothing is allocated.
+ *  - Parameters whose swgqa_workspace_size exceeds 32 MiB return
+ *    SWGQA_ERR_SCRATCH before anything is enqueued (every workload here
+ *    needs at most about 17 MB).
+ *  - device_status: NULL, or a 4-byte aligned device word of the caller's
+ *    into which device-detected item errors OR the bit that
+ *    swgqa_device_status reports (sticky: the caller clears it); with NULL
+ *    such errors are visible only as zero-filled outputs.
+ *  - The first call on a device looks up the array's address and clears its
+ *    counters with a fill kernel on `stream`; make that first call outside
+ *    graph capture.
+ *  - All calls on one GPU share its array: calls that overlap in time on one
+ *    GPU (other streams, other threads) race and must not be issued. */
+swgqa_status swgqa_forward_noalloc(const swgqa_params* params, const void* query,
+                                   const void* key, const void* value,
+                                   const void* past_key, const void* past_value,
+                                   const int32_t* seqlens_k,
+                                   const void* attention_bias, const void* head_sink,
+                                   const void* cos_cache, const void* sin_cache,
+                                   const int64_t* position_ids, void* output,
+                                   void* present_key, void* present_value,
+                                   uint32_t* device_status, void* stream);
 
 /* Enqueues the planner alone: writes B plan records to device memory
  * `plan_out` (B * 64 bytes).  For tests of the resident-range planner. */

@@ -16,11 +16,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libswgqa.so")
 
 F32, F16, BF16 = 0, 1, 2
-OK, ERR_ARG, ERR_UNSUPPORTED, ERR_ALIAS, ERR_DEVICE_INPUT, ERR_HIP = range(6)
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_ALIAS, ERR_DEVICE_INPUT, ERR_HIP, ERR_SCRATCH = range(7)
 
 # Symbols declared in include/swgqa.h.
 EXPORTS = (
-    "swgqa_workspace_size", "swgqa_workspace_init", "swgqa_forward", "swgqa_plan",
+    "swgqa_workspace_size", "swgqa_workspace_init", "swgqa_forward", "swgqa_forward_noalloc",
+    "swgqa_plan",
     "swgqa_resident_length", "swgqa_rollback_exact", "swgqa_device_status",
     "swgqa_status_string",
 )
@@ -90,6 +91,8 @@ def load(path: str = LIB_PATH):
     L.swgqa_workspace_init.argtypes = [vp, sz, vp]
     L.swgqa_forward.restype = ctypes.c_int
     L.swgqa_forward.argtypes = [P] + [vp] * 15 + [sz, vp]
+    L.swgqa_forward_noalloc.restype = ctypes.c_int
+    L.swgqa_forward_noalloc.argtypes = [P] + [vp] * 16
     L.swgqa_plan.restype = ctypes.c_int
     L.swgqa_plan.argtypes = [P, vp, vp, vp]
     L.swgqa_resident_length.restype = i64
@@ -168,6 +171,21 @@ def forward_status(p: Params, query, key, value, past_key, past_value, seqlens_k
         _ptr(past_value), _ptr(seqlens_k), _ptr(attention_bias), _ptr(head_sink),
         _ptr(cos_cache), _ptr(sin_cache), _ptr(position_ids),
         _ptr(output), _ptr(present_key), _ptr(present_value), _ptr(workspace), nbytes,
+        _stream(stream))
+
+
+def forward_noalloc_status(p: Params, query, key, value, past_key, past_value, seqlens_k,
+                           attention_bias, output, present_key, present_value,
+                           device_status=None, stream=None, head_sink=None, cos_cache=None,
+                           sin_cache=None, position_ids=None) -> int:
+    """One step through swgqa_forward_noalloc (the library's static scratch
+    as workspace); returns the status code.  device_status: None or an int32
+    device tensor of one element receiving device item errors."""
+    return load().swgqa_forward_noalloc(
+        ctypes.byref(p), _ptr(query), _ptr(key), _ptr(value), _ptr(past_key),
+        _ptr(past_value), _ptr(seqlens_k), _ptr(attention_bias), _ptr(head_sink),
+        _ptr(cos_cache), _ptr(sin_cache), _ptr(position_ids),
+        _ptr(output), _ptr(present_key), _ptr(present_value), _ptr(device_status),
         _stream(stream))
 
 

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
@@ -251,32 +252,35 @@ bool ranges_partially_overlap(const void* a, const void* b, size_t n) {
   return x < y + n && y < x + n;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t swgqa_workspace_size(const swgqa_params* p) {
+size_t workspace_bytes_for(const swgqa_params* p) {
   if (validate(p) != SWGQA_OK) return 0;
   const SplitPlan s = plan_split(p);
   return rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s)), s).end;
 }
 
-swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-  if (!workspace || workspace_bytes < kHeaderBytes) return SWGQA_ERR_ARG;
-  if (launch_zero_words((uint32_t*)workspace, workspace_bytes / 4, (hipStream_t)stream) !=
-      hipSuccess)
-    return SWGQA_ERR_HIP;
-  return SWGQA_OK;
-}
+// Workspace of swgqa_forward_noalloc: 32 MiB, enough for every workload
+// measured here (the largest, multi-token steps with key splits, needs
+// about 17 MB).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
 
-swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void* key,
-                           const void* value, const void* past_key,
-                           const void* past_value, const int32_t* seqlens_k,
-                           const void* attention_bias, const void* head_sink,
-                           const void* cos_cache, const void* sin_cache,
-                           const int64_t* position_ids, void* output,
-                           void* present_key, void* present_value, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // namespace
+
+// The workspace of swgqa_forward_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never uses this name as an
+// address; it uses what hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// One step with a given workspace; device item errors set bits in
+// *status_word (the workspace's first word, or a word of the caller's).
+swgqa_status forward_impl(const swgqa_params* p, const void* query, const void* key,
+                          const void* value, const void* past_key, const void* past_value,
+                          const int32_t* seqlens_k, const void* attention_bias,
+                          const void* head_sink, const void* cos_cache, const void* sin_cache,
+                          const int64_t* position_ids, void* output, void* present_key,
+                          void* present_value, void* workspace, size_t workspace_bytes,
+                          uint32_t* status_word, void* stream) {
   const swgqa_status v = validate(p);
   if (v != SWGQA_OK) return v;
   if (p->batch_size == 0) return SWGQA_OK;
@@ -363,7 +367,7 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   a.sink = head_sink;
   a.smooth = p->smooth_softmax;
   a.out = output;
-  a.status = (uint32_t*)workspace;
+  a.status = status_word;
   a.slice_counters = (uint32_t*)((char*)workspace + kStatusBytes);
   float* part = (float*)((char*)workspace + kHeaderBytes);
   a.opart = part;
@@ -462,6 +466,81 @@ swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void*
   return SWGQA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's scratch address; on its first use on a device the
+// header (status word and slice counters, which must start at zero) is
+// cleared with a fill kernel on `st`.
+hipError_t device_scratch(void** out, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr || ((uintptr_t)ptr & 255u) != 0) return hipErrorInvalidSymbol;
+    e = launch_zero_words((uint32_t*)ptr, kHeaderBytes / 4, st);
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t swgqa_workspace_size(const swgqa_params* p) { return workspace_bytes_for(p); }
+
+swgqa_status swgqa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < kHeaderBytes) return SWGQA_ERR_ARG;
+  if (launch_zero_words((uint32_t*)workspace, workspace_bytes / 4, (hipStream_t)stream) !=
+      hipSuccess)
+    return SWGQA_ERR_HIP;
+  return SWGQA_OK;
+}
+
+swgqa_status swgqa_forward(const swgqa_params* p, const void* query, const void* key,
+                           const void* value, const void* past_key,
+                           const void* past_value, const int32_t* seqlens_k,
+                           const void* attention_bias, const void* head_sink,
+                           const void* cos_cache, const void* sin_cache,
+                           const int64_t* position_ids, void* output,
+                           void* present_key, void* present_value, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return forward_impl(p, query, key, value, past_key, past_value, seqlens_k, attention_bias,
+                      head_sink, cos_cache, sin_cache, position_ids, output, present_key,
+                      present_value, workspace, workspace_bytes, (uint32_t*)workspace, stream);
+}
+
+swgqa_status swgqa_forward_noalloc(const swgqa_params* p, const void* query, const void* key,
+                                   const void* value, const void* past_key,
+                                   const void* past_value, const int32_t* seqlens_k,
+                                   const void* attention_bias, const void* head_sink,
+                                   const void* cos_cache, const void* sin_cache,
+                                   const int64_t* position_ids, void* output,
+                                   void* present_key, void* present_value,
+                                   uint32_t* device_status, void* stream) {
+  const swgqa_status v = validate(p);
+  if (v != SWGQA_OK) return v;
+  if (p->batch_size == 0) return SWGQA_OK;
+  const size_t need = workspace_bytes_for(p);
+  if (need > kScratchBytes) return SWGQA_ERR_SCRATCH;
+  if (((uintptr_t)device_status & 3u) != 0) return SWGQA_ERR_ARG;
+  void* ws = nullptr;
+  if (device_scratch(&ws, (hipStream_t)stream) != hipSuccess) return SWGQA_ERR_HIP;
+  return forward_impl(p, query, key, value, past_key, past_value, seqlens_k, attention_bias,
+                      head_sink, cos_cache, sin_cache, position_ids, output, present_key,
+                      present_value, ws, kScratchBytes,
+                      device_status ? device_status : (uint32_t*)ws, stream);
+}
+
 swgqa_status swgqa_plan(const swgqa_params* p, const int32_t* seqlens_k,
                         swgqa_plan_entry* plan_out, void* stream) {
   const swgqa_status v = validate(p);
@@ -511,6 +590,7 @@ const char* swgqa_status_string(swgqa_status s) {
     case SWGQA_ERR_ALIAS: return "past and present buffers overlap partially";
     case SWGQA_ERR_DEVICE_INPUT: return "seqlens_k out of range for some item";
     case SWGQA_ERR_HIP: return "HIP runtime error";
+    case SWGQA_ERR_SCRATCH: return "step needs more workspace than the library's static scratch";
   }
   return "unknown status";
 }

@@ -120,7 +120,7 @@ def test_host_validation_without_gpu():
     assert call(pr, ws_bytes=need - 1) == sw.ERR_ARG
     assert call(pr, ws_bytes=need) == sw.ERR_ARG           # no cos/sin caches
     assert lib.swgqa_plan(ctypes.byref(sw.make_params(1, 1, 3, 2, 8, 6, 4, 8)), ptr, ptr, None) == sw.ERR_ARG
-    for s in range(6):
+    for s in range(7):
         assert sw.status_string(s)
 
 
@@ -148,3 +148,25 @@ def test_eight_bit_cache_step_limits():
             assert sw.workspace_size(params(S, sw.F16)) > 0
             assert sw.workspace_size(params(S, sw.BF16)) > 0
             assert sw.workspace_size(params(S, sw.F32, D=128)) > 0
+
+
+def test_noalloc_refuses_oversized_steps_without_gpu():
+    """swgqa_forward_noalloc validates and sizes the step before touching the
+    device: a step needing more than its 32 MiB scratch (rotated rows of a
+    long prefill) returns SWGQA_ERR_SCRATCH, invalid parameters their usual
+    code."""
+    lib = sw.load()
+    buf = np.zeros(1 << 12, np.float32)
+    ptr = buf.ctypes.data
+    seq = np.zeros(8, np.int32).ctypes.data
+    p = sw.make_params(8, 1024, 32, 8, 128, 2048, 1024, 1024, sw.BF16, do_rotary=1,
+                       rotary_cache_rows=2048)
+    assert sw.workspace_size(p) > 32 << 20
+
+    def call(p):
+        return lib.swgqa_forward_noalloc(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, seq, None,
+                                         None, ptr, ptr, None, ptr, ptr, ptr, None, None)
+
+    assert call(p) == sw.ERR_SCRATCH
+    assert call(sw.make_params(1, 1, 3, 2, 8, 6, 4, 8)) == sw.ERR_ARG
+    assert call(sw.make_params(0, 1, 2, 2, 8, 6, 4, 8)) == sw.OK
