@@ -326,10 +326,10 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def stored_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    readings (profiles/traffic.json), or None if absent or taken from other
-    kernel sources."""
+def stored_traffic(label: str, kernel: str):
+    """HBM bytes per launch of `kernel` in workload `label` from the committed
+    rocprofv3 counter readings (profiles/traffic.json), or None if absent or
+    taken from other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -338,19 +338,20 @@ def stored_traffic(kernel: str):
         return None
     if data.get("source_digest") != source_digest():
         return None
-    entry = data.get("kernels", {}).get(kernel)
+    entry = data.get("workloads", {}).get(label, {}).get("kernels", {}).get(kernel)
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
-def roofline(bytes_list, kernel_ms, kernel_name):
+def roofline(bytes_list, kernel_ms, kernel_name, label):
     """Achieved = algorithmic bytes per launch / the kernel's average
-    duration (one kernel per decode step)."""
+    duration (one kernel per decode step); traffic = the counter reading of
+    that kernel in workload `label`, if current."""
     algo = float(sum(b["total"] for b in bytes_list))
     per_launch = algo / len(bytes_list)
     achieved = per_launch / (kernel_ms / 1e3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 5),
-            "traffic": stored_traffic(kernel_name),
+            "traffic": stored_traffic(label, kernel_name),
             "kernel": kernel_name,
             "algorithmic_bytes_per_launch": int(per_launch),
             "avg_launch_us": round(kernel_ms * 1e3, 3)}
@@ -501,7 +502,7 @@ def loop_stats(torch, loop: DecodeLoop, snap, tokens_per_step: int, use_graph: b
     return out, step_ms, r
 
 
-def small_slack(torch, sw, steps: int = 400):
+def small_slack(torch, sw, steps: int = 400, use_graph: bool = True):
     """B=1, 64 Q / 8 KV heads x 64, fp32, W=128, C=136 (G=9): decode steps
     after a 512-token prompt, a block compaction every 9 steps."""
     wl = Workload("small_slack", B=1, Hq=64, Hkv=8, D=64, C=136, W=128, dtype=0,
@@ -512,7 +513,7 @@ def small_slack(torch, sw, steps: int = 400):
     loop = DecodeLoop(torch, sw, wl, P0, steps, K, V)
     loop.run(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    out, _, _ = loop_stats(torch, loop, snap, 1)
+    out, _, _ = loop_stats(torch, loop, snap, 1, use_graph)
     out["workload"] = ("decode after a 512-token prompt, B=1, 64 Q / 8 KV heads x 64, fp32, "
                        f"W=128, C=136 (G=9), {steps} steps")
     return out
@@ -545,12 +546,12 @@ def serving(torch, sw, kind: str, use_graph: bool, steps: int = 128):
     out["workload"] = (f"B=32 decode, 32 Q / 8 KV heads x 128, bf16 queries, {what}, W=4096, "
                        f"C=4608, softcap 50, past lengths U[4096, 32768], {steps} steps")
     out["ms_per_step"] = round(kms, 5)
-    out["roofline"] = roofline(loop.bytes_per_step(), kms, kernel)
+    out["roofline"] = roofline(loop.bytes_per_step(), kms, kernel, "serving")
     del K, V, snap, loop
     return out
 
 
-def rotary_decode(torch, sw, prompt: int, steps: int):
+def rotary_decode(torch, sw, prompt: int, steps: int, use_graph: bool = True):
     """The headline decode with rotary embedding of the query and new key
     rows (half-split pairs, default positions): what the rotary pass adds to
     a step."""
@@ -562,13 +563,14 @@ def rotary_decode(torch, sw, prompt: int, steps: int):
     loop = DecodeLoop(torch, sw, wl, P0, steps, K, V, rotary=0)
     loop.run(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    out, _, _ = loop_stats(torch, loop, snap, 1)
+    out, _, _ = loop_stats(torch, loop, snap, 1, use_graph)
     out["workload"] = (f"decode after a {prompt}-token prompt, B=1, 64 Q / 8 KV heads x 64, "
                        f"fp32, W=128, C=384, rotary on query and new keys, {steps} steps")
     return out
 
 
-def capacity_sweep(torch, sw, slacks=(0, 4, 16, 32, 128, 256, 384), steps=800):
+def capacity_sweep(torch, sw, slacks=(0, 4, 16, 32, 128, 256, 384), steps=800,
+                   use_graph: bool = True):
     """Decode step time against capacity at the pages' shape (W=128): the
     cache at T=2048 (as a 2048-token prefill leaves it), then `steps` decode
     steps, for C = W + slack.  At C = W every step compacts (127 rows per
@@ -585,7 +587,7 @@ def capacity_sweep(torch, sw, slacks=(0, 4, 16, 32, 128, 256, 384), steps=800):
         loop = DecodeLoop(torch, sw, wl, P0, steps, K, V)
         loop.run(torch.cuda.current_stream())
         torch.cuda.synchronize()
-        st, _, _ = loop_stats(torch, loop, snap, 1)
+        st, _, _ = loop_stats(torch, loop, snap, 1, use_graph)
         pt = {"capacity": C, "gap": C - 128 + 1, "step_us": st["step_us"],
               "compacting_steps": st["compacting_steps"],
               "eager_step_us_p50": st["eager_step_us_p50"],
@@ -595,7 +597,8 @@ def capacity_sweep(torch, sw, slacks=(0, 4, 16, 32, 128, 256, 384), steps=800):
         out.append(pt)
         del loop, K, V, snap
     first, last = out[0], out[-1]
-    if first["compacting_steps"] == steps and last["compacting_steps"] < steps // 10:
+    if (len(out) > 1 and first["compacting_steps"] == steps and
+            last["compacting_steps"] < steps // 10):
         extra = first["step_us"] - last["step_us"]
         moved = first["compaction_bytes_per_step"]
         res = {"extra_us_per_step_at_C_eq_W": round(extra, 3),
@@ -611,7 +614,7 @@ def _dev_args(vp, t):
     return None if t is None else vp(t.data_ptr())
 
 
-def chunked_prefill(torch, sw, C: int, nsteps: int = 32):
+def chunked_prefill(torch, sw, C: int, nsteps: int = 32, use_graph: bool = True):
     """B=4, 32 Q / 8 KV heads x 128, fp16, W=1024, capacity C, fp16
     attention_bias N(0, 0.1) of width total_sequence_length: 32-token prompt
     chunks on items whose past lengths are uniform in [1024, 4096] (matrix-
@@ -630,7 +633,7 @@ def chunked_prefill(torch, sw, C: int, nsteps: int = 32):
     loop = DecodeLoop(torch, sw, wl, P0, nsteps, K, V, S=S, bias=bias, total=total)
     loop.run(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    out, step_ms, _ = loop_stats(torch, loop, snap, 4 * S)
+    out, step_ms, _ = loop_stats(torch, loop, snap, 4 * S, use_graph)
     flops = float(np.mean(loop.flops_per_step()))
     peak = 2500.0  # dense fp16 MFMA, TFLOP/s
     out["mfma"] = {"achieved_TFLOPs": round(flops / (step_ms / 1e3) / 1e12, 3),
@@ -812,7 +815,7 @@ def verify_with_rejection(torch, sw, C: int, nverify: int = 32, use_graph: bool 
     return res
 
 
-def verify_steps(torch, sw, C: int, nsteps: int = 64):
+def verify_steps(torch, sw, C: int, nsteps: int = 64, use_graph: bool = True):
     """The verify step alone (B=4, 8 draft tokens per item, every draft
     accepted): one launch sequence per step, for its roofline."""
     import synth
@@ -830,7 +833,7 @@ def verify_steps(torch, sw, C: int, nsteps: int = 64):
     loop = DecodeLoop(torch, sw, wl, P0, nsteps, K, V, S=S, bias=bias, total=total)
     loop.run(torch.cuda.current_stream())
     torch.cuda.synchronize()
-    out, step_ms, _ = loop_stats(torch, loop, snap, 4 * S)
+    out, step_ms, _ = loop_stats(torch, loop, snap, 4 * S, use_graph)
     flops = float(np.mean(loop.flops_per_step()))
     out["mfma"] = {"achieved_TFLOPs": round(flops / (step_ms / 1e3) / 1e12, 3),
                    "peak_TFLOPs": 2500.0,
@@ -881,12 +884,16 @@ SECTIONS = ("prefill", "headline", "decode_prompts", "serving", "serving_int8", 
             "rotary", "small_slack", "chunked", "capacity", "copy", "cpu")
 
 
-def digest_counters(fetch_dir: str, write_dir: str, ref_kernel_prefix: str, ref_bytes: int):
-    """Writes profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE,
-    then WRITE_SIZE; csv output): per kernel, the mean KiB per dispatch of
-    each counter, scaled by what the same counter reads for the bench's
-    reference streaming kernel of known size, and for kernels whose dispatches
-    differ (compacting and drifting steps) the per-dispatch values too."""
+def digest_counters(label: str, fetch_dir: str, write_dir: str, ref_kernel: str,
+                    ref_bytes: int):
+    """Adds the readings of two rocprofv3 --pmc runs (FETCH_SIZE, then
+    WRITE_SIZE; csv output) of one workload to profiles/traffic.json, under
+    `label`: per kernel, HBM bytes per dispatch -- each counter scaled by
+    what it reads for the bench's reference streaming kernel of known size
+    -- as the mean for each of this library's kernels, and, where the
+    dispatches form two groups (e.g. steps that compact and steps that do
+    not), the mean and count of the dispatches above and below the midpoint
+    of their range."""
     import csv
     import glob
 
@@ -903,30 +910,56 @@ def digest_counters(fetch_dir: str, write_dir: str, ref_kernel_prefix: str, ref_
 
     fetch = read(fetch_dir, "FETCH_SIZE")
     write = read(write_dir, "WRITE_SIZE")
-    ref = [k for k in fetch if k.startswith(ref_kernel_prefix)]
-    if not ref:
-        raise SystemExit(f"reference kernel {ref_kernel_prefix!r} not in the counter output")
+    ref = [k for k in fetch if ref_kernel in k]
+    if not ref or ref[0] not in write:
+        raise SystemExit(f"reference kernel {ref_kernel!r} not in the counter output")
+
+    def big(vals):
+        # the reference's own dispatches: the large ones (the same functor
+        # may also run on small tensors)
+        v = np.array(vals)
+        return float(np.median(v[v >= 0.5 * v.max()]))
+
     # the reference kernel reads and writes ref_bytes / 2 each
-    f_scale = (ref_bytes / 2) / (min(fetch[ref[0]]) * 1024)
-    w_scale = (ref_bytes / 2) / (min(write[ref[0]]) * 1024)
+    f_scale = (ref_bytes / 2) / (big(fetch[ref[0]]) * 1024)
+    w_scale = (ref_bytes / 2) / (big(write[ref[0]]) * 1024)
     kernels = {}
     for name in sorted(set(fetch) & set(write)):
+        if "swgqa::" not in name:
+            continue
         fv, wv = np.array(fetch[name]), np.array(write[name])
         n = min(len(fv), len(wv))
         per = fv[:n] * 1024 * f_scale + wv[:n] * 1024 * w_scale
-        kernels[name] = {"dispatches": int(n),
-                         "fetch_size_KiB_raw": round(float(fv.mean()), 1),
-                         "write_size_KiB_raw": round(float(wv.mean()), 1),
-                         "hbm_bytes_per_launch": int(per.mean()),
-                         "hbm_bytes_per_launch_min": int(per.min()),
-                         "hbm_bytes_per_launch_max": int(per.max())}
-    data = {"source_digest": source_digest(), "fetch_scale": round(f_scale, 4),
-            "write_scale": round(w_scale, 4), "reference_kernel": ref[0][:120],
-            "reference_bytes_read_and_written": ref_bytes, "kernels": kernels}
+        short = name.replace("void ", "").replace("swgqa::(anonymous namespace)::", "")
+        short = short.split("(")[0]
+        e = {"dispatches": int(n),
+             "fetch_size_KiB_raw": round(float(fv[:n].mean()), 1),
+             "write_size_KiB_raw": round(float(wv[:n].mean()), 1),
+             "hbm_bytes_per_launch": int(per.mean())}
+        lo, hi = float(per.min()), float(per.max())
+        if n > 1 and hi > 1.2 * lo:
+            mid = 0.5 * (lo + hi)
+            e["high_group"] = {"dispatches": int((per > mid).sum()),
+                               "hbm_bytes_per_launch": int(per[per > mid].mean())}
+            e["low_group"] = {"dispatches": int((per <= mid).sum()),
+                              "hbm_bytes_per_launch": int(per[per <= mid].mean())}
+        kernels[short] = e
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    if data.get("source_digest") != source_digest():
+        data = {"source_digest": source_digest(), "workloads": {}}
+    data["reference_kernel"] = ref[0][:120]
+    data["reference_bytes_read_and_written"] = ref_bytes
+    data.setdefault("workloads", {})[label] = {"fetch_scale": round(f_scale, 4),
+                                               "write_scale": round(w_scale, 4),
+                                               "kernels": kernels}
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
-    print(f"wrote {path}: {len(kernels)} kernels, fetch x{f_scale:.3f}, write x{w_scale:.3f}")
+    print(f"{path}: {label}: {len(kernels)} kernels, fetch x{f_scale:.3f}, write x{w_scale:.3f}")
 
 
 def main():
@@ -941,13 +974,19 @@ def main():
                     help="comma list of sections to run: " + ",".join(SECTIONS))
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-mib", type=int, default=512)
-    ap.add_argument("--digest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc csv runs")
+    ap.add_argument("--chunk-capacities", default="1032,1055",
+                    help="cache capacities of the chunked prefill / verify sections")
+    ap.add_argument("--capacity-slacks", default="0,4,16,32,128,256,384",
+                    help="C - W values of the capacity sweep")
+    ap.add_argument("--digest-counters", nargs=3, metavar=("LABEL", "FETCH_DIR", "WRITE_DIR"),
+                    help="add the readings of two rocprofv3 --pmc csv runs of one workload "
+                         "to profiles/traffic.json")
     args = ap.parse_args()
 
     if args.digest_counters:
-        digest_counters(args.digest_counters[0], args.digest_counters[1],
-                        "at::native::vectorized_elementwise_kernel", 2 * args.copy_mib * (1 << 20))
+        digest_counters(args.digest_counters[0], args.digest_counters[1], args.digest_counters[2],
+                        "AUnaryFunctor<float, float, float, at::native::binary_internal::MulFunctor<float>",
+                        2 * args.copy_mib * (1 << 20))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -999,7 +1038,7 @@ def main():
         result.update({
             "value": round(headline.B * K_steps / gpu_s, 2),
             "ms_per_step": round(gpu_s / K_steps * 1e3, 5),
-            "roofline": roofline(bytes_list, kernel_ms, HEADLINE_KERNEL),
+            "roofline": roofline(bytes_list, kernel_ms, HEADLINE_KERNEL, "headline"),
         })
         result["timing"] = {
             "mode": st["mode"],
@@ -1045,20 +1084,21 @@ def main():
 
     if "rotary" in only:
         log("rotary decode ...")
-        result["rotary_decode"] = rotary_decode(torch, sw, args.prompt, 256)
+        result["rotary_decode"] = rotary_decode(torch, sw, args.prompt, 256, use_graph)
     if "small_slack" in only:
         log("small-slack decode ...")
-        result["small_slack"] = small_slack(torch, sw)
+        result["small_slack"] = small_slack(torch, sw, use_graph=use_graph)
     if "chunked" in only:
-        for C in (1032, 1055):
+        for C in (int(x) for x in args.chunk_capacities.split(",")):
             log(f"chunked prefill and verify, C={C} ...")
-            result[f"chunked_prefill_c{C}"] = chunked_prefill(torch, sw, C)
-            result[f"verify_c{C}"] = verify_steps(torch, sw, C)
+            result[f"chunked_prefill_c{C}"] = chunked_prefill(torch, sw, C, use_graph=use_graph)
+            result[f"verify_c{C}"] = verify_steps(torch, sw, C, use_graph=use_graph)
             result[f"verify_rejection_c{C}"] = verify_with_rejection(torch, sw, C,
                                                                      use_graph=use_graph)
     if "capacity" in only:
         log("capacity sweep ...")
-        pts, comp = capacity_sweep(torch, sw)
+        slacks = tuple(int(x) for x in args.capacity_slacks.split(","))
+        pts, comp = capacity_sweep(torch, sw, slacks, use_graph=use_graph)
         result["capacity_sweep"] = {
             "workload": "pages' shape (B=1, 64 Q / 8 KV heads x 64, fp32, W=128), cache at "
                         "T=2048, 800 decode steps, C = W + slack",
