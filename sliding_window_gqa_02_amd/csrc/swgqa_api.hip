@@ -398,6 +398,17 @@ swgqa_status forward_impl(const swgqa_params* p, const void* query, const void* 
                        (int64_t)p->batch_size * p->kv_num_heads <= kMaxSliceCounters;
   a.fuse_writeback = (shared && s.nsplit == 1 && (s.ntiles == 1 || counted)) ? 1 : 0;
   a.waves = s.waves;
+  // long-gap compactions on the staged kernel, one 8-wave workgroup per
+  // slice (every shift at least one round of the 8 waves' stages); the 8-bit
+  // kernel keeps the move after attention (measured no faster with it fused)
+  {
+    const int64_t gap = (int64_t)p->capacity - p->local_window_size + 1;
+    const bool staged = s.kind == Kind::kDecode && !rot_fused;
+    const int sr = staged ? decode_stage_rows(p->dtype, p->head_size, s.nq) : 0;
+    a.fused_move = (staged && a.fuse_writeback && s.ntiles == 1 && s.nsplit == 1 &&
+                    s.waves == 8 && sr > 0 && gap >= 8 * (int64_t)sr)
+                       ? 1 : 0;
+  }
   // What the attention kernel does not finish -- the merge of key splits, the
   // write-back when it is not done in the attention kernel -- runs in one
   // more launch, after every read.

@@ -64,6 +64,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 #endif
 
 
+
 template <int DT, int D, int NQ>
 struct DecShape {
   static constexpr int e = Elem<DT>::bytes;
@@ -215,7 +216,7 @@ __device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
 // Rows of new keys the rotary variant holds in LDS (S < 16 on this path).
 constexpr int kRotMaxRows = 16;
 
-template <int DT, int D, int NQ, int kWaves, int DEPTH, bool ROT>
+template <int DT, int D, int NQ, int kWaves, int DEPTH, bool ROT, bool FM = false>
 __global__ __launch_bounds__(kWaves * kWave)
 __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kernel(AttnArgs a) {
   constexpr int kThreads = kWaves * kWave;
@@ -386,6 +387,31 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   const uint64_t dv_cache = cv_lane - ck_lane;
   const uint64_t dv_new = nv_lane - nk_lane;
 
+  // FM: a compacting step whose slice this workgroup reads alone (one query
+  // tile, one key split, shared buffer): the surviving rows, stage rows jr in
+  // [ncache - kept, ncache), all of them read here, are stored `shift` rows
+  // down while their stage is computed, rather than read a second time after
+  // attention.  Stage st belongs to round st / kWaves; a destination lies
+  // `shift` rows, at least fm_every = 2^k <= shift / (kWaves * SR) rounds,
+  // below its source, so after a barrier that every wave passes once it has
+  // computed every fm_every-th round (its loads of those rounds returned), all
+  // destinations of the next fm_every rounds are rows no wave still reads.
+  // Rows below the read range (evicted) are read by nobody.
+  constexpr int kRoundRows = kWaves * SR;
+  const bool fmove = FM && !ROT && a.fuse_writeback && a.ntiles == 1 && a.nsplit == 1 &&
+                     pl.shift >= kRoundRows && pl.kept > 0 && pl.kept <= ncache;
+  const int nrounds = (nst + kWaves - 1) / kWaves;
+  int fm_mask = 0;
+  if (fmove) {
+    const int64_t q = pl.shift / kRoundRows;  // >= 1
+    const int lg = 63 - __builtin_clzll((uint64_t)q);
+    fm_mask = (1 << (lg < 20 ? lg : 20)) - 1;
+  }
+  const int32_t fm_lo = ncache - (int32_t)(fmove ? pl.kept : 0);
+  const uint64_t fm_k =
+      (uint64_t)a.present_k + (uint64_t)((slice_row0 - pl.shift) * kRowBytes) + sub * 16;
+  const uint64_t fm_dv = (uint64_t)a.present_v - (uint64_t)a.present_k;
+
   const bool has_cap = a.softcap > 0.0f;
   const float cap = a.softcap;
   const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
@@ -474,6 +500,21 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
 #pragma unroll
       for (int t = 0; t < NQ; ++t) part[(t * SR + row) * LPR + sub] = chunk_dot<DT>(qw[t], kr[u], 0.0f);
     }
+    uint32_t tok = 0u;
+    if constexpr (FM && !ROT) {
+      if (fmove) {  // the moved rows' K words
+        const int32_t s0 = st * SR;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int32_t jr = s0 + u * RPW + rslot;
+          if (jr >= fm_lo && jr < ncache)
+            store16_global<SWGQA_FM_NT>(fm_k + ((uint64_t)(uint32_t)jr << kRowShift),
+                           u32x4{kr[u][0], kr[u][1], kr[u][2], kr[u][3]});
+#pragma unroll
+          for (int w = 0; w < 4; ++w) tok ^= kr[u][w];
+        }
+      }
+    }
     wave_lds_fence();
     // B. scores, stage max, probabilities
     float s[PPL];
@@ -556,6 +597,22 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
         for (int k = 0; k < EPL; ++k) acc[t][k] = fmaf(pr[t], vf[k], acc[t][k]);
     }
     wave_lds_fence();
+    if constexpr (FM && !ROT) {
+      if (fmove) {  // the moved rows' V words, and the round's barrier
+        const int32_t s0 = st * SR;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int32_t jr = s0 + u * RPW + rslot;
+          if (jr >= fm_lo && jr < ncache)
+            store16_global<SWGQA_FM_NT>(fm_k + fm_dv + ((uint64_t)(uint32_t)jr << kRowShift),
+                           u32x4{vr[u][0], vr[u][1], vr[u][2], vr[u][3]});
+#pragma unroll
+          for (int w = 0; w < 4; ++w) tok ^= vr[u][w];
+        }
+        const int m = st / kWaves;
+        if (m + 1 < nrounds && ((m + 1) & fm_mask) == 0) barrier_after(tok);
+      }
+    }
   };
 
   // ROT: rotation of the query tile and of the slice's new key chunks, once
@@ -705,6 +762,14 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
     }
   }
 
+  // the barriers of rounds this wave had no stage in
+  if (FM && fmove) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int done = nst > wv ? (nst - wv + kWaves - 1) / kWaves : 0;
+    for (int m = done; m + 1 < nrounds; ++m)
+      if (((m + 1) & fm_mask) == 0) barrier_after(0u);
+  }
+
   // Wave result: acc summed over row slots, l over the lanes of each query.
   const float l_tot = allreduce_q<NQ, false>(l_run);
   // (sum over the lanes that share lane % LPR: the row slots)
@@ -769,7 +834,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
     }
   }
 
-  slice_tail<DT>(a, pl, b, kvh, D, ROT ? (a.S == 1 ? &s_knew1[0][0] : &s_knew[0]) : nullptr);
+  slice_tail<DT>(a, pl, b, kvh, D, ROT ? (a.S == 1 ? &s_knew1[0][0] : &s_knew[0]) : nullptr,
+                 fmove);
 }
 
 template <int DT, int D, int NQ, bool ROT>
@@ -778,7 +844,14 @@ hipError_t launch_nq(const AttnArgs& a, hipStream_t st) {
     const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
     // with rotary, 8-wave workgroups (at most 256 registers a lane) keep two
     // stages in flight: a third spills
-    if (a.waves == 8)
+    // the variant that moves surviving rows while reading them (compacting
+    // steps of long windows; see the kernel) where the host asks for it, in
+    // shapes whose three register sets leave room for it (no spills)
+    using Sh = DecShape<DT, D, NQ>;
+    constexpr bool kFm = SWGQA_FUSED_MOVE && !ROT && Sh::U <= 4 && Sh::PPL <= 2;
+    if (kFm && a.waves == 8 && a.fused_move)
+      attn_decode_kernel<DT, D, NQ, 8, SWGQA_DEC_DEPTH, false, kFm><<<grid, 8 * kWave, 0, st>>>(a);
+    else if (a.waves == 8)
       attn_decode_kernel<DT, D, NQ, 8, ROT ? 2 : SWGQA_DEC_DEPTH, ROT><<<grid, 8 * kWave, 0, st>>>(a);
     else
       attn_decode_kernel<DT, D, NQ, 4, SWGQA_DEC_DEPTH, ROT><<<grid, 4 * kWave, 0, st>>>(a);

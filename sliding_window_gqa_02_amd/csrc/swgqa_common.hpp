@@ -220,6 +220,35 @@ __device__ __forceinline__ u32x4 load16_global(uint64_t addr) {
   else return *(gptr)addr;
 }
 
+// 16-byte store to a global-memory address held as an integer (a GLOBAL
+// instruction, for the same reason).
+template <bool NT = false>
+__device__ __forceinline__ void store16_global(uint64_t addr, const u32x4& v) {
+  typedef u32x4 __attribute__((address_space(1)))* gptr;
+  if constexpr (NT) __builtin_nontemporal_store(v, (gptr)addr);
+  else *(gptr)addr = v;
+}
+
+// Decode kernels: the variant that moves a compacting slice's surviving rows
+// while reading them (1), and whether those stores are non-temporal (1).
+#ifndef SWGQA_FUSED_MOVE
+#define SWGQA_FUSED_MOVE 1
+#endif
+#ifndef SWGQA_FM_NT
+#define SWGQA_FM_NT 1
+#endif
+
+// Workgroup barrier that a wave reaches only once `tok` -- a value computed
+// from its last stage's loaded words -- exists, i.e. once those loads (and,
+// returning in order, all earlier ones) have returned; no wait for memory
+// beyond that, so the loads of later stages stay in flight.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_after(uint32_t tok) {
+  asm volatile("" ::"v"(tok) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // One element at a global-memory address held as an integer, as float.
 template <int DT>
 __device__ __forceinline__ float load_elem_global(uint64_t addr) {

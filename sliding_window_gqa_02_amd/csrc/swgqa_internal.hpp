@@ -42,6 +42,9 @@ struct AttnArgs {
   int32_t smooth;
   int32_t fuse_writeback;  // shared buffer, one key split: write-back in the kernel
   int32_t waves;           // waves per workgroup of the staged kernel
+  // staged decode kernel, 8 waves, one workgroup per slice: the variant that
+  // moves a compacting slice's surviving rows as it reads them
+  int32_t fused_move;
   // rotary embedding fused into the staged decode kernel (rot_cos non-NULL):
   // tables (rot_rows, D/2), 16-byte aligned; positions (B, S) or NULL (P + i)
   const void* rot_cos;

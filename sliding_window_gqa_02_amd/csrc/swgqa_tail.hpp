@@ -60,17 +60,19 @@ __device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w
   }
 }
 
-// Cache write-back of slice (b, kvh) for both K and V, shared buffer.
+// Cache write-back of slice (b, kvh) for both K and V, shared buffer; with
+// `moved` the surviving rows are already in place and only the new rows land.
 __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const ItemPlan& pl,
                                                        int b, int kvh, int D, int e,
-                                                       const u32x4* knew, const u32x4* vnew) {
+                                                       const u32x4* knew, const u32x4* vnew,
+                                                       bool moved) {
   const int64_t rowb = (int64_t)D * e;
   const int64_t w16 = rowb / 16;
   const int64_t off = ((int64_t)b * a.Hkv + kvh) * a.C * rowb;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   if (pl.shift > 0) {
-    if (pl.kept > 0)
+    if (pl.kept > 0 && !moved)
       move_rows_in_place((u32x4*)((char*)a.present_k + off), (u32x4*)((char*)a.present_v + off),
                          w16, __builtin_ctzll(w16), pl.shift, pl.kept, tid, nthr);
     // new rows after the move (they may land on rows the move read)
@@ -100,10 +102,12 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
 //
 // ce is the cache element size in bytes; knew / vnew, if not NULL, hold the
 // step's new key / value rows of the slice in cache form (S rows of D * ce /
-// 16 words, in LDS) to store in place of a.k's / a.v's.
+// 16 words, in LDS) to store in place of a.k's / a.v's.  `moved`: the only
+// reader of the slice has already moved the surviving rows while reading
+// them.
 __device__ __forceinline__ void slice_tail_rows(const AttnArgs& a, const ItemPlan& pl, int b,
                                                 int kvh, int D, int ce, const u32x4* knew,
-                                                const u32x4* vnew) {
+                                                const u32x4* vnew, bool moved = false) {
   if (!a.fuse_writeback || pl.shift == 0) return;  // drifting: appended by tile 0
   __syncthreads();  // all reads of this slice by this workgroup are done
   if (a.ntiles > 1) {
@@ -119,13 +123,14 @@ __device__ __forceinline__ void slice_tail_rows(const AttnArgs& a, const ItemPla
     __syncthreads();
     if (!s_last) return;
   }
-  slice_writeback_shared(a, pl, b, kvh, D, ce, knew, vnew);
+  slice_writeback_shared(a, pl, b, kvh, D, ce, knew, vnew, moved);
 }
 
 template <int DT>
 __device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl, int b, int kvh,
-                                           int D, const u32x4* knew = nullptr) {
-  slice_tail_rows(a, pl, b, kvh, D, Elem<DT>::bytes, knew, nullptr);
+                                           int D, const u32x4* knew = nullptr,
+                                           bool moved = false) {
+  slice_tail_rows(a, pl, b, kvh, D, Elem<DT>::bytes, knew, nullptr, moved);
 }
 
 }  // namespace swgqa

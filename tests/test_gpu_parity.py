@@ -215,6 +215,60 @@ def test_pages_shape_tight_capacity(slack):
     say(f"  worst scaled error {run.worst:.3g}, {events} compactions")
 
 
+# Compactions with a long gap on the 8-wave staged decode kernel, one
+# workgroup per (item, KV head): the surviving rows are stored at their new
+# place while attention reads them, behind a barrier every 2^k rounds of the
+# waves' stages (the gap holds at least one round).  Each item starts a few
+# steps before its next compaction (past lengths seeded in the contract
+# layout), so every item compacts once or twice; every output, every resident
+# row byte for byte, the poison of unwritten rows and the canaries are checked
+# after every step.  Shapes: the gap exactly one round (a barrier after every
+# round), two and more rounds, a window that is not a whole number of rounds,
+# fp32 / fp16 / bf16 at the stage shapes the variant is built for, and
+# two-token steps on a one-tile slice.
+FUSED_MOVE = [
+    (Cfg(B=8, Hq=32, Hkv=8, D=128, C=327, W=200, seed=151, dtype=synth.BF16), [1]),
+    (Cfg(B=8, Hq=32, Hkv=8, D=128, C=600, W=200, seed=152, dtype=synth.BF16, softcap=30.0),
+     [1]),
+    (Cfg(B=16, Hq=32, Hkv=8, D=128, C=1300, W=1000, seed=153, dtype=synth.BF16), [1]),
+    (Cfg(B=8, Hq=32, Hkv=8, D=64, C=400, W=230, seed=154, dtype=synth.F32), [1]),
+    (Cfg(B=2, Hq=2, Hkv=2, D=64, C=495, W=240, seed=155, dtype=synth.F16), [1, 2]),
+    (Cfg(B=32, Hq=16, Hkv=2, D=32, C=313, W=250, seed=156, dtype=synth.F32), [1]),
+    # 8-bit caches at the same shapes: the kernel that moves rows after
+    # attention (long gaps, one 8-wave workgroup per slice)
+    (Cfg(B=8, Hq=32, Hkv=8, D=128, C=327, W=200, seed=157, dtype=synth.BF16, kv_int8=True,
+         k_scale=0.03, v_scale=0.02), [1]),
+    (Cfg(B=8, Hq=32, Hkv=8, D=64, C=400, W=230, seed=158, dtype=synth.F16, kv_fp8=True,
+         k_scale=0.05, v_scale=0.04, softcap=30.0), [1]),
+]
+
+
+@pytest.mark.parametrize("cfg,steps", FUSED_MOVE,
+                         ids=lambda c: f"W{c.W}G{c.C - c.W + 1}D{c.D}t{c.dtype}"
+                         f"{'i8' if c.kv_int8 else 'f8' if c.kv_fp8 else ''}"
+                         if isinstance(c, Cfg) else "")
+def test_long_gap_compaction_moves_while_reading(cfg, steps):
+    G = cfg.C - cfg.W + 1
+    syn = cfg.synth()
+    # item b compacts on its step offs[b] + 1 (its past length reaches C + G);
+    # the small batches run on through a second compaction
+    offs = [(3 + 11 * b) % min(G, 40) for b in range(cfg.B)]
+    P = np.array([cfg.C + G - 1 - o for o in offs], dtype=np.int64)
+    n = max(offs) + 2 + (G if cfg.B * cfg.Hq <= 256 else 0)
+    vers = Versions(cfg.B, n=int(P.max()) + 2 * n + 8)
+    K, V = seeded_cache(cfg, syn, P, vers)
+    run = Lockstep(cfg, K=K, V=V, vers=vers)
+    say(f"long-gap compaction {cfg}: G={G}, {n} steps from P={list(P[:4])}")
+    events = 0
+    for i in range(n):
+        S = steps[i % len(steps)]
+        _, _, plan = run.step(P, S, check_regen=(i % 5 == 0))
+        events += int((plan[:, 5] > 0).sum())
+        P = P + S
+    say(f"  {events} compaction events, worst scaled error {run.worst:.3g}")
+    assert events >= cfg.B
+
+
 # Rows wider than 256 bytes: fp32 at head size 128 and 256, bf16 at 256.
 # Steps of few query rows go to the generic split kernel (whole slices, and
 # key splits merged by the step tail over a long window); fp32 D = 128 and
