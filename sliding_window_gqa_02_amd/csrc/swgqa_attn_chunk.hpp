@@ -66,7 +66,7 @@ struct ChunkShape {
   static constexpr int e = Elem<DT>::bytes;
   // LDS row strides (elements), chosen so the MFMA operand reads of 16 lanes
   // on 16 different rows fall in distinct banks
-  static constexpr int KS = (DT == kF32) ? D + 2 : D + 8;   // K rows: [key][d]
+  static constexpr int KS = (DT == kF32) ? D + 4 : D + 8;   // K rows: [key][d]
   static constexpr int VS = (DT == kF32) ? D + 4 : BN + 4;  // fp32 V [key][d]; 16-bit V^T [d][key]
   static constexpr int KELEMS = BN * KS;
   static constexpr int VELEMS = (DT == kF32) ? BN * VS : D * VS;
@@ -139,8 +139,14 @@ __device__ __forceinline__ u32x4 codes_to_elems(const u32x4& c) {
 }
 
 // CT: 0 for a cache in the element type, else the code type of the cache.
+#ifndef SWGQA_CHUNK_F32_WPE
+#define SWGQA_CHUNK_F32_WPE 1
+#endif
+
 template <int DT, int D, bool BIAS, int NW, int CT>
-__global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * kWave)
+__attribute__((amdgpu_waves_per_eu(DT == kF32 ? SWGQA_CHUNK_F32_WPE : 1, 8)))
+void attn_chunk_kernel(AttnArgs a) {
   constexpr bool Q8 = CT != 0;
   using Sh = ChunkShape<DT, D, NW>;
   constexpr int kThreads = Sh::kThreads;
@@ -154,8 +160,10 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   static_assert(Sh::ok, "unsupported chunk shape");
   static_assert(!Q8 || D >= 16, "int8 rows of whole 16-byte chunks");
 
-  __shared__ LT sK[Sh::KELEMS];
-  __shared__ LT sV[Sh::VELEMS];
+  // two K/V buffers: block blk is staged in buffer blk & 1 while the other
+  // holds the block being computed
+  __shared__ __attribute__((aligned(16))) LT sK[2 * Sh::KELEMS];
+  __shared__ __attribute__((aligned(16))) LT sV[2 * Sh::VELEMS];
 
   // work item P of the launch: slice P / T, item (tile, split) P % T
   const uint32_t T = gridDim.x;  // ntiles * nsplit
@@ -188,14 +196,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   const int i_first = q0 / a.group;
   const int i_last = (min(q0 + BQ, nq_item) - 1) / a.group;
 
-  // Q^T operand: fp32 step s holds Q[q][4s + lg]; 16-bit step s holds
-  // Q[q][16s + 4lg .. +3].
+  // Q^T operand: fp32 step s holds Q[q][(D / 4) lg + s] (the steps split
+  // the head dimension as d = (D / 4) k + s over the 4 reduction lanes k, so
+  // a lane's K and Q operands are D / 4 consecutive elements); 16-bit step s
+  // holds Q[q][16s + 4lg .. +3].
   const char* qrow = (const char*)a.q + ((((int64_t)b * a.S + my_i) * a.Hq + my_h) * D) * e;
   float qf[DT == kF32 ? DSTEPS : 1];
   uint32_t qh[DT == kF32 ? 1 : DSTEPS][2];
   if constexpr (DT == kF32) {
 #pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) qf[s] = ((const float*)qrow)[4 * s + lg];
+    for (int s = 0; s < DSTEPS; s += 4) {
+      const f4 v = *(const f4*)((const float*)qrow + DSTEPS * lg + s);
+      qf[s] = v[0]; qf[s + 1] = v[1]; qf[s + 2] = v[2]; qf[s + 3] = v[3];
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < DSTEPS; ++s) {
@@ -283,6 +296,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
     kc_lane[u] = ck + off;
     vc_lane[u] = cv + off;
   }
+  // and of new rows: key c / CPR at new row (j0 - P) + key, part c % CPR
+  uint32_t nw_lane[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
+    nw_lane[u] = (uint32_t)((c / CPR) * new_stride + (c % CPR) * kPartB);
+  }
   const uint64_t bias_lane =
       BIAS ? (uint64_t)a.bias + (uint64_t)((bias_row + 4 * lg) * e) : 0;
   const int64_t cache_end = pl.P < ke ? pl.P : ke;  // keys below this are cache rows
@@ -297,6 +317,18 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
         } else {
           rg.k[u] = load16_global<false>(kc_lane[u] + boff);
           rg.v[u] = load16_global<false>(vc_lane[u] + boff);
+        }
+      }
+    } else if (j0 >= pl.P && j0 + BN <= ke) {  // uniform: only new rows (prefill)
+      const uint64_t boff = (uint64_t)((j0 - pl.P) * new_stride);
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        if constexpr (Q8) {
+          rg.k[u] = load_codes<DT>(nk + boff + nw_lane[u]);
+          rg.v[u] = load_codes<DT>(nv + boff + nw_lane[u]);
+        } else {
+          rg.k[u] = load16_global<false>(nk + boff + nw_lane[u]);
+          rg.v[u] = load16_global<false>(nv + boff + nw_lane[u]);
         }
       }
     } else {
@@ -337,7 +369,9 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
       }
     }
   };
-  auto store_block = [&](const BlockRegs& rg) __attribute__((always_inline)) {
+  auto store_block = [&](const BlockRegs& rg, int buf) __attribute__((always_inline)) {
+    LT* const bK = sK + buf * Sh::KELEMS;
+    LT* const bV = sV + buf * Sh::VELEMS;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int c = tid + u * kThreads;
@@ -348,23 +382,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
       const u32x4 kw = Q8 ? codes_to_elems<DT, CT>(rg.k[u]) : rg.k[u];
       const u32x4 vw = Q8 ? codes_to_elems<DT, CT>(rg.v[u]) : rg.v[u];
       if constexpr (DT == kF32) {
-        float* kd = (float*)sK + key * KS + d0;
-        float* vd = (float*)sV + key * VS + d0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          kd[w] = __uint_as_float(kw[w]);
-          vd[w] = __uint_as_float(vw[w]);
-        }
+        // rows of 16-byte multiples: one store per chunk
+        *(u32x4*)((float*)bK + key * KS + d0) = kw;
+        *(u32x4*)((float*)bV + key * VS + d0) = vw;
       } else {
         // K rows are 16-byte aligned: one store per chunk
-        *(u32x4*)((uint16_t*)sK + key * KS + d0) = kw;
+        *(u32x4*)((uint16_t*)bK + key * KS + d0) = kw;
         // V transposed, sV[d][key ^ swz(d)]: the 16 parts of a key row land
         // on rows 8 apart, which the swizzle spreads over the banks
         const int kx = key ^ vt_swizzle(d0);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          ((uint16_t*)sV)[(d0 + 2 * w) * VS + kx] = (uint16_t)(vw[w] & 0xFFFFu);
-          ((uint16_t*)sV)[(d0 + 2 * w + 1) * VS + kx] = (uint16_t)(vw[w] >> 16);
+          ((uint16_t*)bV)[(d0 + 2 * w) * VS + kx] = (uint16_t)(vw[w] & 0xFFFFu);
+          ((uint16_t*)bV)[(d0 + 2 * w + 1) * VS + kx] = (uint16_t)(vw[w] >> 16);
         }
       }
     }
@@ -386,18 +416,34 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
   const float qk_scale = Q8 ? a.scale * a.k_scale : a.scale;
   // One block: scores, online softmax, PV, from the block staged in LDS.
   auto compute_block = [&](int blk, const float* bias_blk) __attribute__((always_inline)) {
+    const LT* const bK = sK + (blk & 1) * Sh::KELEMS;
+    const LT* const bV = sV + (blk & 1) * Sh::VELEMS;
     // S^T for the two 16-key tiles of the block
     f4 sc[2];
+    if constexpr (DT == kF32) {
+      // lane: key rows lq and 16 + lq, elements [DSTEPS lg, DSTEPS lg +
+      // DSTEPS) of each, four at a time; the two tiles' products alternate
+      f4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      const float* k0 = (const float*)bK + lq * KS + DSTEPS * lg;
+      const float* k1 = k0 + 16 * KS;
+#pragma unroll
+      for (int s = 0; s < DSTEPS; s += 4) {
+        const f4 a0 = *(const f4*)(k0 + s);
+        const f4 a1 = *(const f4*)(k1 + s);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], qf[s + t], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[t], qf[s + t], acc1, 0, 0, 0);
+        }
+      }
+      sc[0] = acc0;
+      sc[1] = acc1;
+    } else {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (DT == kF32) {
-        const float* kr = (const float*)sK + (kt * 16 + lq) * KS + lg;
-#pragma unroll
-        for (int s = 0; s < DSTEPS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[4 * s], qf[s], acc, 0, 0, 0);
-      } else {
-        const uint16_t* kr = (const uint16_t*)sK + (kt * 16 + lq) * KS + 4 * lg;
+      {
+        const uint16_t* kr = (const uint16_t*)bK + (kt * 16 + lq) * KS + 4 * lg;
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
           const uint2 kv = *(const uint2*)(kr + 16 * s);
@@ -413,6 +459,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
         }
       }
       sc[kt] = acc;
+    }
     }
 
     // Scores: key j = j0 + 16 kt + 4 lg + r, query lq.
@@ -473,12 +520,27 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       if constexpr (DT == kF32) {
+        // fp32: O^T tile dt holds rows d = DT16 i + dt, so a lane's V
+        // operands for all tiles are DT16 consecutive elements of one key
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
-          const float* vr = (const float*)sV + (kt * 16 + 4 * lg + t4) * VS + lq;
+          const float* vr = (const float*)bV + (kt * 16 + 4 * lg + t4) * VS + DT16 * lq;
+          float va[DT16];
+          if constexpr (DT16 % 4 == 0) {
+#pragma unroll
+            for (int c = 0; c < DT16; c += 4) {
+              const f4 w = *(const f4*)(vr + c);
+              va[c] = w[0]; va[c + 1] = w[1]; va[c + 2] = w[2]; va[c + 3] = w[3];
+            }
+          } else if constexpr (DT16 == 2) {
+            const float2 w = *(const float2*)vr;
+            va[0] = w.x; va[1] = w.y;
+          } else {
+            va[0] = vr[0];
+          }
 #pragma unroll
           for (int dt = 0; dt < DT16; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * dt], sc[kt][t4], o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[dt], sc[kt][t4], o[dt], 0, 0, 0);
         }
       } else {
         uint32_t pw[2], pl2[2];
@@ -501,7 +563,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < DT16; ++dt) {
-          const uint2 vv = *(const uint2*)((const uint16_t*)sV + (16 * dt + lq) * VS +
+          const uint2 vv = *(const uint2*)((const uint16_t*)bV + (16 * dt + lq) * VS +
                                            ((kt * 16 + 4 * lg) ^ vt_swizzle(16 * dt + lq)));
           if constexpr (DT == kF16) {
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
@@ -519,14 +581,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
       }
     }
   };
-  // A block's K/V/bias loads are issued three blocks ahead (register ring of
-  // three), so two blocks of loads stay in flight while one is computed;
-  // blocks past the band's end reload its last block.
-  auto block_start = [&](int blk) { return kb + (int64_t)min(blk, nblocks - 1) * BN; };
-  auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
-    __syncthreads();  // the previous block's LDS reads are done
-    store_block(rg);
-    float bias_blk[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  // The attention_bias entries of block blk as floats, from its raw words.
+  auto block_bias = [&](int blk, const BlockRegs& rg, float* bias_blk) __attribute__((always_inline)) {
     if constexpr (BIAS) {
       const int64_t j0 = kb + (int64_t)blk * BN;
 #pragma unroll
@@ -549,21 +605,40 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
         for (int r = 0; r < 4; ++r) bias_blk[kt * 4 + r] = x[r];
       }
     }
+  };
+  // A block's K/V/bias loads are issued three steps before it is staged
+  // (register ring of three), so two blocks of loads stay in flight while
+  // one is computed; blocks past the band's end reload its last block.  Step
+  // blk computes block blk from LDS buffer blk & 1, then stages block blk + 1
+  // (in the ring since step blk - 3) into the other buffer -- whose block,
+  // blk - 1, every wave finished before the barrier that ended step blk - 1
+  // -- reloads those registers with block blk + 4, and ends with a barrier,
+  // after which block blk + 1 is visible and buffer blk & 1 free: one
+  // barrier per block.
+  auto block_start = [&](int blk) { return kb + (int64_t)min(blk, nblocks - 1) * BN; };
+  float bias_cur[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
+    compute_block(blk, bias_cur);
+    store_block(rg, (blk + 1) & 1);
+    block_bias(blk + 1, rg, bias_cur);  // compute_block(blk) is done with it
+    load_block(block_start(blk + 4), rg);
     __syncthreads();
-    load_block(block_start(blk + 3), rg);
-    compute_block(blk, bias_blk);
   };
   if (nblocks > 0) {
     BlockRegs r0, r1, r2;
     load_block(block_start(0), r0);
     load_block(block_start(1), r1);
     load_block(block_start(2), r2);
+    store_block(r0, 0);
+    block_bias(0, r0, bias_cur);
+    load_block(block_start(3), r0);
+    __syncthreads();
     for (int blk = 0; blk < nblocks;) {
-      step(blk, r0);
-      if (++blk >= nblocks) break;
       step(blk, r1);
       if (++blk >= nblocks) break;
       step(blk, r2);
+      if (++blk >= nblocks) break;
+      step(blk, r0);
       ++blk;
     }
   }
@@ -577,12 +652,26 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
       float m_fin = m_run;
       const float inv = fold_sink<DT>(a.sink, a.smooth, my_h, m_fin, l_run) / l_run *
                         (Q8 ? a.v_scale : 1.0f);
+      if constexpr (DT == kF32) {
+        // element DT16 (4 lg + r) + dt of the row is o[dt][r]
+        float* orow = (float*)a.out + row * D + DT16 * 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (DT16 % 4 == 0) {
+#pragma unroll
+            for (int c = 0; c < DT16; c += 4)
+              *(f4*)(orow + DT16 * r + c) =
+                  f4{o[c][r] * inv, o[c + 1][r] * inv, o[c + 2][r] * inv, o[c + 3][r] * inv};
+          } else {
+#pragma unroll
+            for (int dt = 0; dt < DT16; ++dt) orow[DT16 * r + dt] = o[dt][r] * inv;
+          }
+        }
+      } else {
 #pragma unroll
       for (int dt = 0; dt < DT16; ++dt) {
         const int d0 = 16 * dt + 4 * lg;
-        if constexpr (DT == kF32) {
-          *(f4*)((float*)a.out + row * D + d0) = o[dt] * inv;
-        } else {
+        {
           uint32_t w0, w1;
           if constexpr (DT == kF16) {
             w0 = (uint32_t)f32_to_f16_bits(o[dt][0] * inv) | ((uint32_t)f32_to_f16_bits(o[dt][1] * inv) << 16);
@@ -594,11 +683,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_chunk_kernel(AttnArgs a) {
           *(uint2*)((uint16_t*)a.out + row * D + d0) = make_uint2(w0, w1);
         }
       }
+      }
     } else {
       float* op = a.opart + (row * a.nsplit + split) * D;
+      const float vs = Q8 ? a.v_scale : 1.0f;
+      if constexpr (DT == kF32) {
 #pragma unroll
-      for (int dt = 0; dt < DT16; ++dt)
-        *(f4*)(op + 16 * dt + 4 * lg) = Q8 ? o[dt] * a.v_scale : o[dt];
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int dt = 0; dt < DT16; ++dt) op[DT16 * (4 * lg + r) + dt] = o[dt][r] * vs;
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt) *(f4*)(op + 16 * dt + 4 * lg) = o[dt] * vs;
+      }
       if (lg == 0) {
         a.ml[(row * a.nsplit + split) * 2 + 0] = m_run;
         a.ml[(row * a.nsplit + split) * 2 + 1] = l_run;
