@@ -149,11 +149,9 @@ SplitPlan plan_split(const swgqa_params* p) {
     // multi-token step on the matrix cores (its bias reads take rows of at
     // least 4 entries)
     s.kind = Kind::kChunk;
-    // 16-bit types: 8-wave workgroups (128 query rows) once a KV head has
-    // that many rows -- twice the matrix work per staged K/V block, two
-    // waves per SIMD (measured slower for fp32, whose operands take twice
-    // the registers)
-    s.waves = (p->dtype != SWGQA_F32 && per_kv >= kChunkWideRows) ? 8 : 4;
+    // 8-wave workgroups (128 query rows) once a KV head has that many rows:
+    // twice the matrix work per staged K/V block
+    s.waves = per_kv >= kChunkWideRows ? 8 : 4;
     s.nq = chunk_rows_per_workgroup(s.waves);
     s.ntiles = (per_kv + s.nq - 1) / s.nq;
     const int64_t span = std::min<int64_t>(p->sequence_length, (s.nq + group - 1) / group + 1);

@@ -139,13 +139,22 @@ __device__ __forceinline__ u32x4 codes_to_elems(const u32x4& c) {
 }
 
 // CT: 0 for a cache in the element type, else the code type of the cache.
-#ifndef SWGQA_CHUNK_F32_WPE
-#define SWGQA_CHUNK_F32_WPE 1
+#ifndef SWGQA_CHUNK_DB_ALL
+#define SWGQA_CHUNK_DB_ALL 0
 #endif
+
+// Waves per SIMD the compiler must leave room for: fp32 with rows of at
+// most 256 bytes, 4 in 8-wave workgroups (its operands fit 128 registers
+// with two blocks of loads in flight; measured faster than 2 or 3 waves) and
+// 3 in 4-wave ones (whose bias path needs a little more); otherwise no floor.
+template <int DT, int D, int NW>
+constexpr int chunk_min_waves() {
+  return DT == kF32 && D <= 64 ? (NW == 8 ? 4 : 3) : 1;
+}
 
 template <int DT, int D, bool BIAS, int NW, int CT>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(DT == kF32 ? SWGQA_CHUNK_F32_WPE : 1, 8)))
+__attribute__((amdgpu_waves_per_eu(chunk_min_waves<DT, D, NW>(), 8)))
 void attn_chunk_kernel(AttnArgs a) {
   constexpr bool Q8 = CT != 0;
   using Sh = ChunkShape<DT, D, NW>;
@@ -160,10 +169,13 @@ void attn_chunk_kernel(AttnArgs a) {
   static_assert(Sh::ok, "unsupported chunk shape");
   static_assert(!Q8 || D >= 16, "int8 rows of whole 16-byte chunks");
 
-  // two K/V buffers: block blk is staged in buffer blk & 1 while the other
-  // holds the block being computed
-  __shared__ __attribute__((aligned(16))) LT sK[2 * Sh::KELEMS];
-  __shared__ __attribute__((aligned(16))) LT sV[2 * Sh::VELEMS];
+  // DB (fp32): two K/V buffers, block blk staged in buffer blk & 1 while the
+  // other holds the block being computed; 16-bit types stage every block in
+  // one buffer between two barriers (measured faster for them)
+  constexpr bool DB = SWGQA_CHUNK_DB_ALL || DT == kF32;
+  constexpr int NBUF = DB ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) LT sK[NBUF * Sh::KELEMS];
+  __shared__ __attribute__((aligned(16))) LT sV[NBUF * Sh::VELEMS];
 
   // work item P of the launch: slice P / T, item (tile, split) P % T
   const uint32_t T = gridDim.x;  // ntiles * nsplit
@@ -413,36 +425,40 @@ void attn_chunk_kernel(AttnArgs a) {
   for (int t = 0; t < DT16; ++t) o[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int nblocks = ke > kb ? (int)((ke - kb + BN - 1) / BN) : 0;
+  const int32_t nk_band = ke > kb ? (int32_t)(ke - kb) : 0;  // keys of this split
   const float qk_scale = Q8 ? a.scale * a.k_scale : a.scale;
   // One block: scores, online softmax, PV, from the block staged in LDS.
   auto compute_block = [&](int blk, const float* bias_blk) __attribute__((always_inline)) {
-    const LT* const bK = sK + (blk & 1) * Sh::KELEMS;
-    const LT* const bV = sV + (blk & 1) * Sh::VELEMS;
+    const LT* const bK = sK + (DB ? (blk & 1) : 0) * Sh::KELEMS;
+    const LT* const bV = sV + (DB ? (blk & 1) : 0) * Sh::VELEMS;
+    // the block's second 16-key tile holds keys of the band (else its
+    // scores are masked and its products are skipped: P = 0 there)
+    const bool tile1 = blk * BN + 16 < nk_band;
     // S^T for the two 16-key tiles of the block
     f4 sc[2];
     if constexpr (DT == kF32) {
-      // lane: key rows lq and 16 + lq, elements [DSTEPS lg, DSTEPS lg +
-      // DSTEPS) of each, four at a time; the two tiles' products alternate
-      f4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      const float* k0 = (const float*)bK + lq * KS + DSTEPS * lg;
-      const float* k1 = k0 + 16 * KS;
+      // lane: key row 16 kt + lq, elements [DSTEPS lg, DSTEPS lg + DSTEPS),
+      // four at a time
 #pragma unroll
-      for (int s = 0; s < DSTEPS; s += 4) {
-        const f4 a0 = *(const f4*)(k0 + s);
-        const f4 a1 = *(const f4*)(k1 + s);
+      for (int kt = 0; kt < 2; ++kt) {
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (kt == 0 || tile1) {
+          const float* kr = (const float*)bK + (16 * kt + lq) * KS + DSTEPS * lg;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[t], qf[s + t], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[t], qf[s + t], acc1, 0, 0, 0);
+          for (int s = 0; s < DSTEPS; s += 4) {
+            const f4 k4 = *(const f4*)(kr + s);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k4[t], qf[s + t], acc, 0, 0, 0);
+          }
         }
+        sc[kt] = acc;
       }
-      sc[0] = acc0;
-      sc[1] = acc1;
     } else {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      {
+      if (kt == 0 || tile1) {
         const uint16_t* kr = (const uint16_t*)bK + (kt * 16 + lq) * KS + 4 * lg;
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
@@ -519,6 +535,7 @@ void attn_chunk_kernel(AttnArgs a) {
     // O^T += V^T . P^T
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      if (kt == 1 && !tile1) break;
       if constexpr (DT == kF32) {
         // fp32: O^T tile dt holds rows d = DT16 i + dt, so a lane's V
         // operands for all tiles are DT16 consecutive elements of one key
@@ -594,8 +611,13 @@ void attn_chunk_kernel(AttnArgs a) {
         const uint32_t* w = &rg.bias[kt * BW / 2];
         float x[4];
         if constexpr (DT == kF32) {
+          // (selects, not an index: a register array indexed at run time
+          // would live in scratch memory)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = __uint_as_float(w[min(r + sh, 3)]);
+          for (int r = 0; r < 4; ++r) {
+            const int i = min(r + sh, 3);
+            x[r] = __uint_as_float(i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3]);
+          }
         } else {
           const uint64_t v = (((uint64_t)w[1] << 32) | w[0]) >> (16 * sh);
           unpack_word<DT>((uint32_t)v, x);
@@ -617,29 +639,55 @@ void attn_chunk_kernel(AttnArgs a) {
   // barrier per block.
   auto block_start = [&](int blk) { return kb + (int64_t)min(blk, nblocks - 1) * BN; };
   float bias_cur[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  // (fp32, and 16-bit rows of 512 bytes: two, which keeps them within the
+  // registers of their occupancy)
+  constexpr int RING = (DT == kF32 || D * e >= 512) ? 2 : 3;
   auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
     compute_block(blk, bias_cur);
     store_block(rg, (blk + 1) & 1);
     block_bias(blk + 1, rg, bias_cur);  // compute_block(blk) is done with it
-    load_block(block_start(blk + 4), rg);
+    load_block(block_start(blk + 1 + RING), rg);
     __syncthreads();
   };
-  if (nblocks > 0) {
-    BlockRegs r0, r1, r2;
-    load_block(block_start(0), r0);
-    load_block(block_start(1), r1);
-    load_block(block_start(2), r2);
-    store_block(r0, 0);
-    block_bias(0, r0, bias_cur);
-    load_block(block_start(3), r0);
+  // single buffer: barrier, stage block blk, barrier, reload its registers
+  // with block blk + RING, compute block blk
+  auto step1 = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
+    __syncthreads();  // the previous block's LDS reads are done
+    store_block(rg, 0);
+    block_bias(blk, rg, bias_cur);
+    __syncthreads();
+    load_block(block_start(blk + RING), rg);
+    compute_block(blk, bias_cur);
+  };
+  if constexpr (!DB) {
+    if (nblocks > 0) {
+      BlockRegs rg[RING];
+#pragma unroll
+      for (int i = 0; i < RING; ++i) load_block(block_start(i), rg[i]);
+      for (int blk = 0; blk < nblocks;) {
+#pragma unroll
+        for (int i = 0; i < RING; ++i) {
+          if (blk >= nblocks) break;
+          step1(blk, rg[i]);
+          ++blk;
+        }
+      }
+    }
+  } else if (nblocks > 0) {
+    BlockRegs rg[RING];
+#pragma unroll
+    for (int i = 0; i < RING; ++i) load_block(block_start(i), rg[i]);
+    store_block(rg[0], 0);
+    block_bias(0, rg[0], bias_cur);
+    load_block(block_start(RING), rg[0]);
     __syncthreads();
     for (int blk = 0; blk < nblocks;) {
-      step(blk, r1);
-      if (++blk >= nblocks) break;
-      step(blk, r2);
-      if (++blk >= nblocks) break;
-      step(blk, r0);
-      ++blk;
+#pragma unroll
+      for (int i = 0; i < RING; ++i) {
+        if (blk >= nblocks) break;
+        step(blk, rg[(i + 1) % RING]);
+        ++blk;
+      }
     }
   }
 
@@ -716,7 +764,7 @@ void attn_chunk_kernel(AttnArgs a) {
     }
   }
 
-  slice_tail_rows(a, pl, b, kvh, D, CE, nullptr, nullptr);
+  slice_tail_rows<8>(a, pl, b, kvh, D, CE, nullptr, nullptr);
 }
 
 template <int DT, int D, int NW, int CT>

@@ -18,7 +18,12 @@
 
 namespace swgqa {
 
-constexpr int kMoveUnroll = 16;  // 16-byte words per thread and tensor per pass
+// 16-byte words per thread and tensor that one pass of a move holds in
+// registers: kernels whose occupancy is bounded by their attention loop take
+// 16; those whose attention loop needs fewer registers than 16 words of K
+// and V would take 8 (the move's peak would otherwise set the kernel's
+// register count and with it its occupancy).
+constexpr int kMoveUnroll = 16;
 
 // In-place move of rows [shift, shift + kept) -> [0, kept) of the K slice and,
 // if `v` is not null, of the V slice at the same offsets; rows are `w16`
@@ -29,18 +34,19 @@ constexpr int kMoveUnroll = 16;  // 16-byte words per thread and tensor per pass
 // that its destinations overlap its own sources -- a barrier, then its
 // stores, then a barrier before the next pass, whose destinations are this
 // pass's sources.
+template <int UNROLL = kMoveUnroll>
 __device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w16, int wlog,
                                                    int64_t shift, int64_t kept, int tid,
                                                    int nthr) {
-  const int64_t cap_rows = ((int64_t)nthr * kMoveUnroll) >> wlog;
+  const int64_t cap_rows = ((int64_t)nthr * UNROLL) >> wlog;
   const int64_t pass = cap_rows > 0 ? cap_rows : 1;
   const int64_t wmask = ((int64_t)1 << wlog) - 1;
   for (int64_t r0 = 0; r0 < kept; r0 += pass) {
     const int64_t nr = kept - r0 < pass ? kept - r0 : pass;
     const int64_t nw = nr << wlog;
-    u32x4 bk[kMoveUnroll], bv[kMoveUnroll];
+    u32x4 bk[UNROLL], bv[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kMoveUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t idx = min(tid + (int64_t)u * nthr, nw - 1);
       const int64_t at = (shift + r0 + (idx >> wlog)) * w16 + (idx & wmask);
       bk[u] = k[at];
@@ -48,7 +54,7 @@ __device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w
     }
     if (nr > shift) __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kMoveUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int64_t idx = tid + (int64_t)u * nthr;
       if (idx < nw) {
         const int64_t at = (r0 + (idx >> wlog)) * w16 + (idx & wmask);
@@ -62,6 +68,7 @@ __device__ __forceinline__ void move_rows_in_place(u32x4* k, u32x4* v, int64_t w
 
 // Cache write-back of slice (b, kvh) for both K and V, shared buffer; with
 // `moved` the surviving rows are already in place and only the new rows land.
+template <int UNROLL>
 __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const ItemPlan& pl,
                                                        int b, int kvh, int D, int e,
                                                        const u32x4* knew, const u32x4* vnew,
@@ -73,7 +80,7 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
   const int nthr = blockDim.x;
   if (pl.shift > 0) {
     if (pl.kept > 0 && !moved)
-      move_rows_in_place((u32x4*)((char*)a.present_k + off), (u32x4*)((char*)a.present_v + off),
+      move_rows_in_place<UNROLL>((u32x4*)((char*)a.present_k + off), (u32x4*)((char*)a.present_v + off),
                          w16, __builtin_ctzll(w16), pl.shift, pl.kept, tid, nthr);
     // new rows after the move (they may land on rows the move read)
     const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;
@@ -105,6 +112,7 @@ __device__ __forceinline__ void slice_writeback_shared(const AttnArgs& a, const 
 // 16 words, in LDS) to store in place of a.k's / a.v's.  `moved`: the only
 // reader of the slice has already moved the surviving rows while reading
 // them.
+template <int UNROLL = kMoveUnroll>
 __device__ __forceinline__ void slice_tail_rows(const AttnArgs& a, const ItemPlan& pl, int b,
                                                 int kvh, int D, int ce, const u32x4* knew,
                                                 const u32x4* vnew, bool moved = false) {
@@ -123,7 +131,7 @@ __device__ __forceinline__ void slice_tail_rows(const AttnArgs& a, const ItemPla
     __syncthreads();
     if (!s_last) return;
   }
-  slice_writeback_shared(a, pl, b, kvh, D, ce, knew, vnew, moved);
+  slice_writeback_shared<UNROLL>(a, pl, b, kvh, D, ce, knew, vnew, moved);
 }
 
 template <int DT>
