@@ -48,8 +48,8 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD published
 # library's launch planner picks them from the shapes: 2-query tiles x 4 per
 # KV head and 4 waves for the pages' shape, one 4-query tile and 8 waves per
 # slice for the batched serving decode)
-HEADLINE_KERNEL = "attn_decode_kernel<0, 64, 2, 4, 3, false>"
-SERVING_KERNEL = "attn_decode_kernel<2, 128, 4, 8, 3, false>"
+HEADLINE_KERNEL = "attn_decode_kernel<0, 64, 2, 4, 3, false, false>"
+SERVING_KERNEL = "attn_decode_kernel<2, 128, 4, 8, 3, false, true>"
 SERVING_INT8_KERNEL = "attn_decode_q8_kernel<2, 128, 4, 8, 1>"
 SERVING_FP8_KERNEL = "attn_decode_q8_kernel<2, 128, 4, 8, 2>"
 
