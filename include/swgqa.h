@@ -7,11 +7,11 @@
  *    (onnxruntime PR #32419), Description: with capacity C (dimension 2 of
  *    past_key), window W = local_window_size, total length T and gap
  *    G = C - W + 1, the resident length is L(T) = T for T <= C and
- *    T - G*ceil((T - C)/G) otherwise; after a step, rows [0, L) of
- *    present_key/present_value hold the L most recent positions in order
- *    (row i = absolute position T - L + i) and rows [L, C) are unspecified.
- *    Any S >= 1 is accepted, including S > C; attention_bias columns are
- *    absolute key positions (last dimension total_sequence_length).
+ *    T - G*ceil((T - C)/G) otherwise.  After a step, present row i of a
+ *    slice, 0 <= i < L(T), holds absolute position T - L(T) + i; the content
+ *    of rows L(T) .. C-1 is not defined.  S may be any value >= 1 (S > C
+ *    too), and the last dimension of attention_bias (total_sequence_length)
+ *    indexes absolute key positions.
  *  - "[CPU] Add windowed kv cache for GQA" (onnxruntime PR #31142), key design
  *    decisions: block (gap-sized) eviction, compaction skipped on drifting
  *    steps, staging of multi-token steps that would evict history their

@@ -14,7 +14,7 @@
 //  * "[CPU] Add windowed kv cache for GQA" (onnxruntime PR #31142), key design
 //    decisions: gap = C - W + 1, the drifting layout, the per-item plan
 //    (end before / end after / rows kept), staging of hazardous multi-token
-//    steps, and "numerically identical to a full-length cache".
+//    steps, and results equal to those of a full-length cache.
 //  * "GQA In-Place KV Cache: Investigation Report" (onnxruntime/mobius issue
 //    #111), sections 1.1-1.3: operator inputs/outputs, BNSH caches,
 //    seqlens_k = total length - 1, buffer-sharing modes, attributes (scale
@@ -400,8 +400,9 @@ void swgqa_oracle_resident_lengths(const int64_t* T, int64_t n, int64_t C,
   for (int64_t i = 0; i < n; ++i) out[i] = resident_length(T[i], C, W);
 }
 
-// Rollback rule, PR #32419 Description: rejecting k drafts needs no cache edit
-// and is exact when L(T - k) == L(T) - k.
+// Rollback rule ("Specify GroupQueryAttention windowed KV cache layout
+// contract", Description): dropping the last k of T positions leaves the
+// cache valid as it stands iff L(T - k) == L(T) - k.
 int swgqa_oracle_rollback_exact(int64_t T, int64_t k, int64_t C, int64_t W) {
   if (k < 0 || k > T) return 0;
   return resident_length(T - k, C, W) == resident_length(T, C, W) - k ? 1 : 0;

@@ -364,9 +364,6 @@ __device__ __forceinline__ u32x4 quant_chunk16(const void* row, int64_t c0, floa
   return r;
 }
 
-// seqlens_k[b] (uniform across the workgroup) through the scalar data cache:
-// the array is read-only for the whole launch, and one scalar fetch per CU
-// replaces a vector load from every wave.
 // op(x of lane l, x of lane l ^ 16) in every lane: v_permlane16_swap on two
 // copies of x exchanges rows 1 and 3 of the first with rows 0 and 2 of the
 // second, so each lane then holds its own value in one copy and its
@@ -388,6 +385,9 @@ __device__ __forceinline__ float reduce_xor32(float x, Op op) {
 
 __device__ __forceinline__ float add_f(float a, float b) { return a + b; }
 
+// seqlens_k[b] (uniform across the workgroup) read through the scalar data
+// cache: the array is read-only for the whole launch, and one scalar fetch per
+// CU replaces a vector load from every wave.
 __device__ __forceinline__ int32_t load_seqlen(const int32_t* seqlens, int b) {
   return ((const int32_t __attribute__((address_space(4)))*)seqlens)[b];
 }
