@@ -47,6 +47,8 @@
 #include "swgqa_tail.hpp"
 
 #include <math.h>
+#include <stdint.h>
+#include <type_traits>
 
 namespace swgqa {
 
@@ -144,17 +146,18 @@ __device__ __forceinline__ u32x4 codes_to_elems(const u32x4& c) {
 #endif
 
 // Waves per SIMD the compiler must leave room for: fp32 with rows of at
-// most 256 bytes, 4 in 8-wave workgroups (its operands fit 128 registers
-// with two blocks of loads in flight; measured faster than 2 or 3 waves) and
-// 3 in 4-wave ones (whose bias path needs a little more); otherwise no floor.
-template <int DT, int D, int NW>
+// most 256 bytes, 4 in 8-wave workgroups without bias (its operands fit 128
+// registers with two blocks of loads in flight; measured faster than 2 or 3
+// waves) and 3 otherwise (the bias path and 4-wave workgroups need a little
+// more); no floor for the other types.
+template <int DT, int D, int NW, bool BIAS>
 constexpr int chunk_min_waves() {
-  return DT == kF32 && D <= 64 ? (NW == 8 ? 4 : 3) : 1;
+  return DT == kF32 && D <= 64 ? (NW == 8 && !BIAS ? 4 : 3) : 1;
 }
 
 template <int DT, int D, bool BIAS, int NW, int CT>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(chunk_min_waves<DT, D, NW>(), 8)))
+__attribute__((amdgpu_waves_per_eu(chunk_min_waves<DT, D, NW, BIAS>(), 8)))
 void attn_chunk_kernel(AttnArgs a) {
   constexpr bool Q8 = CT != 0;
   using Sh = ChunkShape<DT, D, NW>;
@@ -417,6 +420,15 @@ void attn_chunk_kernel(AttnArgs a) {
   const int64_t vhi = (my_pos < ke - 1 ? my_pos : ke - 1) - kb;
   const int32_t vis_lo = my_ok ? (int32_t)(vlo < -(int64_t)0x7fffffff ? -0x7fffffff : vlo) : 1;
   const int32_t vis_hi = my_ok ? (int32_t)vhi : 0;
+  // the keys every query of this wave sees: [w_vis_lo, w_vis_hi] (lanes
+  // without a query do not narrow it)
+  int32_t w_vis_lo = my_ok ? vis_lo : INT32_MIN;
+  int32_t w_vis_hi = my_ok ? vis_hi : INT32_MAX;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    w_vis_lo = max(w_vis_lo, __shfl_xor(w_vis_lo, o, kWave));
+    w_vis_hi = min(w_vis_hi, __shfl_xor(w_vis_hi, o, kWave));
+  }
 
   float m_run = -INFINITY;  // log2 units, per query (same in all 4 lane groups)
   float l_run = 0.0f;       // this lane's share of the sum
@@ -478,30 +490,50 @@ void attn_chunk_kernel(AttnArgs a) {
     }
     }
 
-    // Scores: key j = j0 + 16 kt + 4 lg + r, query lq.
+    // Scores: key j = j0 + 16 kt + 4 lg + r, query lq.  Blocks every query
+    // of the wave sees whole, without softcap or bias, take the plain
+    // transform (the same roundings); the others one of two loops chosen
+    // once per block, with and without softcap.
     float smax = -INFINITY;
+    auto transform = [&](auto capc) __attribute__((always_inline)) {
+      constexpr bool CAP = decltype(capc)::value;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int32_t jr = blk * BN + kt * 16 + 4 * lg + r;
-        const bool vis = jr >= vis_lo && jr <= vis_hi;
-        float x = sc[kt][r] * qk_scale;
-        if (has_cap) {
-          const float y = x * inv_cap;
-          if constexpr (DT == kF32) {
-            x = cap * tanhf(y);
-          } else {
-            const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(
-                                       __builtin_amdgcn_exp2f(2.0f * kLog2e * fabsf(y)) + 1.0f);
-            x = cap * copysignf(t, y);
+        for (int r = 0; r < 4; ++r) {
+          const int32_t jr = blk * BN + kt * 16 + 4 * lg + r;
+          const bool vis = jr >= vis_lo && jr <= vis_hi;
+          float x = sc[kt][r] * qk_scale;
+          if constexpr (CAP) {
+            const float y = x * inv_cap;
+            if constexpr (DT == kF32) {
+              x = cap * tanhf(y);
+            } else {
+              const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(
+                                         __builtin_amdgcn_exp2f(2.0f * kLog2e * fabsf(y)) + 1.0f);
+              x = cap * copysignf(t, y);
+            }
           }
+          if (has_bias) x += bias_blk[kt * 4 + r];
+          x = vis ? x * kLog2e : -INFINITY;
+          sc[kt][r] = x;
+          smax = fmaxf(smax, x);
         }
-        if (has_bias) x += bias_blk[kt * 4 + r];
-        x = vis ? x * kLog2e : -INFINITY;
-        sc[kt][r] = x;
-        smax = fmaxf(smax, x);
-      }
+    };
+    if (!has_cap && !has_bias && blk * BN >= w_vis_lo && blk * BN + BN - 1 <= w_vis_hi) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = (sc[kt][r] * qk_scale) * kLog2e;
+          sc[kt][r] = x;
+          smax = fmaxf(smax, x);
+        }
+    } else if (has_cap) {
+      transform(std::true_type{});
+    } else {
+      transform(std::false_type{});
+    }
     auto fmax_op = [](float x, float y) { return fmaxf(x, y); };
     smax = reduce_xor16(smax, fmax_op);
     smax = reduce_xor32(smax, fmax_op);
