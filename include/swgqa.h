@@ -143,9 +143,10 @@ typedef struct {
 
 /* Bytes of device workspace swgqa_forward needs for these parameters: the
  * status word in bytes [0, 4), per-(item, KV head) arrival counters in bytes
- * [256, 16384) that every call leaves at zero, then key-split partials and,
- * with do_rotary, the rotated query and key rows and the per-item lengths
- * (scratch).  0 if the parameters are invalid.  Pure host function.  A
+ * [256, 16384) that every call leaves at zero, then key-split partials, the
+ * rows that multi-token 16-bit steps with key splits set aside while they
+ * compact the cache, and, with do_rotary, the rotated query and key rows and
+ * the per-item lengths (scratch).  0 if the parameters are invalid.  Pure host function.  A
  * workspace of at least this size serves any parameter set whose own size is
  * not larger. */
 size_t swgqa_workspace_size(const swgqa_params* params);
@@ -190,7 +191,7 @@ swgqa_status swgqa_forward(const swgqa_params* params, const void* query,
  * library, one per GPU, held until the process ends.  Nothing is allocated.
  *  - Parameters whose swgqa_workspace_size exceeds 32 MiB return
  *    SWGQA_ERR_SCRATCH before anything is enqueued (every workload here
- *    needs at most about 17 MB).
+ *    needs at most about 22 MB).
  *  - device_status: NULL, or a 4-byte aligned device word of the caller's
  *    into which device-detected item errors OR the bit that
  *    swgqa_device_status reports (sticky: the caller clears it); with NULL

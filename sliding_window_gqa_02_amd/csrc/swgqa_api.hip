@@ -216,8 +216,35 @@ size_t partial_bytes(const swgqa_params* p, const SplitPlan& s) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Rotary scratch (after the partials): rotated query rows, rotated key rows,
-// per-item lengths.
+// Rows per (item, KV head, key split, K|V) that the chunk kernel's key
+// splits set aside when they move a compacting step's surviving rows
+// themselves (one query tile per slice, a 16-bit cache in the element type):
+// the step's largest shift -- a multiple of the gap G = C - W + 1 no larger
+// than G - 1 + S, since a step keeps at least W rows once T > C -- capped at
+// kStashRows; 0 when no shift fits (every step's move is then the step
+// tail's).
+int chunk_stash_rows(const swgqa_params* p, const SplitPlan& s) {
+  if (s.kind != Kind::kChunk || p->kv_cache_type != 0 || s.ntiles != 1 || s.nsplit <= 1 ||
+      !chunk_kernel_moves_rows(p->dtype))
+    return 0;
+  const int64_t G = (int64_t)p->capacity - p->local_window_size + 1;
+  if (G > kStashRows) return 0;
+  const int64_t most = (G - 1 + p->sequence_length) / G * G;
+  return (int)std::min<int64_t>(most, kStashRows);
+}
+
+size_t stash_bytes(const swgqa_params* p, const SplitPlan& s) {
+  return (size_t)p->batch_size * p->kv_num_heads * s.nsplit * 2 * chunk_stash_rows(p, s) *
+         p->head_size * elem_bytes(p->dtype);
+}
+
+// Start of the scratch after the header, the split partials and the stash.
+size_t scratch_start(const swgqa_params* p, const SplitPlan& s) {
+  return kHeaderBytes + align256(partial_bytes(p, s)) + align256(stash_bytes(p, s));
+}
+
+// Rotary scratch (after the partials and the stash): rotated query rows,
+// rotated key rows, per-item lengths.
 struct RotaryScratch {
   size_t q_off, k_off, seq_off, end;
   size_t kq_off, vq_off;  // int8 codes of the new rows (chunk kernel over an int8 cache)
@@ -253,12 +280,12 @@ bool ranges_partially_overlap(const void* a, const void* b, size_t n) {
 size_t workspace_bytes_for(const swgqa_params* p) {
   if (validate(p) != SWGQA_OK) return 0;
   const SplitPlan s = plan_split(p);
-  return rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s)), s).end;
+  return rotary_scratch(p, scratch_start(p, s), s).end;
 }
 
 // Workspace of swgqa_forward_noalloc: 32 MiB, enough for every workload
 // measured here (the largest, multi-token steps with key splits, needs
-// about 17 MB).
+// about 22 MB).
 constexpr size_t kScratchBytes = (size_t)32 << 20;
 
 }  // namespace
@@ -301,7 +328,7 @@ swgqa_status forward_impl(const swgqa_params* p, const void* query, const void* 
   if (align_or & 15u) return SWGQA_ERR_ARG;
 
   const SplitPlan s = plan_split(p);
-  const RotaryScratch rs = rotary_scratch(p, kHeaderBytes + align256(partial_bytes(p, s)), s);
+  const RotaryScratch rs = rotary_scratch(p, scratch_start(p, s), s);
   if (workspace_bytes < rs.end) return SWGQA_ERR_ARG;
   if (p->do_rotary && (!cos_cache || !sin_cache)) return SWGQA_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
@@ -373,6 +400,9 @@ swgqa_status forward_impl(const swgqa_params* p, const void* query, const void* 
                     p->head_size;
   a.present_k = shared ? present_key : nullptr;
   a.present_v = shared ? present_value : nullptr;
+  a.stash_rows = shared ? chunk_stash_rows(p, s) : 0;
+  a.stash = a.stash_rows > 0 ? (char*)workspace + kHeaderBytes + align256(partial_bytes(p, s))
+                             : nullptr;
   a.B = p->batch_size;
   a.S = p->sequence_length;
   a.Hq = p->num_heads;

@@ -12,6 +12,16 @@ bool chunk_kernel_supports(int dtype, int D) {
 
 int chunk_rows_per_workgroup(int waves) { return 16 * waves; }
 int chunk_keys_per_block() { return BN; }
+static_assert(BN == kChunkBlockKeys, "key split ranges of the step tail");
+
+bool chunk_kernel_moves_rows(int dtype) {
+  switch (dtype) {
+    case kF32: return chunk_split_moves<kF32, 0>();
+    case kF16: return chunk_split_moves<kF16, 0>();
+    case kBF16: return chunk_split_moves<kBF16, 0>();
+    default: return false;
+  }
+}
 
 hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t st) {
   switch (dtype) {

@@ -145,6 +145,19 @@ __device__ __forceinline__ u32x4 codes_to_elems(const u32x4& c) {
 #define SWGQA_CHUNK_DB_ALL 0
 #endif
 
+// Blocks of loads in flight, 16-bit rows of under 512 bytes.
+#ifndef SWGQA_CHUNK_RING16
+#define SWGQA_CHUNK_RING16 3
+#endif
+
+// Two LDS buffers per block (fp32), else one staged between two barriers.
+template <int DT>
+constexpr bool chunk_double_buffer() { return SWGQA_CHUNK_DB_ALL || DT == kF32; }
+// Whether the kernel's key splits can move a compacting slice's surviving
+// rows (one LDS buffer, a cache in the element type).
+template <int DT, int CT>
+constexpr bool chunk_split_moves() { return !chunk_double_buffer<DT>() && CT == 0; }
+
 // Waves per SIMD the compiler must leave room for: fp32 with rows of at
 // most 256 bytes, 4 in 8-wave workgroups without bias (its operands fit 128
 // registers with two blocks of loads in flight; measured faster than 2 or 3
@@ -175,7 +188,7 @@ void attn_chunk_kernel(AttnArgs a) {
   // DB (fp32): two K/V buffers, block blk staged in buffer blk & 1 while the
   // other holds the block being computed; 16-bit types stage every block in
   // one buffer between two barriers (measured faster for them)
-  constexpr bool DB = SWGQA_CHUNK_DB_ALL || DT == kF32;
+  constexpr bool DB = chunk_double_buffer<DT>();
   constexpr int NBUF = DB ? 2 : 1;
   __shared__ __attribute__((aligned(16))) LT sK[NBUF * Sh::KELEMS];
   __shared__ __attribute__((aligned(16))) LT sV[NBUF * Sh::VELEMS];
@@ -321,6 +334,36 @@ void attn_chunk_kernel(AttnArgs a) {
   const uint64_t bias_lane =
       BIAS ? (uint64_t)a.bias + (uint64_t)((bias_row + 4 * lg) * e) : 0;
   const int64_t cache_end = pl.P < ke ? pl.P : ke;  // keys below this are cache rows
+
+  // Compaction by the key splits (16-bit cache; the host gives a stash only
+  // to one-tile launches over a shared buffer, and both sides take the same
+  // per-item decision): the surviving rows this split reads, positions
+  // [mv_lo, mv_hi), are stored at their new place pos - shift from the block
+  // registers once their block is staged -- every load of that block and of
+  // the blocks before it has completed by then, and the blocks still to come
+  // lie above every row it overwrites; no other split reads this split's
+  // rows -- except those below mv_stash, whose new place lies in the previous
+  // split's part, possibly still being read: they go to this split's stash
+  // slots (pos - kb) for the step tail to store.
+  constexpr bool kCanMove = chunk_split_moves<DT, CT>();
+  bool fmove = false;
+  int64_t mv_lo = 0, mv_hi = 0, mv_stash = 0;
+  uint64_t mv_k = 0, mv_v = 0, st_k = 0, st_v = 0;
+  if constexpr (kCanMove) {
+    fmove = a.stash != nullptr && chunk_moves_rows(pl, a.W, a.stash_rows);
+    if (fmove) {
+      mv_lo = base + pl.shift > kb ? base + pl.shift : kb;
+      mv_hi = cache_end;
+      mv_stash = split > 0 ? kb + pl.shift : kb;
+      const int64_t slice_off = (int64_t)(b * a.Hkv + kvh) * a.C * kRowB;
+      mv_k = (uint64_t)((char*)a.present_k + slice_off - (base + pl.shift) * kRowB);
+      mv_v = (uint64_t)((char*)a.present_v + slice_off - (base + pl.shift) * kRowB);
+      const int64_t slot = ((int64_t)(b * a.Hkv + kvh) * a.nsplit + split) * 2 * a.stash_rows;
+      st_k = (uint64_t)((char*)a.stash + (slot - kb) * kRowB);
+      st_v = (uint64_t)((char*)a.stash + (slot + a.stash_rows - kb) * kRowB);
+    }
+  }
+
   auto load_block = [&](int64_t j0, BlockRegs& rg) __attribute__((always_inline)) {
     if (j0 + BN <= cache_end) {  // uniform
       const uint64_t boff = (uint64_t)(j0 * kRowB);
@@ -412,6 +455,23 @@ void attn_chunk_kernel(AttnArgs a) {
           ((uint16_t*)bV)[(d0 + 2 * w + 1) * VS + kx] = (uint16_t)(vw[w] >> 16);
         }
       }
+    }
+  };
+
+  // The block's surviving rows to their new place (or the stash).
+  auto move_block = [&](int blk, const BlockRegs& rg) __attribute__((always_inline)) {
+    const int64_t j0 = kb + (int64_t)blk * BN;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * kThreads;
+      if constexpr (Sh::CHUNKS % kThreads != 0)
+        if (c >= Sh::CHUNKS) continue;
+      const int64_t pos = j0 + c / CPR;
+      if (pos < mv_lo || pos >= mv_hi) continue;
+      const bool st = pos < mv_stash;
+      const uint64_t off = (uint64_t)(pos * kRowB + (c % CPR) * kPartB);
+      store16_global<SWGQA_FM_NT>((st ? st_k : mv_k) + off, rg.k[u]);
+      store16_global<SWGQA_FM_NT>((st ? st_v : mv_v) + off, rg.v[u]);
     }
   };
 
@@ -673,7 +733,7 @@ void attn_chunk_kernel(AttnArgs a) {
   float bias_cur[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   // (fp32, and 16-bit rows of 512 bytes: two, which keeps them within the
   // registers of their occupancy)
-  constexpr int RING = (DT == kF32 || D * e >= 512) ? 2 : 3;
+  constexpr int RING = (DT == kF32 || D * e >= 512) ? 2 : SWGQA_CHUNK_RING16;
   auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
     compute_block(blk, bias_cur);
     store_block(rg, (blk + 1) & 1);
@@ -688,6 +748,8 @@ void attn_chunk_kernel(AttnArgs a) {
     store_block(rg, 0);
     block_bias(blk, rg, bias_cur);
     __syncthreads();
+    if constexpr (kCanMove)
+      if (fmove) move_block(blk, rg);
     load_block(block_start(blk + RING), rg);
     compute_block(blk, bias_cur);
   };

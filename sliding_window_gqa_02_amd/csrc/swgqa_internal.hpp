@@ -55,7 +55,20 @@ struct AttnArgs {
   int32_t* seqlens_out;    // per-item lengths for the step tail (-2: bad position), or NULL
   // int8 cache (the int8 decode kernel): element = code * scale
   float k_scale, v_scale;
+  // 16-bit chunk kernel, key splits over one query tile per slice, shared
+  // buffer (else NULL): on compacting steps whose surviving rows all lie in
+  // the key band and whose shift is at most stash_rows, the split that reads
+  // a surviving row stores it at its new place -- except rows whose new place
+  // lies in an earlier split's part, which go here, (item, KV head, split,
+  // K|V, stash_rows rows), for the step tail to store
+  void* stash;
+  int32_t stash_rows;
 };
+
+// Keys per LDS block of the chunk kernel.
+constexpr int kChunkBlockKeys = 32;
+// Largest stash_rows (rows set aside per item, KV head, key split and K|V).
+constexpr int kStashRows = 64;
 
 struct CopyArgs {
   const void* past_k;
@@ -102,6 +115,8 @@ hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
 bool chunk_kernel_supports(int dtype, int D);
 int chunk_rows_per_workgroup(int waves);  // 4 or 8 waves
 int chunk_keys_per_block();
+// Whether the kernel (cache in the element type) honours AttnArgs::stash.
+bool chunk_kernel_moves_rows(int dtype);
 hipError_t launch_attn_chunk(int dtype, int D, const AttnArgs& a, hipStream_t stream);
 // The same kernel over an int8 / fp8 E4M3 cache (swgqa_attn_chunk_q8.hip,
 // swgqa_attn_chunk_f8.hip); a.k / a.v hold the step's new rows as codes

@@ -22,7 +22,9 @@
 // overlaps itself whenever kept > shift; it is done per (item, KV head,
 // K|V, column part) with the pass-wise register-staged move of
 // swgqa_tail.hpp.  The append waits for the whole move, since new rows may
-// land on rows the move still reads.
+// land on rows the move still reads.  After a 16-bit chunk step with key
+// splits that moved the surviving rows itself, only the rows it set aside
+// (those whose new place another split was still to read) are stored here.
 #include "swgqa_common.hpp"
 #include "swgqa_internal.hpp"
 #include "swgqa_tail.hpp"
@@ -53,20 +55,15 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t bl
   const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (pl.ok) {
-    // Splits in groups of kMergeGroup whose loads are all issued before any
-    // is used (one memory round trip per group, not per split); indices past
-    // the last split repeat it and are not summed.
+    // Splits in groups of kMergeGroup whose loads (pairs and partials) are
+    // all issued before any is used: one memory round trip per group, not
+    // per split or per pass.  The group's largest m joins the running one,
+    // the sums so far are rescaled to it, and the group's terms are added;
+    // indices past the last split repeat it and are not summed.
     const int64_t r0 = (int64_t)row * a.nsplit;
     const int ns = a.nsplit;
     const float2* ml2 = (const float2*)a.ml;
     float M = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += kMergeGroup) {
-      float2 v[kMergeGroup];
-#pragma unroll
-      for (int j = 0; j < kMergeGroup; ++j) v[j] = ml2[r0 + min(s0 + j, ns - 1)];
-#pragma unroll
-      for (int j = 0; j < kMergeGroup; ++j) M = fmaxf(M, v[j].x);
-    }
     float L = 0.0f;
     float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < ns; s0 += kMergeGroup) {
@@ -78,6 +75,16 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t bl
         v[j] = ml2[s];
         p[j] = *(const float4*)(a.opart + s * D + d);
       }
+      float Mg = M;
+#pragma unroll
+      for (int j = 0; j < kMergeGroup; ++j) Mg = fmaxf(Mg, v[j].x);
+      if (s0 > 0) {
+        const float r = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mg);
+        L *= r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[i] *= r;
+      }
+      M = Mg;
 #pragma unroll
       for (int j = 0; j < kMergeGroup; ++j) {
         const bool in = s0 + j < ns;
@@ -103,9 +110,11 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t bl
 }
 
 // Write-back of one (item, KV head, K|V, column part).  With an int8 cache
-// the new rows are quantized as they are written (16 codes per word).
+// the new rows are quantized as they are written (16 codes per word).  `at`
+// is the attention launch's arguments (its key splits and stash).
 template <int DT>
-__device__ __forceinline__ void writeback_part(const CopyArgs& a, uint32_t idx) {
+__device__ __forceinline__ void writeback_part(const CopyArgs& a, const AttnArgs& at,
+                                               uint32_t idx) {
   const int64_t rowb = (int64_t)a.D * a.elem_bytes;
   const int64_t w16 = rowb / 16;  // 16-byte words per row (a power of two)
   const int ncol = writeback_columns((int)w16);
@@ -132,7 +141,27 @@ __device__ __forceinline__ void writeback_part(const CopyArgs& a, uint32_t idx) 
   const int tid = threadIdx.x;
 
   // 1. Surviving old rows: [shift, shift + kept) -> [0, kept).
-  if (pl.kept > 0 && (!shared || pl.shift > 0)) {
+  if (shared && at.stash && chunk_moves_rows(pl, at.W, at.stash_rows)) {
+    // moved by the chunk kernel's key splits but for the first `shift`
+    // positions of every split after the first, set aside in its stash
+    // slots (pos - kb); they land on the previous split's rows
+    const int64_t rowsz = pl.shift * wn;  // words of one split's slots
+    const int64_t nw = (at.nsplit - 1) * rowsz;
+    const int64_t lo_keep = pl.P - pl.Lb + pl.shift;  // first surviving position
+    for (int64_t i = tid; i < nw; i += kTailThreads) {
+      const int s = 1 + (int)(i / rowsz);
+      const int64_t r = (i % rowsz) >> wlog;
+      const int64_t w = i & (wn - 1);
+      int64_t kb, ke;
+      chunk_split_range(pl, a.S, at.W, at.nsplit, s, kb, ke);
+      const int64_t pos = kb + r;
+      if (pos < lo_keep || pos >= ke || pos >= pl.P) continue;
+      const int64_t slot = ((((int64_t)b * a.Hkv + kvh) * at.nsplit + s) * 2 + which) *
+                               at.stash_rows + r;
+      dst[(pos - lo_keep) * w16 + w] =
+          ((const u32x4*)((const char*)at.stash + slot * rowb) + col * wn)[w];
+    }
+  } else if (pl.kept > 0 && (!shared || pl.shift > 0)) {
     if (shared) {
       move_rows_in_place(dst, nullptr, w16, wlog, pl.shift, pl.kept, tid, kTailThreads);
     } else {
@@ -184,7 +213,7 @@ template <int DT>
 __global__ __launch_bounds__(kTailThreads) void step_tail_kernel(AttnArgs a, CopyArgs c,
                                                                  uint32_t merge_blocks) {
   if (blockIdx.x < merge_blocks) merge_rows<DT>(a, c.D, blockIdx.x);
-  else writeback_part<DT>(c, blockIdx.x - merge_blocks);
+  else writeback_part<DT>(c, a, blockIdx.x - merge_blocks);
 }
 
 }  // namespace

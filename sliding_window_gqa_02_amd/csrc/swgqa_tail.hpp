@@ -134,6 +134,31 @@ __device__ __forceinline__ void slice_tail_rows(const AttnArgs& a, const ItemPla
   slice_writeback_shared<UNROLL>(a, pl, b, kvh, D, ce, knew, vnew, moved);
 }
 
+// Key range of split `split` (of nsplit) of a slice read as one query tile
+// by the chunk kernel: the band [max(P - W + 1, 0), P + S - 1] cut into
+// parts of whole kChunkBlockKeys-key blocks (the kernel's split rule).
+__device__ __forceinline__ void chunk_split_range(const ItemPlan& pl, int S, int W, int nsplit,
+                                                  int split, int64_t& kb, int64_t& ke) {
+  const int64_t p_last = pl.P + S - 1;
+  const int64_t lo = pl.P - W + 1 > 0 ? pl.P - W + 1 : 0;
+  const int64_t nkeys = p_last - lo + 1;
+  const int64_t per = ((nkeys + nsplit - 1) / nsplit + kChunkBlockKeys - 1) / kChunkBlockKeys *
+                      kChunkBlockKeys;
+  kb = lo + split * per;
+  ke = kb + per < p_last + 1 ? kb + per : p_last + 1;
+}
+
+// Whether the key splits of a one-tile chunk step move the surviving rows of
+// this item themselves: a compacting step (shift > 0, kept > 0) whose shift
+// fits the rows set aside per split, and whose surviving rows -- positions
+// P - Lb + shift .. P - 1 -- all lie in the key band (so every one of them is
+// read, and stored, by exactly one split).
+__device__ __forceinline__ bool chunk_moves_rows(const ItemPlan& pl, int W, int stash_rows) {
+  const int64_t lo = pl.P - W + 1 > 0 ? pl.P - W + 1 : 0;
+  return pl.shift > 0 && pl.kept > 0 && pl.shift <= stash_rows &&
+         pl.P - pl.Lb + pl.shift >= lo;
+}
+
 template <int DT>
 __device__ __forceinline__ void slice_tail(const AttnArgs& a, const ItemPlan& pl, int b, int kvh,
                                            int D, const u32x4* knew = nullptr,

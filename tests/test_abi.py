@@ -87,6 +87,25 @@ def test_workspace_size():
     assert sw.workspace_size(sw.make_params(1, 1, 2, 2, 12, 6, 4, 8)) == 0
 
 
+def test_workspace_holds_the_split_stash():
+    """Multi-token 16-bit steps with key splits over one query tile per slice
+    reserve, per (item, KV head, split, K|V), the step's largest shift in rows
+    -- a multiple of the gap G = C - W + 1 no larger than G - 1 + S, at most
+    64 -- and nothing once G exceeds 64; the fp32 step (same kernel, same
+    partials) reserves none."""
+    def extra_rows(S, C, W):
+        f16 = sw.workspace_size(sw.make_params(4, S, 32, 8, 128, C, W, C + 100, sw.F16))
+        f32 = sw.workspace_size(sw.make_params(4, S, 32, 8, 128, C, W, C + 100, sw.F32))
+        assert f16 > 0 and f32 > 0
+        rows, rem = divmod(f16 - f32, 4 * 8 * 2 * 128 * 2)
+        assert rem == 0
+        return rows
+    for S, C, most in [(32, 1032, 36), (8, 1032, 9), (32, 1087, 64), (16, 1024, 16)]:
+        rows = extra_rows(S, C, 1024)
+        assert rows > 0 and rows % most == 0, (S, C, rows)
+    assert extra_rows(32, 1088, 1024) == 0  # G = 65
+
+
 def test_host_validation_without_gpu():
     lib = sw.load()
     buf = np.zeros(1 << 12, np.float32)

@@ -508,6 +508,57 @@ def test_chunk_key_splits_long_window():
     say(f"  worst scaled error {run.worst:.3g}")
 
 
+# Key splits of a one-tile chunk step that move the surviving rows as they
+# read them (16-bit cache, shared buffer): each split stores its kept rows at
+# their new place, the first `shift` of them (whose new place lies in the
+# previous split's part) through a stash that the step tail stores.  Shapes:
+# verify and chunked-prefill steps at gap 9 with bias, gap 1 (every step
+# compacts by S), 512-byte rows, shifts over the 64-row stash (66 rows: the
+# step tail moves every row), and compactions that keep rows below the key
+# band (the step tail moves every row); ragged items compact on different
+# steps.
+SPLIT_MOVE = [
+    (Cfg(B=2, Hq=8, Hkv=2, D=128, C=508, W=500, seed=161, dtype=synth.F16), [32, 8, 8, 32, 8], True),
+    (Cfg(B=2, Hq=16, Hkv=2, D=64, C=300, W=300, seed=162, dtype=synth.BF16, softcap=30.0),
+     [16, 8, 16], False),
+    (Cfg(B=1, Hq=8, Hkv=2, D=256, C=419, W=400, seed=163, dtype=synth.F16), [16, 8], False),
+    (Cfg(B=2, Hq=4, Hkv=2, D=128, C=432, W=400, seed=164, dtype=synth.BF16), [64, 16, 64], False),
+    (Cfg(B=2, Hq=8, Hkv=2, D=64, C=329, W=300, seed=165, dtype=synth.F16), [16, 20], True),
+]
+
+
+@pytest.mark.parametrize("cfg,steps,with_bias", SPLIT_MOVE,
+                         ids=lambda c: f"W{c.W}G{c.C - c.W + 1}D{c.D}t{c.dtype}"
+                         if isinstance(c, Cfg) else "")
+def test_chunk_key_splits_move_while_reading(cfg, steps, with_bias):
+    import sliding_window_gqa_02_amd as sw
+    G = cfg.C - cfg.W + 1
+    if cfg.D <= 128:
+        # the stash is planned: the 16-bit step's workspace exceeds that of
+        # the fp32 step (same kernel and partials, no stash) by it
+        ws = [sw.workspace_size(sw.make_params(cfg.B, steps[0], cfg.Hq, cfg.Hkv, cfg.D, cfg.C,
+                                               cfg.W, cfg.C + 4 * G, dt, 0.0, 0.0, 1, 1))
+              for dt in (cfg.dtype, synth.F32)]
+        assert ws[0] > ws[1] > 0, ws
+    syn = cfg.synth()
+    vers = Versions(cfg.B, n=cfg.C + 40 * max(steps) + 64)
+    P = np.array([cfg.C - 5 - 7 * b for b in range(cfg.B)], dtype=np.int64)
+    K, V = seeded_cache(cfg, syn, P, vers)
+    run = Lockstep(cfg, K=K, V=V, vers=vers)
+    n = 4 * len(steps) + 4
+    say(f"split-move {cfg}: G={G}, {n} steps from P={list(P)}")
+    events = 0
+    for i in range(n):
+        S = steps[i % len(steps)]
+        total = int((P + S).max())
+        bias = _bias_nan_outside(cfg, syn, P, S, total) if with_bias and i % 2 == 0 else None
+        _, _, plan = run.step(P, S, bias=bias, total=total, check_regen=(i % 3 == 0))
+        events += int((plan[:, 5] > 0).sum())
+        P = P + S
+    say(f"  {events} compaction events, worst scaled error {run.worst:.3g}")
+    assert events >= 2 * cfg.B
+
+
 # ---------------------------------------------------------------------------
 # Softmax sink (head_sink per query head, or smooth_softmax's logit 0) on
 # every output path: whole-slice decode and MFMA chunks (fp32, bf16), the
