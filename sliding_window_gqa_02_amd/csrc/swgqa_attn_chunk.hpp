@@ -61,6 +61,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+// C += A B over a reduction of 32 (gfx950's 16x16x32 products, twice the
+// work per instruction of the 16x16x16 ones): lane i + 16 g holds row i of A
+// and column i of B, each at reduction elements 8 g .. 8 g + 7 in its 8
+// halves, so any assignment of reduction indices to (g, element) that A and
+// B share gives the same sum.
+template <int DT>
+__device__ __forceinline__ f4 mfma_x32(const uint4& a, const uint4& b, const f4& c) {
+  if constexpr (DT == kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a),
+                                                  __builtin_bit_cast(h8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a),
+                                                   __builtin_bit_cast(b8, b), c, 0, 0, 0);
+}
 
 template <int DT, int D, int NW>
 struct ChunkShape {
@@ -86,6 +103,25 @@ template <> struct LdsT<kBF16> { using T = uint16_t; };
 // Key swizzle of row d of the transposed V tile (16-bit types): XOR of key
 // bits 2..4 with d / 8, so groups of 4 consecutive keys stay contiguous.
 __device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) << 2; }
+
+// Key and 16-byte part of chunk c of a staged block whose rows are CPR
+// chunks long.  In every 64 chunks (one wave's), lane group g = (c / 16) % 4
+// holds key 4 q + g at the same parts as the other three groups (keys 4 q ..
+// 4 q + 3: what the transposed V store exchanges across lane groups), and
+// the 16 lanes of a group run along rows, so each row's chunks stay
+// contiguous in memory.
+template <int CPR>
+__device__ __forceinline__ int chunk_key(int c) {
+  const int g = (c >> 4) & 3, p = c & 15, unit = c >> 6;
+  if constexpr (CPR >= 16) return 4 * (unit / (CPR / 16)) + g;
+  else return 4 * (unit * (16 / CPR) + p / CPR) + g;
+}
+template <int CPR>
+__device__ __forceinline__ int chunk_part(int c) {
+  const int p = c & 15, unit = c >> 6;
+  if constexpr (CPR >= 16) return 16 * (unit % (CPR / 16)) + p;
+  else return p % CPR;
+}
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   union { _Float16 h; uint16_t u; } c;
@@ -227,15 +263,27 @@ void attn_chunk_kernel(AttnArgs a) {
   // Q^T operand: fp32 step s holds Q[q][(D / 4) lg + s] (the steps split
   // the head dimension as d = (D / 4) k + s over the 4 reduction lanes k, so
   // a lane's K and Q operands are D / 4 consecutive elements); 16-bit step s
-  // holds Q[q][16s + 4lg .. +3].
+  // holds Q[q][32s + 8lg .. +7] (16x16x32 products; D = 16: Q[q][4lg .. +3],
+  // one 16x16x16 product).
+  constexpr bool QX32 = DT != kF32 && D % 32 == 0;
+  constexpr int QST = QX32 ? D / 32 : DSTEPS;  // 16-bit S^T MFMA steps
   const char* qrow = (const char*)a.q + ((((int64_t)b * a.S + my_i) * a.Hq + my_h) * D) * e;
   float qf[DT == kF32 ? DSTEPS : 1];
-  uint32_t qh[DT == kF32 ? 1 : DSTEPS][2];
+  uint32_t qh[DT == kF32 ? 1 : QST][QX32 ? 4 : 2];
   if constexpr (DT == kF32) {
 #pragma unroll
     for (int s = 0; s < DSTEPS; s += 4) {
       const f4 v = *(const f4*)((const float*)qrow + DSTEPS * lg + s);
       qf[s] = v[0]; qf[s + 1] = v[1]; qf[s + 2] = v[2]; qf[s + 3] = v[3];
+    }
+  } else if constexpr (QX32) {
+#pragma unroll
+    for (int s = 0; s < QST; ++s) {
+      const uint4 v = *(const uint4*)(qrow + (32 * s + 8 * lg) * 2);
+      qh[s][0] = v.x;
+      qh[s][1] = v.y;
+      qh[s][2] = v.z;
+      qh[s][3] = v.w;
     }
   } else {
 #pragma unroll
@@ -298,10 +346,10 @@ void attn_chunk_kernel(AttnArgs a) {
       : 0;
 
   // Block loads into registers, issued unconditionally (so the compiler can
-  // wait for exactly the loads it needs): chunk c of the block = key c / CPR,
-  // 16-byte part c % CPR; keys past the band's end are clamped to its last
-  // key (finite data the mask removes); chunks past the block repeat the last
-  // one and are not stored.  The attention_bias entries this lane scores in
+  // wait for exactly the loads it needs): chunk c of the block = key
+  // chunk_key(c), 16-byte part chunk_part(c); keys past the band's end are
+  // clamped to its last key (finite data the mask removes); chunks past the
+  // block repeat the last one and are not stored.  The attention_bias entries this lane scores in
   // the block (keys j0 + 16 kt + 4 lg + r) come with them.
   // The bias entries stay raw words until the block is computed: converting
   // them where they are loaded would make every block wait for all loads in
@@ -320,16 +368,17 @@ void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
-    const uint64_t off = (uint64_t)(((int64_t)(c / CPR) - base) * kRowB + (c % CPR) * kPartB);
+    const uint64_t off = (uint64_t)(((int64_t)chunk_key<CPR>(c) - base) * kRowB +
+                                    chunk_part<CPR>(c) * kPartB);
     kc_lane[u] = ck + off;
     vc_lane[u] = cv + off;
   }
-  // and of new rows: key c / CPR at new row (j0 - P) + key, part c % CPR
+  // and of new rows: the chunk's key at new row (j0 - P) + key
   uint32_t nw_lane[CPT];
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
-    nw_lane[u] = (uint32_t)((c / CPR) * new_stride + (c % CPR) * kPartB);
+    nw_lane[u] = (uint32_t)(chunk_key<CPR>(c) * new_stride + chunk_part<CPR>(c) * kPartB);
   }
   const uint64_t bias_lane =
       BIAS ? (uint64_t)a.bias + (uint64_t)((bias_row + 4 * lg) * e) : 0;
@@ -393,7 +442,7 @@ void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const int c = min(tid + u * kThreads, Sh::CHUNKS - 1);
-        const int key = c / CPR, part = c % CPR;
+        const int key = chunk_key<CPR>(c), part = chunk_part<CPR>(c);
         const int64_t j = min(j0 + key, ke - 1);
         const bool in_cache = j < pl.P;
         const uint64_t msk = 0ull - (uint64_t)in_cache;
@@ -435,7 +484,7 @@ void attn_chunk_kernel(AttnArgs a) {
       const int c = tid + u * kThreads;
       if constexpr (Sh::CHUNKS % kThreads != 0)
         if (c >= Sh::CHUNKS) continue;
-      const int key = c / CPR, part = c % CPR;
+      const int key = chunk_key<CPR>(c), part = chunk_part<CPR>(c);
       const int d0 = part * (16 / e);
       const u32x4 kw = Q8 ? codes_to_elems<DT, CT>(rg.k[u]) : rg.k[u];
       const u32x4 vw = Q8 ? codes_to_elems<DT, CT>(rg.v[u]) : rg.v[u];
@@ -446,14 +495,42 @@ void attn_chunk_kernel(AttnArgs a) {
       } else {
         // K rows are 16-byte aligned: one store per chunk
         *(u32x4*)((uint16_t*)bK + key * KS + d0) = kw;
-        // V transposed, sV[d][key ^ swz(d)]: the 16 parts of a key row land
-        // on rows 8 apart, which the swizzle spreads over the banks
-        const int kx = key ^ vt_swizzle(d0);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          ((uint16_t*)bV)[(d0 + 2 * w) * VS + kx] = (uint16_t)(vw[w] & 0xFFFFu);
-          ((uint16_t*)bV)[(d0 + 2 * w + 1) * VS + kx] = (uint16_t)(vw[w] >> 16);
+        // V transposed, sV[d][key ^ swz(d)].  The wave's 4 lane groups hold
+        // keys 4q .. 4q + 3 at the same columns d0 .. d0 + 7, word w = columns
+        // d0 + 2w, + 1: a 4x4 exchange of the words across lane groups (two
+        // swaps of lane halves, two of lane rows; every lane of the wave
+        // takes part) leaves group g with word g of all 4 keys, i.e. columns
+        // d0 + 2g and d0 + 2g + 1 of keys 4q .. 4q + 3: two 8-byte rows.
+        const int g = (tid >> 4) & 3;
+        uint32_t w0 = vw[0], w1 = vw[1], w2 = vw[2], w3 = vw[3];
+        {
+          const auto r = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+          w0 = r[0];
+          w2 = r[1];
         }
+        {
+          const auto r = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+          w1 = r[0];
+          w3 = r[1];
+        }
+        {
+          const auto r = __builtin_amdgcn_permlane16_swap(w0, w1, false, false);
+          w0 = r[0];
+          w1 = r[1];
+        }
+        {
+          const auto r = __builtin_amdgcn_permlane16_swap(w2, w3, false, false);
+          w2 = r[0];
+          w3 = r[1];
+        }
+        // word i now holds key 4q + i; columns d0 + 2g (low halves) and
+        // d0 + 2g + 1 (high halves)
+        const int col = (key - g) ^ vt_swizzle(d0);
+        uint16_t* const vr = (uint16_t*)bV + (d0 + 2 * g) * VS + col;
+        *(uint2*)vr = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x05040100u),
+                                 __builtin_amdgcn_perm(w3, w2, 0x05040100u));
+        *(uint2*)(vr + VS) = make_uint2(__builtin_amdgcn_perm(w1, w0, 0x07060302u),
+                                        __builtin_amdgcn_perm(w3, w2, 0x07060302u));
       }
     }
   };
@@ -466,10 +543,10 @@ void attn_chunk_kernel(AttnArgs a) {
       const int c = tid + u * kThreads;
       if constexpr (Sh::CHUNKS % kThreads != 0)
         if (c >= Sh::CHUNKS) continue;
-      const int64_t pos = j0 + c / CPR;
+      const int64_t pos = j0 + chunk_key<CPR>(c);
       if (pos < mv_lo || pos >= mv_hi) continue;
       const bool st = pos < mv_stash;
-      const uint64_t off = (uint64_t)(pos * kRowB + (c % CPR) * kPartB);
+      const uint64_t off = (uint64_t)(pos * kRowB + chunk_part<CPR>(c) * kPartB);
       store16_global<SWGQA_FM_NT>((st ? st_k : mv_k) + off, rg.k[u]);
       store16_global<SWGQA_FM_NT>((st ? st_v : mv_v) + off, rg.v[u]);
     }
@@ -523,6 +600,27 @@ void attn_chunk_kernel(AttnArgs a) {
             for (int t = 0; t < 4; ++t)
               acc = __builtin_amdgcn_mfma_f32_16x16x4f32(k4[t], qf[s + t], acc, 0, 0, 0);
           }
+        }
+        sc[kt] = acc;
+      }
+    } else if constexpr (QX32) {
+      // lane: key row 16 kt + lq, elements 32 s + 8 lg .. +7; two
+      // accumulators per tile (even and odd steps) shorten the dependent
+      // chains of products
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (kt == 0 || tile1) {
+          const uint16_t* kr = (const uint16_t*)bK + (kt * 16 + lq) * KS + 8 * lg;
+          f4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < QST; ++s) {
+            const uint4 kv = *(const uint4*)(kr + 32 * s);
+            const uint4 qv = make_uint4(qh[s][0], qh[s][1], qh[s][2], qh[s][3]);
+            if (s % 2 == 0) acc = mfma_x32<DT>(kv, qv, acc);
+            else acc1 = mfma_x32<DT>(kv, qv, acc1);
+          }
+          if constexpr (QST > 1) acc += acc1;
         }
         sc[kt] = acc;
       }
@@ -625,10 +723,10 @@ void attn_chunk_kernel(AttnArgs a) {
     }
 
     // O^T += V^T . P^T
+    if constexpr (DT == kF32) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (kt == 1 && !tile1) break;
-      if constexpr (DT == kF32) {
+      for (int kt = 0; kt < 2; ++kt) {
+        if (kt == 1 && !tile1) break;
         // fp32: O^T tile dt holds rows d = DT16 i + dt, so a lane's V
         // operands for all tiles are DT16 consecutive elements of one key
 #pragma unroll
@@ -651,42 +749,47 @@ void attn_chunk_kernel(AttnArgs a) {
           for (int dt = 0; dt < DT16; ++dt)
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[dt], sc[kt][t4], o[dt], 0, 0, 0);
         }
+      }
+    } else {
+      // One 16x16x32 product per O^T tile over the block's 32 keys: lane
+      // group lg's reduction elements are keys 4lg .. 4lg + 3 and 16 + 4lg ..
+      // + 3, the keys its scores hold.  P is 0 on masked keys, and on the
+      // whole second tile when it lies past the band (whose V rows are
+      // clamped copies of the band's last row: finite).
+      uint32_t pw[4], pl2[4];
+      if constexpr (DT == kF16) {
+        pw[0] = p16[0][0];
+        pw[1] = p16[0][1];
+        pw[2] = p16[1][0];
+        pw[3] = p16[1][1];
       } else {
-        uint32_t pw[2], pl2[2];
-        if constexpr (DT == kF16) {
-          pw[0] = p16[kt][0];
-          pw[1] = p16[kt][1];
-        } else {
-          // bf16 keeps 8 significant bits, too few for P: P = hi + lo, both
-          // bf16, and two products (relative error ~2^-17)
+        // bf16 keeps 8 significant bits, too few for P: P = hi + lo, both
+        // bf16, and two products (relative error ~2^-17)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
           uint16_t hi[4], lo[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             hi[r] = f32_to_bf16(sc[kt][r]);
             lo[r] = f32_to_bf16(sc[kt][r] - __uint_as_float((uint32_t)hi[r] << 16));
           }
-          pw[0] = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
-          pw[1] = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
-          pl2[0] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-          pl2[1] = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+          pw[2 * kt] = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+          pw[2 * kt + 1] = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+          pl2[2 * kt] = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+          pl2[2 * kt + 1] = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
         }
+      }
+      const uint4 pv = make_uint4(pw[0], pw[1], pw[2], pw[3]);
 #pragma unroll
-        for (int dt = 0; dt < DT16; ++dt) {
-          const uint2 vv = *(const uint2*)((const uint16_t*)bV + (16 * dt + lq) * VS +
-                                           ((kt * 16 + 4 * lg) ^ vt_swizzle(16 * dt + lq)));
-          if constexpr (DT == kF16) {
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_bit_cast(h4, vv), __builtin_bit_cast(h4, make_uint2(pw[0], pw[1])), o[dt],
-                0, 0, 0);
-          } else {
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                __builtin_bit_cast(s4, vv), __builtin_bit_cast(s4, make_uint2(pw[0], pw[1])), o[dt],
-                0, 0, 0);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                __builtin_bit_cast(s4, vv), __builtin_bit_cast(s4, make_uint2(pl2[0], pl2[1])), o[dt],
-                0, 0, 0);
-          }
-        }
+      for (int dt = 0; dt < DT16; ++dt) {
+        const uint16_t* vrow = (const uint16_t*)bV + (16 * dt + lq) * VS;
+        const int sw = vt_swizzle(16 * dt + lq);
+        const uint2 v0 = *(const uint2*)(vrow + ((4 * lg) ^ sw));
+        const uint2 v1 = *(const uint2*)(vrow + ((16 + 4 * lg) ^ sw));
+        const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        o[dt] = mfma_x32<DT>(vv, pv, o[dt]);
+        if constexpr (DT == kBF16)
+          o[dt] = mfma_x32<DT>(vv, make_uint4(pl2[0], pl2[1], pl2[2], pl2[3]), o[dt]);
       }
     }
   };
