@@ -145,9 +145,10 @@ SplitPlan plan_split(const swgqa_params* p) {
     return s;
   }
   if (multi_token && chunk_kernel_supports(p->dtype, p->head_size) &&
-      p->total_sequence_length >= 4) {
+      (p->total_sequence_length >= 8 || p->kv_cache_type != 0)) {
     // multi-token step on the matrix cores (its bias reads take rows of at
-    // least 4 entries)
+    // least 8 entries; an 8-bit cache has no other kernel for steps of 16 or
+    // more tokens, and with a shorter total none of their items is valid)
     s.kind = Kind::kChunk;
     // 8-wave workgroups (128 query rows) once a KV head has that many rows:
     // twice the matrix work per staged K/V block

@@ -86,7 +86,7 @@ struct ChunkShape {
   // LDS row strides (elements), chosen so the MFMA operand reads of 16 lanes
   // on 16 different rows fall in distinct banks
   static constexpr int KS = (DT == kF32) ? D + 4 : D + 8;   // K rows: [key][d]
-  static constexpr int VS = (DT == kF32) ? D + 4 : BN + 4;  // fp32 V [key][d]; 16-bit V^T [d][key]
+  static constexpr int VS = (DT == kF32) ? D + 4 : BN + 8;  // fp32 V [key][d]; 16-bit V^T [d][key]
   static constexpr int KELEMS = BN * KS;
   static constexpr int VELEMS = (DT == kF32) ? BN * VS : D * VS;
   static constexpr int CHUNKS = BN * D * e / 16;           // 16-byte chunks per block per tensor
@@ -101,8 +101,28 @@ template <> struct LdsT<kF16> { using T = uint16_t; };
 template <> struct LdsT<kBF16> { using T = uint16_t; };
 
 // Key swizzle of row d of the transposed V tile (16-bit types): XOR of key
-// bits 2..4 with d / 8, so groups of 4 consecutive keys stay contiguous.
-__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 7) << 2; }
+// bits 3..4 with (d / 8) mod 4, so groups of 8 consecutive keys stay
+// contiguous and in order.
+__device__ __forceinline__ int vt_swizzle(int d) { return ((d >> 3) & 3) << 3; }
+
+// 16-bit types: row i of the block's score tile kt holds key 8 (i / 4) +
+// 4 kt + i % 4, so lane group g, which receives rows 4g .. 4g + 3 of both
+// tiles, holds keys 8g .. 8g + 7 -- one contiguous run of the block, for its
+// attention_bias entries and its part of the 32-key value products.  K is
+// staged in that order (key k at LDS row k_slot(k) = 16 kt + i), so the score
+// products read consecutive rows.  fp32 keeps key 16 kt + i (its value
+// products run per tile, and a second tile past the band's end is skipped).
+template <int DT>
+__device__ __forceinline__ int k_slot(int k) {
+  if constexpr (DT == kF32) return k;
+  else return 16 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3);
+}
+// The key of score r (0..3) of tile kt in lane group g.
+template <int DT>
+__device__ __forceinline__ int score_key(int kt, int g, int r) {
+  if constexpr (DT == kF32) return 16 * kt + 4 * g + r;
+  else return 8 * g + 4 * kt + r;
+}
 
 // Key and 16-byte part of chunk c of a staged block whose rows are CPR
 // chunks long.  In every 64 chunks (one wave's), lane group g = (c / 16) % 4
@@ -381,7 +401,7 @@ void attn_chunk_kernel(AttnArgs a) {
     nw_lane[u] = (uint32_t)(chunk_key<CPR>(c) * new_stride + chunk_part<CPR>(c) * kPartB);
   }
   const uint64_t bias_lane =
-      BIAS ? (uint64_t)a.bias + (uint64_t)((bias_row + 4 * lg) * e) : 0;
+      BIAS ? (uint64_t)a.bias + (uint64_t)((bias_row + (DT == kF32 ? 4 : 8) * lg) * e) : 0;
   const int64_t cache_end = pl.P < ke ? pl.P : ke;  // keys below this are cache rows
 
   // Compaction by the key splits (16-bit cache; the host gives a stash only
@@ -460,19 +480,25 @@ void attn_chunk_kernel(AttnArgs a) {
       }
     }
     if constexpr (BIAS) {
-      // keys j0 + 16 kt + 4 lg + [0, 4): one 4-element load per tile, at
-      // element (not vector) alignment -- global memory takes unaligned
-      // vector loads on this target.  The start is clamped to total - 4 so
-      // the load stays inside the row (a valid item has total >= T >= S, and
-      // the host sends steps of S < 16 here only when total >= 4); entries
-      // of keys past the band's end are masked, and a group moved back by the
-      // clamp is shifted into place when the block is computed (shifts of
-      // more than 3 leave only masked keys).  One path for every block, so no
-      // load waits on another.
+      // the keys of this lane's scores (16-bit: j0 + 8 lg + [0, 8), one
+      // 8-element load; fp32: j0 + 16 kt + 4 lg + [0, 4), one 4-element
+      // load per tile) at element (not vector) alignment -- global memory
+      // takes unaligned vector loads on this target.  The start is clamped
+      // to total - (elements loaded) so the load stays inside the row (a
+      // valid item has total >= T >= S, and the host sends steps here only
+      // when total >= 8); entries of keys past the band's end are masked,
+      // and a group moved back by the clamp is shifted into place when the
+      // block is computed.  One path for every block, so no load waits on
+      // another.
+      if constexpr (DT == kF32) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int64_t g0 = min(j0 + kt * 16, (int64_t)a.total - 4 - 4 * lg);
-        load4_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), &rg.bias[kt * BW / 2]);
+        for (int kt = 0; kt < 2; ++kt) {
+          const int64_t g0 = min(j0 + kt * 16, (int64_t)a.total - 4 - 4 * lg);
+          load4_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), &rg.bias[kt * BW / 2]);
+        }
+      } else {
+        const int64_t g0 = min(j0, (int64_t)a.total - 8 - 8 * lg);
+        load8_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), rg.bias);
       }
     }
   };
@@ -490,11 +516,11 @@ void attn_chunk_kernel(AttnArgs a) {
       const u32x4 vw = Q8 ? codes_to_elems<DT, CT>(rg.v[u]) : rg.v[u];
       if constexpr (DT == kF32) {
         // rows of 16-byte multiples: one store per chunk
-        *(u32x4*)((float*)bK + key * KS + d0) = kw;
+        *(u32x4*)((float*)bK + k_slot<DT>(key) * KS + d0) = kw;
         *(u32x4*)((float*)bV + key * VS + d0) = vw;
       } else {
         // K rows are 16-byte aligned: one store per chunk
-        *(u32x4*)((uint16_t*)bK + key * KS + d0) = kw;
+        *(u32x4*)((uint16_t*)bK + k_slot<DT>(key) * KS + d0) = kw;
         // V transposed, sV[d][key ^ swz(d)].  The wave's 4 lane groups hold
         // keys 4q .. 4q + 3 at the same columns d0 .. d0 + 7, word w = columns
         // d0 + 2w, + 1: a 4x4 exchange of the words across lane groups (two
@@ -580,9 +606,10 @@ void attn_chunk_kernel(AttnArgs a) {
   auto compute_block = [&](int blk, const float* bias_blk) __attribute__((always_inline)) {
     const LT* const bK = sK + (DB ? (blk & 1) : 0) * Sh::KELEMS;
     const LT* const bV = sV + (DB ? (blk & 1) : 0) * Sh::VELEMS;
-    // the block's second 16-key tile holds keys of the band (else its
-    // scores are masked and its products are skipped: P = 0 there)
-    const bool tile1 = blk * BN + 16 < nk_band;
+    // the block's second score tile (fp32: keys 16 .. 31; 16-bit: keys
+    // 8g + 4 .. 8g + 7) holds keys of the band (else its scores are masked
+    // and its products are skipped: P = 0 there)
+    const bool tile1 = blk * BN + (DT == kF32 ? 16 : 4) < nk_band;
     // S^T for the two 16-key tiles of the block
     f4 sc[2];
     if constexpr (DT == kF32) {
@@ -611,7 +638,7 @@ void attn_chunk_kernel(AttnArgs a) {
       for (int kt = 0; kt < 2; ++kt) {
         f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         if (kt == 0 || tile1) {
-          const uint16_t* kr = (const uint16_t*)bK + (kt * 16 + lq) * KS + 8 * lg;
+          const uint16_t* kr = (const uint16_t*)bK + (16 * kt + lq) * KS + 8 * lg;
           f4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int s = 0; s < QST; ++s) {
@@ -629,7 +656,7 @@ void attn_chunk_kernel(AttnArgs a) {
     for (int kt = 0; kt < 2; ++kt) {
       f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
       if (kt == 0 || tile1) {
-        const uint16_t* kr = (const uint16_t*)bK + (kt * 16 + lq) * KS + 4 * lg;
+        const uint16_t* kr = (const uint16_t*)bK + (16 * kt + lq) * KS + 4 * lg;
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
           const uint2 kv = *(const uint2*)(kr + 16 * s);
@@ -659,7 +686,7 @@ void attn_chunk_kernel(AttnArgs a) {
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int32_t jr = blk * BN + kt * 16 + 4 * lg + r;
+          const int32_t jr = blk * BN + score_key<DT>(kt, lg, r);
           const bool vis = jr >= vis_lo && jr <= vis_hi;
           float x = sc[kt][r] * qk_scale;
           if constexpr (CAP) {
@@ -752,10 +779,10 @@ void attn_chunk_kernel(AttnArgs a) {
       }
     } else {
       // One 16x16x32 product per O^T tile over the block's 32 keys: lane
-      // group lg's reduction elements are keys 4lg .. 4lg + 3 and 16 + 4lg ..
-      // + 3, the keys its scores hold.  P is 0 on masked keys, and on the
-      // whole second tile when it lies past the band (whose V rows are
-      // clamped copies of the band's last row: finite).
+      // group lg's reduction elements are keys 8lg .. 8lg + 7, the keys its
+      // scores hold.  P is 0 on masked keys, and on the whole second score
+      // tile when it lies past the band (whose V rows are clamped copies of
+      // the band's last row: finite).
       uint32_t pw[4], pl2[4];
       if constexpr (DT == kF16) {
         pw[0] = p16[0][0];
@@ -784,9 +811,7 @@ void attn_chunk_kernel(AttnArgs a) {
       for (int dt = 0; dt < DT16; ++dt) {
         const uint16_t* vrow = (const uint16_t*)bV + (16 * dt + lq) * VS;
         const int sw = vt_swizzle(16 * dt + lq);
-        const uint2 v0 = *(const uint2*)(vrow + ((4 * lg) ^ sw));
-        const uint2 v1 = *(const uint2*)(vrow + ((16 + 4 * lg) ^ sw));
-        const uint4 vv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+        const uint4 vv = *(const uint4*)(vrow + ((8 * lg) ^ sw));
         o[dt] = mfma_x32<DT>(vv, pv, o[dt]);
         if constexpr (DT == kBF16)
           o[dt] = mfma_x32<DT>(vv, make_uint4(pl2[0], pl2[1], pl2[2], pl2[3]), o[dt]);
@@ -797,30 +822,45 @@ void attn_chunk_kernel(AttnArgs a) {
   auto block_bias = [&](int blk, const BlockRegs& rg, float* bias_blk) __attribute__((always_inline)) {
     if constexpr (BIAS) {
       const int64_t j0 = kb + (int64_t)blk * BN;
+      float x[8];  // entry 4 kt + r: the bias of score r of tile kt
+      if constexpr (DT == kF32) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        // elements the clamp moved the group back by (0 unless the group
-        // passes the end of the row)
-        const int64_t g = j0 + kt * 16 + 4 * lg;
-        const int sh = (int)min(g - min(g, (int64_t)a.total - 4), (int64_t)3);
-        const uint32_t* w = &rg.bias[kt * BW / 2];
-        float x[4];
-        if constexpr (DT == kF32) {
+        for (int kt = 0; kt < 2; ++kt) {
+          // elements the clamp moved the group back by (0 unless the group
+          // passes the end of the row)
+          const int64_t g = j0 + kt * 16 + 4 * lg;
+          const int sh = (int)min(g - min(g, (int64_t)a.total - 4), (int64_t)3);
+          const uint32_t* w = &rg.bias[kt * BW / 2];
           // (selects, not an index: a register array indexed at run time
           // would live in scratch memory)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = min(r + sh, 3);
-            x[r] = __uint_as_float(i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3]);
+            x[4 * kt + r] =
+                __uint_as_float(i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3]);
           }
-        } else {
-          const uint64_t v = (((uint64_t)w[1] << 32) | w[0]) >> (16 * sh);
-          unpack_word<DT>((uint32_t)v, x);
-          unpack_word<DT>((uint32_t)(v >> 32), x + 2);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bias_blk[kt * 4 + r] = x[r];
+      } else {
+        // elements the clamp moved the group back by (0 unless the group
+        // passes the end of the row; entries r >= 8 - sh are then past it,
+        // and masked)
+        const int64_t g = j0 + 8 * lg;
+        const int sh = (int)min(g - min(g, (int64_t)a.total - 8), (int64_t)7);
+        const uint32_t* w = rg.bias;
+        // the 8 entries as one 128-bit value, shifted right by sh entries
+        const uint64_t lo = ((uint64_t)w[1] << 32) | w[0];
+        const uint64_t hi = ((uint64_t)w[3] << 32) | w[2];
+        const int bits = 16 * sh;
+        const uint64_t nlo =
+            bits == 0 ? lo : bits < 64 ? (lo >> bits) | (hi << (64 - bits)) : hi >> (bits - 64);
+        const uint64_t nhi = bits < 64 ? hi >> bits : 0;
+        unpack_word<DT>((uint32_t)nlo, x);
+        unpack_word<DT>((uint32_t)(nlo >> 32), x + 2);
+        unpack_word<DT>((uint32_t)nhi, x + 4);
+        unpack_word<DT>((uint32_t)(nhi >> 32), x + 6);
       }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) bias_blk[r] = x[r];
     }
   };
   // A block's K/V/bias loads are issued three steps before it is staged

@@ -281,6 +281,20 @@ __device__ __forceinline__ void load4_raw_unaligned(uint64_t addr, uint32_t* out
   }
 }
 
+// The same for 8 consecutive elements (fp32: two 16-byte loads).
+template <int DT>
+__device__ __forceinline__ void load8_raw_unaligned(uint64_t addr, uint32_t* out) {
+  if constexpr (DT == kF32) {
+    load4_raw_unaligned<DT>(addr, out);
+    load4_raw_unaligned<DT>(addr + 16, out + 4);
+  } else {
+    typedef u32x4 v_t __attribute__((aligned(2)));
+    const v_t w = *(const v_t __attribute__((address_space(1)))*)addr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = w[i];
+  }
+}
+
 // int8 cache codes ("GQA In-Place KV Cache: Investigation Report", section
 // 1.1, names k_scale / v_scale; reading: the code of x is the binary32
 // quotient x / scale rounded to an integer with ties to even, saturated to

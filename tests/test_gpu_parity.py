@@ -457,15 +457,16 @@ def test_chunked_steps_ragged_bias(cfg, mode):
 
 
 def test_bias_rows_shorter_than_a_load_group():
-    """Bias rows of 2, 5 and 7 entries: the chunk kernel reads bias in groups
-    of 4 entries clamped to the row's end (shifted back when computed), and a
-    step with rows of fewer than 4 entries goes to the staged decode kernel."""
+    """Bias rows of 2, 9 and 13 entries: the chunk kernel reads bias in groups
+    of 8 entries clamped to the row's end (shifted back when computed: by 7
+    and 3 entries here), and a step with rows of fewer than 8 entries goes to
+    the staged decode kernel."""
     cfg = Cfg(B=2, Hq=32, Hkv=2, D=64, C=12, W=10, seed=37, dtype=synth.F16)
     syn = cfg.synth()
     vers = Versions(cfg.B)
     run = Lockstep(cfg, vers=vers)
     P = np.array([0, 0])
-    for S in [2, 3, 2]:
+    for S in [2, 7, 4]:
         total = int((P + S).max())
         run.step(P, S, bias=_bias_nan_outside(cfg, syn, P, S, total), total=total)
         P = P + S
