@@ -218,10 +218,12 @@ constexpr bool chunk_split_moves() { return !chunk_double_buffer<DT>() && CT == 
 // most 256 bytes, 4 in 8-wave workgroups without bias (its operands fit 128
 // registers with two blocks of loads in flight; measured faster than 2 or 3
 // waves) and 3 otherwise (the bias path and 4-wave workgroups need a little
-// more); no floor for the other types.
+// more); 16-bit rows of at most 128 bytes in 8-wave workgroups without bias,
+// 4 (two workgroups per CU); no floor for the other shapes.
 template <int DT, int D, int NW, bool BIAS>
 constexpr int chunk_min_waves() {
-  return DT == kF32 && D <= 64 ? (NW == 8 && !BIAS ? 4 : 3) : 1;
+  if constexpr (DT == kF32) return D <= 64 ? (NW == 8 && !BIAS ? 4 : 3) : 1;
+  else return D <= 64 && NW == 8 && !BIAS ? 4 : 1;
 }
 
 template <int DT, int D, bool BIAS, int NW, int CT>
@@ -257,8 +259,8 @@ void attn_chunk_kernel(AttnArgs a) {
   const uint32_t t = P - slice * T;
   const int b = (int)div_gap(slice, a.hdiv);
   const int kvh = (int)slice - b * a.Hkv;
-  const int tile = (int)t / a.nsplit;
-  const int split = (int)t % a.nsplit;
+  const int tile = (int)div_gap(t, a.sdiv);
+  const int split = (int)t - tile * a.nsplit;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -267,6 +269,13 @@ void attn_chunk_kernel(AttnArgs a) {
 
   // seqlens_k first: the plan and every K/V address wait on it
   const int32_t seqlen = load_seqlen(a.seqlens, b);
+  // The launch arguments the plan and the addresses use, wanted here (an
+  // empty statement that takes them in scalar registers): their scalar
+  // loads then go out in one batch with seqlens_k's, not one round trip
+  // each where first used behind the plan's branches.
+  asm volatile("" ::"s"(a.k), "s"(a.v), "s"(a.past_k), "s"(a.past_v), "s"(a.C), "s"(a.W),
+               "s"(a.total), "s"(a.S), "s"(a.Hkv), "s"(a.gdiv.magic), "s"(a.gdiv.G),
+               "s"(a.gdiv.sh1), "s"(a.gdiv.sh2));
   const int nq_item = a.S * a.group;
   const int q0 = tile * BQ;
 
@@ -344,7 +353,9 @@ void attn_chunk_kernel(AttnArgs a) {
   const int64_t p_last = pl.P + i_last;
   const int64_t lo = p_first - a.W + 1 > 0 ? p_first - a.W + 1 : 0;
   const int64_t nkeys = p_last - lo + 1;
-  const int64_t per = ((nkeys + a.nsplit - 1) / a.nsplit + BN - 1) / BN * BN;
+  // (nkeys + nsplit - 1 < 2^32: the division by invariant)
+  const int64_t per =
+      ((int64_t)div_gap((uint32_t)(nkeys + a.nsplit - 1), a.sdiv) + BN - 1) / BN * BN;
   const int64_t kb = lo + split * per;
   const int64_t ke = kb + per < p_last + 1 ? kb + per : p_last + 1;
 
@@ -583,14 +594,21 @@ void attn_chunk_kernel(AttnArgs a) {
   const int64_t vhi = (my_pos < ke - 1 ? my_pos : ke - 1) - kb;
   const int32_t vis_lo = my_ok ? (int32_t)(vlo < -(int64_t)0x7fffffff ? -0x7fffffff : vlo) : 1;
   const int32_t vis_hi = my_ok ? (int32_t)vhi : 0;
-  // the keys every query of this wave sees: [w_vis_lo, w_vis_hi] (lanes
-  // without a query do not narrow it)
-  int32_t w_vis_lo = my_ok ? vis_lo : INT32_MIN;
-  int32_t w_vis_hi = my_ok ? vis_hi : INT32_MAX;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    w_vis_lo = max(w_vis_lo, __shfl_xor(w_vis_lo, o, kWave));
-    w_vis_hi = min(w_vis_hi, __shfl_xor(w_vis_hi, o, kWave));
+  // the keys every query of this wave sees: [w_vis_lo, w_vis_hi] -- both
+  // bounds grow with the position, so they are those of the wave's last and
+  // first query rows (scalars; lanes without a query do not narrow it)
+  int32_t w_vis_lo = INT32_MIN;
+  int32_t w_vis_hi = INT32_MAX;
+  {
+    const int qw0 = q0 + 16 * __builtin_amdgcn_readfirstlane(wave);
+    if (qw0 < nq_item) {
+      const int qw1 = min(qw0 + 15, nq_item - 1);
+      const int64_t p_lo = pl.P + qw1 / a.group;  // largest position: the highest lower bound
+      const int64_t p_hi = pl.P + qw0 / a.group;  // smallest position: the lowest upper bound
+      const int64_t wlo = p_lo - a.W + 1 - kb;
+      w_vis_lo = (int32_t)(wlo < -(int64_t)0x7fffffff ? -0x7fffffff : wlo);
+      w_vis_hi = (int32_t)((p_hi < ke - 1 ? p_hi : ke - 1) - kb);
+    }
   }
 
   float m_run = -INFINITY;  // log2 units, per query (same in all 4 lane groups)

@@ -33,6 +33,7 @@ struct AttnArgs {
   GapDiv gdiv;  // division by the gap C - W + 1
   GapDiv tdiv;  // division by ntiles * nsplit (work items per slice)
   GapDiv hdiv;  // division by Hkv
+  GapDiv sdiv;  // division by nsplit
   int32_t ntiles, nsplit;
   float scale, softcap;
   int32_t bias_b, bias_h;
