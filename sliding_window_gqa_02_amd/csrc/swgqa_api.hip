@@ -162,6 +162,13 @@ SplitPlan plan_split(const swgqa_params* p) {
     int64_t ns = base >= kChunkMinWorkgroups ? 1 : (kChunkMinWorkgroups + base - 1) / base;
     const int64_t ns_max = (nkeys + 4 * chunk_keys_per_block() - 1) / (4 * chunk_keys_per_block());
     if (ns > ns_max) ns = ns_max;
+    if (ns < 1) ns = 1;
+    // splits take whole blocks, ceil(nkeys / ns) rounded up to a block: as
+    // many splits as that covers the band with (the rest would be empty
+    // workgroups whose partials the merge still reads)
+    const int64_t bn = chunk_keys_per_block();
+    const int64_t per = ((nkeys + ns - 1) / ns + bn - 1) / bn * bn;
+    ns = (nkeys + per - 1) / per;
     s.nsplit = ns < 1 ? 1 : (int)ns;
     return s;
   }

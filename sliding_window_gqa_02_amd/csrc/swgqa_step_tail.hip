@@ -52,29 +52,35 @@ __device__ __forceinline__ void merge_rows(const AttnArgs& a, int D, uint32_t bl
   if (row >= nrows) return;
   const int d = (int)(threadIdx.x % tpr) * 4;
   const int b = (int)(row / (uint32_t)(a.S * a.Hq));
+  // Splits in groups of kMergeGroup whose loads (pairs and partials) are all
+  // issued before any is used: one memory round trip per group, not per
+  // split or per pass -- the first group's before the item's plan, whose
+  // seqlens_k read would otherwise come first.  The group's largest m joins
+  // the running one, the sums so far are rescaled to it, and the group's
+  // terms are added; indices past the last split repeat it and are not
+  // summed.
+  const int64_t r0 = (int64_t)row * a.nsplit;
+  const int ns = a.nsplit;
+  const float2* ml2 = (const float2*)a.ml;
+  float2 v[kMergeGroup];
+  float4 p[kMergeGroup];
+  auto load_group = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kMergeGroup; ++j) {
+      const int64_t s = r0 + min(s0 + j, ns - 1);
+      v[j] = ml2[s];
+      p[j] = *(const float4*)(a.opart + s * D + d);
+    }
+  };
+  load_group(0);
   const ItemPlan pl = plan_item(a.seqlens[b], a.S, a.C, a.gdiv, a.total);
   float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (pl.ok) {
-    // Splits in groups of kMergeGroup whose loads (pairs and partials) are
-    // all issued before any is used: one memory round trip per group, not
-    // per split or per pass.  The group's largest m joins the running one,
-    // the sums so far are rescaled to it, and the group's terms are added;
-    // indices past the last split repeat it and are not summed.
-    const int64_t r0 = (int64_t)row * a.nsplit;
-    const int ns = a.nsplit;
-    const float2* ml2 = (const float2*)a.ml;
     float M = -INFINITY;
     float L = 0.0f;
     float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < ns; s0 += kMergeGroup) {
-      float2 v[kMergeGroup];
-      float4 p[kMergeGroup];
-#pragma unroll
-      for (int j = 0; j < kMergeGroup; ++j) {
-        const int64_t s = r0 + min(s0 + j, ns - 1);
-        v[j] = ml2[s];
-        p[j] = *(const float4*)(a.opart + s * D + d);
-      }
+      if (s0 > 0) load_group(s0);
       float Mg = M;
 #pragma unroll
       for (int j = 0; j < kMergeGroup; ++j) Mg = fmaxf(Mg, v[j].x);
@@ -141,25 +147,40 @@ __device__ __forceinline__ void writeback_part(const CopyArgs& a, const AttnArgs
   const int tid = threadIdx.x;
 
   // 1. Surviving old rows: [shift, shift + kept) -> [0, kept).
-  if (shared && at.stash && chunk_moves_rows(pl, at.W, at.stash_rows)) {
+  const bool stashed = shared && at.stash && chunk_moves_rows(pl, at.W, at.stash_rows);
+  if (stashed) {
     // moved by the chunk kernel's key splits but for the first `shift`
     // positions of every split after the first, set aside in its stash
-    // slots (pos - kb); they land on the previous split's rows
-    const int64_t rowsz = pl.shift * wn;  // words of one split's slots
-    const int64_t nw = (at.nsplit - 1) * rowsz;
+    // slots (pos - kb); they land on the previous split's rows.  Loads of
+    // kCopyUnroll words per thread are issued together.
+    const ChunkSplits cs = chunk_splits(pl, a.S, at.W, at.nsplit, at.sdiv);
+    const uint32_t rowsz = (uint32_t)pl.shift << wlog;  // words of one split's slots
+    const uint32_t nw = (uint32_t)(at.nsplit - 1) * rowsz;
     const int64_t lo_keep = pl.P - pl.Lb + pl.shift;  // first surviving position
-    for (int64_t i = tid; i < nw; i += kTailThreads) {
-      const int s = 1 + (int)(i / rowsz);
-      const int64_t r = (i % rowsz) >> wlog;
-      const int64_t w = i & (wn - 1);
-      int64_t kb, ke;
-      chunk_split_range(pl, a.S, at.W, at.nsplit, s, kb, ke);
-      const int64_t pos = kb + r;
-      if (pos < lo_keep || pos >= ke || pos >= pl.P) continue;
-      const int64_t slot = ((((int64_t)b * a.Hkv + kvh) * at.nsplit + s) * 2 + which) *
-                               at.stash_rows + r;
-      dst[(pos - lo_keep) * w16 + w] =
-          ((const u32x4*)((const char*)at.stash + slot * rowb) + col * wn)[w];
+    const u32x4* const stash =
+        (const u32x4*)at.stash + (((int64_t)b * a.Hkv + kvh) * at.nsplit * 2 + which) *
+                                     at.stash_rows * w16 + col * wn;
+    for (uint32_t i0 = tid; i0 < nw; i0 += kCopyUnroll * kTailThreads) {
+      u32x4 x[kCopyUnroll];
+      int64_t to[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const uint32_t i = i0 + (uint32_t)u * kTailThreads;
+        const uint32_t sm1 = i < nw ? i / rowsz : 0;  // split - 1
+        const uint32_t r = (i - sm1 * rowsz) >> wlog;
+        const uint32_t w = i & (uint32_t)(wn - 1);
+        const int64_t kb = cs.lo + (int64_t)(sm1 + 1) * cs.per;
+        const int64_t ke = kb + cs.per < cs.p_last + 1 ? kb + cs.per : cs.p_last + 1;
+        const int64_t pos = kb + r;
+        const bool ok = i < nw && pos >= lo_keep && pos < ke && pos < pl.P;
+        // slot r of split sm1 + 1 (K or V), this column part; word 0 of the
+        // first slot when there is nothing to store
+        x[u] = stash[ok ? ((int64_t)(sm1 + 1) * 2 * at.stash_rows + r) * w16 + w : 0];
+        to[u] = ok ? (pos - lo_keep) * w16 + w : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u)
+        if (to[u] >= 0) dst[to[u]] = x[u];
     }
   } else if (pl.kept > 0 && (!shared || pl.shift > 0)) {
     if (shared) {
@@ -182,7 +203,8 @@ __device__ __forceinline__ void writeback_part(const CopyArgs& a, const AttnArgs
       }
     }
   }
-  __syncthreads();
+  // (stashed rows land below kept, from their own buffer: no wait for them)
+  if (!stashed) __syncthreads();
 
   // 2. New rows i in [max(0, -kept), S) -> row kept + i.
   const int64_t i0 = pl.kept < 0 ? -pl.kept : 0;

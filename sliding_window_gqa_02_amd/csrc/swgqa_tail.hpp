@@ -134,18 +134,23 @@ __device__ __forceinline__ void slice_tail_rows(const AttnArgs& a, const ItemPla
   slice_writeback_shared<UNROLL>(a, pl, b, kvh, D, ce, knew, vnew, moved);
 }
 
-// Key range of split `split` (of nsplit) of a slice read as one query tile
-// by the chunk kernel: the band [max(P - W + 1, 0), P + S - 1] cut into
-// parts of whole kChunkBlockKeys-key blocks (the kernel's split rule).
-__device__ __forceinline__ void chunk_split_range(const ItemPlan& pl, int S, int W, int nsplit,
-                                                  int split, int64_t& kb, int64_t& ke) {
-  const int64_t p_last = pl.P + S - 1;
-  const int64_t lo = pl.P - W + 1 > 0 ? pl.P - W + 1 : 0;
-  const int64_t nkeys = p_last - lo + 1;
-  const int64_t per = ((nkeys + nsplit - 1) / nsplit + kChunkBlockKeys - 1) / kChunkBlockKeys *
-                      kChunkBlockKeys;
-  kb = lo + split * per;
-  ke = kb + per < p_last + 1 ? kb + per : p_last + 1;
+// Key splits of a slice read as one query tile by the chunk kernel: the band
+// [lo, p_last] = [max(P - W + 1, 0), P + S - 1] cut into parts of `per` keys,
+// ceil(nkeys / nsplit) rounded up to whole kChunkBlockKeys-key blocks (the
+// kernel's split rule); split s reads [lo + s per, min(lo + (s + 1) per,
+// p_last + 1)).
+struct ChunkSplits {
+  int64_t lo, p_last, per;
+};
+__device__ __forceinline__ ChunkSplits chunk_splits(const ItemPlan& pl, int S, int W, int nsplit,
+                                                    const GapDiv& sdiv) {
+  ChunkSplits c;
+  c.p_last = pl.P + S - 1;
+  c.lo = pl.P - W + 1 > 0 ? pl.P - W + 1 : 0;
+  const int64_t nkeys = c.p_last - c.lo + 1;
+  c.per = ((int64_t)div_gap((uint32_t)(nkeys + nsplit - 1), sdiv) + kChunkBlockKeys - 1) /
+          kChunkBlockKeys * kChunkBlockKeys;
+  return c;
 }
 
 // Whether the key splits of a one-tile chunk step move the surviving rows of
