@@ -425,6 +425,7 @@ swgqa_status forward_impl(const swgqa_params* p, const void* query, const void* 
   a.tdiv = make_gap_div((uint32_t)(s.ntiles * s.nsplit));
   a.hdiv = make_gap_div((uint32_t)p->kv_num_heads);
   a.sdiv = make_gap_div((uint32_t)s.nsplit);
+  a.qdiv = make_gap_div((uint32_t)(p->num_heads / p->kv_num_heads));
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_size);
   a.softcap = p->softcap;
   a.bias_b = p->bias_dim0_is_batch ? 1 : 0;

@@ -284,10 +284,11 @@ void attn_chunk_kernel(AttnArgs a) {
   const int my_qi = q0 + wave * 16 + lq;
   const bool my_ok = my_qi < nq_item;
   const int my_qc = my_ok ? my_qi : nq_item - 1;
-  const int my_i = my_qc / a.group;
-  const int my_h = kvh * a.group + my_qc % a.group;
-  const int i_first = q0 / a.group;
-  const int i_last = (min(q0 + BQ, nq_item) - 1) / a.group;
+  // (divisions by invariants)
+  const int my_i = (int)div_gap((uint32_t)my_qc, a.qdiv);
+  const int my_h = kvh * a.group + my_qc - my_i * a.group;
+  const int i_first = (int)div_gap((uint32_t)q0, a.qdiv);
+  const int i_last = (int)div_gap((uint32_t)(min(q0 + BQ, nq_item) - 1), a.qdiv);
 
   // Q^T operand: fp32 step s holds Q[q][(D / 4) lg + s] (the steps split
   // the head dimension as d = (D / 4) k + s over the 4 reduction lanes k, so
@@ -332,7 +333,7 @@ void attn_chunk_kernel(AttnArgs a) {
       const int t = idx / D, d = idx % D;
       const int qi = q0 + t;
       if (qi >= nq_item) continue;
-      const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+      const int i = (int)div_gap((uint32_t)qi, a.qdiv), h = kvh * a.group + qi - i * a.group;
       const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
       if (a.nsplit == 1) {
         if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = 0.0f;
@@ -603,8 +604,9 @@ void attn_chunk_kernel(AttnArgs a) {
     const int qw0 = q0 + 16 * __builtin_amdgcn_readfirstlane(wave);
     if (qw0 < nq_item) {
       const int qw1 = min(qw0 + 15, nq_item - 1);
-      const int64_t p_lo = pl.P + qw1 / a.group;  // largest position: the highest lower bound
-      const int64_t p_hi = pl.P + qw0 / a.group;  // smallest position: the lowest upper bound
+      // largest position: the highest lower bound; smallest: the lowest upper bound
+      const int64_t p_lo = pl.P + div_gap((uint32_t)qw1, a.qdiv);
+      const int64_t p_hi = pl.P + div_gap((uint32_t)qw0, a.qdiv);
       const int64_t wlo = p_lo - a.W + 1 - kb;
       w_vis_lo = (int32_t)(wlo < -(int64_t)0x7fffffff ? -0x7fffffff : wlo);
       w_vis_hi = (int32_t)((p_hi < ke - 1 ? p_hi : ke - 1) - kb);

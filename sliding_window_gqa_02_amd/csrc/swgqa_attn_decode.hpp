@@ -235,8 +235,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   const int kvh = (int)slice - b * a.Hkv;
   // seqlens_k first: the plan and every K/V address wait on it
   const int32_t seqlen = load_seqlen(a.seqlens, b);
-  const int tile = a.nsplit == 1 ? (int)t : (int)t / a.nsplit;
-  const int split = a.nsplit == 1 ? 0 : (int)t % a.nsplit;
+  const int tile = a.nsplit == 1 ? (int)t : (int)div_gap(t, a.sdiv);
+  const int split = (int)t - tile * a.nsplit;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -283,7 +283,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   // Query tile: (position, head) pairs q0 .. q0 + NQ - 1, position-major,
   // walked with a carry (pairs past the item's last repeat it).  Loaded
   // before the plan: their addresses do not depend on seqlens_k.
-  const int i_first = q0 / a.group;
+  const int i_first = (int)div_gap((uint32_t)q0, a.qdiv);
   int i_last = i_first;
   uint32_t qw[NQ][4];
   int q_row[NQ];  // position index i of each pair (ROT)
@@ -326,7 +326,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
       const int t = idx / D, d = idx % D;
       const int qi = q0 + t;
       if (qi >= nq_item) continue;
-      const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+      const int i = (int)div_gap((uint32_t)qi, a.qdiv), h = kvh * a.group + qi - i * a.group;
       const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
       if (a.nsplit == 1) {
         if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = 0.0f;
@@ -346,8 +346,9 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   const int my_q = lane % NQ;
   const int my_qi = q0 + my_q;
   const bool my_q_ok = my_qi < nq_item;
-  const int my_i = my_q_ok ? my_qi / a.group : i_last;
-  const int my_h = kvh * a.group + (my_q_ok ? my_qi % a.group : 0);
+  const int my_qd = (int)div_gap((uint32_t)my_qi, a.qdiv);  // (divisions by invariants)
+  const int my_i = my_q_ok ? my_qd : i_last;
+  const int my_h = kvh * a.group + (my_q_ok ? my_qi - my_qd * a.group : 0);
   const int64_t my_pos = pl.P + my_i;
 
   // Union key range of the tile, split evenly (n < 2^31: keys are positions
@@ -357,7 +358,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
   const int64_t lo = p_first - a.W + 1 > 0 ? p_first - a.W + 1 : 0;
   const int64_t n = p_last - lo + 1;
   const int64_t chunk =
-      a.nsplit == 1 ? n : (int64_t)(((uint32_t)n + (uint32_t)a.nsplit - 1u) / (uint32_t)a.nsplit);
+      a.nsplit == 1 ? n : (int64_t)div_gap((uint32_t)n + (uint32_t)a.nsplit - 1u, a.sdiv);
   const int64_t kb = lo + split * chunk;
   const int64_t ke = kb + chunk < p_last + 1 ? kb + chunk : p_last + 1;
   const int32_t nk = ke > kb ? (int32_t)(ke - kb) : 0;  // keys kb + jr, 0 <= jr < nk
@@ -804,7 +805,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
       L += s_l[w][t] * c;
       A += s_acc[w][t][d] * c;
     }
-    const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+    const int i = (int)div_gap((uint32_t)qi, a.qdiv), h = kvh * a.group + qi - i * a.group;
     const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
     if (a.nsplit == 1) {
       const float c = fold_sink<DT>(a.sink, a.smooth, h, M, L);

@@ -207,8 +207,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   const int b = (int)div_gap(slice, a.hdiv);
   const int kvh = (int)slice - b * a.Hkv;
   const int32_t seqlen = load_seqlen(a.seqlens, b);
-  const int tile = a.nsplit == 1 ? (int)t : (int)t / a.nsplit;
-  const int split = a.nsplit == 1 ? 0 : (int)t % a.nsplit;
+  const int tile = a.nsplit == 1 ? (int)t : (int)div_gap(t, a.sdiv);
+  const int split = (int)t - tile * a.nsplit;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -229,7 +229,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   // Query tile: elements [sub * 16, sub * 16 + 16) of each pair, as 16
   // words (fp32) or 8 packed pairs (fp16 / bf16); pairs walked
   // position-major with a carry.
-  const int i_first = q0 / a.group;
+  const int i_first = (int)div_gap((uint32_t)q0, a.qdiv);
   int i_last = i_first;
   constexpr int QW = EPL * e / 4;  // words of a query chunk
   uint32_t qw[MK ? 1 : NQ][QW];
@@ -287,7 +287,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       const int tq = idx / D, d = idx % D;
       const int qi = q0 + tq;
       if (qi >= nq_item) continue;
-      const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+      const int i = (int)div_gap((uint32_t)qi, a.qdiv), h = kvh * a.group + qi - i * a.group;
       const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
       if (a.nsplit == 1) {
         if constexpr (DT == kF32) ((float*)a.out)[row * D + d] = 0.0f;
@@ -318,8 +318,9 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   const int my_q = lane % NQ;
   const int my_qi = q0 + my_q;
   const bool my_q_ok = my_qi < nq_item;
-  const int my_i = my_q_ok ? my_qi / a.group : i_last;
-  const int my_h = kvh * a.group + (my_q_ok ? my_qi % a.group : 0);
+  const int my_qd = (int)div_gap((uint32_t)my_qi, a.qdiv);  // (divisions by invariants)
+  const int my_i = my_q_ok ? my_qd : i_last;
+  const int my_h = kvh * a.group + (my_q_ok ? my_qi - my_qd * a.group : 0);
   const int64_t my_pos = pl.P + my_i;
 
   // Union key range of the tile, split evenly.
@@ -721,7 +722,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
       A += s_acc[w][tq][d] * c;
     }
     A *= a.v_scale;  // the value sum was taken over codes
-    const int i = qi / a.group, h = kvh * a.group + qi % a.group;
+    const int i = (int)div_gap((uint32_t)qi, a.qdiv), h = kvh * a.group + qi - i * a.group;
     const int64_t row = ((int64_t)b * a.S + i) * a.Hq + h;
     if (a.nsplit == 1) {
       const float c = fold_sink<DT>(a.sink, a.smooth, h, M, L);

@@ -34,6 +34,7 @@ struct AttnArgs {
   GapDiv tdiv;  // division by ntiles * nsplit (work items per slice)
   GapDiv hdiv;  // division by Hkv
   GapDiv sdiv;  // division by nsplit
+  GapDiv qdiv;  // division by group (query heads per KV head)
   int32_t ntiles, nsplit;
   float scale, softcap;
   int32_t bias_b, bias_h;
