@@ -428,6 +428,7 @@ swgqa_status forward_impl(const swgqa_params* p, const void* query, const void* 
   a.qdiv = make_gap_div((uint32_t)(p->num_heads / p->kv_num_heads));
   a.scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)p->head_size);
   a.softcap = p->softcap;
+  a.inv_softcap = p->softcap > 0.0f ? 1.0f / p->softcap : 0.0f;
   a.bias_b = p->bias_dim0_is_batch ? 1 : 0;
   a.bias_h = p->bias_dim1_is_heads ? 1 : 0;
   // in-kernel write-back: one workgroup per slice, or (staged decode) the

@@ -415,7 +415,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
 
   const bool has_cap = a.softcap > 0.0f;
   const float cap = a.softcap;
-  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
+  const float inv_cap = a.inv_softcap;  // (made on the host)
   const bool has_bias = a.bias != nullptr;
   const int64_t bias_row = has_bias
       ? ((((a.bias_b ? (int64_t)b : 0) * (a.bias_h ? a.Hq : 1) + (a.bias_h ? my_h : 0)) * a.S + my_i) *
@@ -447,7 +447,15 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_kerne
     const uint32_t s0 = (uint32_t)min(st, nst) * SR;  // no overflow: nst * SR < 2^31 + SR
     const uint32_t last = (uint32_t)(nk - 1);
     uint64_t ka[U], va[U];
-    if (min(s0 + SR, (uint32_t)nk) <= (uint32_t)ncache) {  // uniform: only cache rows
+    if (s0 + SR <= (uint32_t)ncache) {  // uniform: a whole stage of cache rows, no clamp
+      // (ncache <= nk; the rows' offsets from the stage's first are constants)
+      const uint64_t k0 = ck_lane + ((uint64_t)(s0 + rslot) << kRowShift);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ka[u] = k0 + ((uint64_t)(u * RPW) << kRowShift);
+        va[u] = ka[u] + dv_cache;
+      }
+    } else if (min(s0 + SR, (uint32_t)nk) <= (uint32_t)ncache) {  // uniform: only cache rows
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t off = (uint64_t)min(s0 + u * RPW + rslot, last) << kRowShift;

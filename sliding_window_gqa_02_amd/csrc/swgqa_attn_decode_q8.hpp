@@ -359,7 +359,7 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
 
   const bool has_cap = a.softcap > 0.0f;
   const float cap = a.softcap;
-  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
+  const float inv_cap = a.inv_softcap;  // (made on the host)
   const bool has_bias = a.bias != nullptr;
   const int64_t bias_row = has_bias
       ? ((((a.bias_b ? (int64_t)b : 0) * (a.bias_h ? a.Hq : 1) + (a.bias_h ? my_h : 0)) * a.S + my_i) *

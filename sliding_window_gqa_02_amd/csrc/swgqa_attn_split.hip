@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(AttnArgs a) {
   const bool has_bias = a.bias != nullptr;
   const bool has_cap = a.softcap > 0.0f;
   const float cap = a.softcap;
-  const float inv_cap = has_cap ? 1.0f / a.softcap : 0.0f;
+  const float inv_cap = a.inv_softcap;  // (made on the host)
 
   for (int64_t j0 = kb + (int64_t)wave * RPW; j0 < ke; j0 += (int64_t)kWaves * RPW) {
     const int64_t j = j0 + rslot;

@@ -37,6 +37,7 @@ struct AttnArgs {
   GapDiv qdiv;  // division by group (query heads per KV head)
   int32_t ntiles, nsplit;
   float scale, softcap;
+  float inv_softcap;  // 1 / softcap (binary32 quotient), or 0 without softcap
   int32_t bias_b, bias_h;
   // softmax sink: head_sink (Hq elements) or, with smooth != 0 and no
   // head_sink, a logit of 0; it joins the denominator with a zero value row
