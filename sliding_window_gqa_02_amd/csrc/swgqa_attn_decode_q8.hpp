@@ -200,8 +200,8 @@ __attribute__((amdgpu_waves_per_eu((kWaves + 3) / 4, 8))) void attn_decode_q8_ke
   constexpr bool PROUND = MV || PV16;     // P rounded to fp16
 
   const uint32_t T = gridDim.x;  // ntiles * nsplit
-  const uint32_t P = slice_work_index(blockIdx.x + T * (blockIdx.y + gridDim.y * blockIdx.z),
-                                      T * gridDim.y * gridDim.z, T);
+  const uint32_t P = xcd_contiguous(blockIdx.x + T * (blockIdx.y + gridDim.y * blockIdx.z),
+                                    T * gridDim.y * gridDim.z);
   const uint32_t slice = div_gap(P, a.tdiv);
   const uint32_t t = P - slice * T;
   const int b = (int)div_gap(slice, a.hdiv);

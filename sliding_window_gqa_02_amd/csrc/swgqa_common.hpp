@@ -91,16 +91,6 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t L, uint32_t N) {
   return x * q + (x < r ? x : r) + k;
 }
 
-// Work index of linear id L (of N) in a launch of T work items per (item, KV
-// head) slice.  With several (query tiles or key splits that read the same
-// rows), the XCD-contiguous placement above.  With one, the identity: the
-// round-robin deal then sends consecutive slices -- the KV heads of one item
-// -- to different XCDs, so the rows of an item's compacting slices move
-// through eight L2s and memory ports instead of one.
-__device__ __forceinline__ uint32_t slice_work_index(uint32_t L, uint32_t N, uint32_t T) {
-  return T == 1 ? L : xcd_contiguous(L, N);
-}
-
 // L(T) for the lengths a step can see: 0 <= T <= 2^31 and 1 <= W <= C < 2^31,
 // so ceil((T - C) / G) = (T - C - 1) / G + 1 with a 32-bit numerator.
 __host__ __device__ __forceinline__ int64_t resident_len_step(int64_t T, int32_t C,
