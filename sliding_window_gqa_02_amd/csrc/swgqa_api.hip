@@ -54,6 +54,10 @@ constexpr int kChunkMinRows = SWGQA_CHUNK_MIN_ROWS;
 #endif
 constexpr int kChunkWideRows = SWGQA_CHUNK_WIDE_ROWS;
 constexpr int64_t kChunkMinWorkgroups = SWGQA_CHUNK_MIN_WORKGROUPS;
+#ifndef SWGQA_CHUNK_GROUPS
+#define SWGQA_CHUNK_GROUPS 1
+#endif
+constexpr bool kChunkGroups = SWGQA_CHUNK_GROUPS != 0;
 constexpr int64_t kWholeSliceMinTiles = SWGQA_WHOLE_SLICE_MIN_TILES;
 constexpr int64_t kWholeSliceMaxKeys = SWGQA_WHOLE_SLICE_MAX_KEYS;
 constexpr int64_t kDecodeMinWorkgroups = SWGQA_DECODE_MIN_WORKGROUPS;
@@ -100,6 +104,7 @@ struct SplitPlan {
   int ntiles;   // tiles per (item, KV head)
   int nsplit;   // key splits per tile
   int waves;    // waves per workgroup (staged kernel)
+  int groups = 1;  // chunk kernel: groups of waves that share the tile's rows
 };
 
 SplitPlan plan_split(const swgqa_params* p) {
@@ -153,7 +158,14 @@ SplitPlan plan_split(const swgqa_params* p) {
     // 8-wave workgroups (128 query rows) once a KV head has that many rows:
     // twice the matrix work per staged K/V block
     s.waves = per_kv >= kChunkWideRows ? 8 : 4;
-    s.nq = chunk_rows_per_workgroup(s.waves);
+    // at most 32 rows per KV head (short steps: verify, small groups): 8
+    // waves in 4 groups of 2 that take turns over the split's blocks
+    if (kChunkGroups && per_kv <= 32 && p->dtype != SWGQA_F32 && p->kv_cache_type == 0 &&
+        p->head_size * 2 <= 256) {
+      s.waves = 8;
+      s.groups = 4;
+    }
+    s.nq = chunk_rows_per_workgroup(s.waves, s.groups);
     s.ntiles = (per_kv + s.nq - 1) / s.nq;
     const int64_t span = std::min<int64_t>(p->sequence_length, (s.nq + group - 1) / group + 1);
     int64_t nkeys = (int64_t)p->local_window_size + span - 1;
@@ -437,6 +449,7 @@ swgqa_status forward_impl(const swgqa_params* p, const void* query, const void* 
                        (int64_t)p->batch_size * p->kv_num_heads <= kMaxSliceCounters;
   a.fuse_writeback = (shared && s.nsplit == 1 && (s.ntiles == 1 || counted)) ? 1 : 0;
   a.waves = s.waves;
+  a.chunk_groups = s.groups;
   // long-gap compactions on the staged kernel, one 8-wave workgroup per
   // slice (every shift at least one round of the 8 waves' stages); the 8-bit
   // kernel keeps the move after attention (measured no faster with it fused)

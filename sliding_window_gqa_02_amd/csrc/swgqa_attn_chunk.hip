@@ -10,7 +10,7 @@ bool chunk_kernel_supports(int dtype, int D) {
   return D >= 16 && D % 16 == 0 && D <= 256 && D * e <= 512;
 }
 
-int chunk_rows_per_workgroup(int waves) { return 16 * waves; }
+int chunk_rows_per_workgroup(int waves, int groups) { return 16 * waves / groups; }
 int chunk_keys_per_block() { return BN; }
 static_assert(BN == kChunkBlockKeys, "key split ranges of the step tail");
 

@@ -220,20 +220,29 @@ constexpr bool chunk_split_moves() { return !chunk_double_buffer<DT>() && CT == 
 // waves) and 3 otherwise (the bias path and 4-wave workgroups need a little
 // more); 16-bit rows of at most 128 bytes in 8-wave workgroups without bias,
 // 4 (two workgroups per CU); no floor for the other shapes.
-template <int DT, int D, int NW, bool BIAS>
+template <int DT, int D, int NW, bool BIAS, int GRP = 1>
 constexpr int chunk_min_waves() {
-  if constexpr (DT == kF32) return D <= 64 ? (NW == 8 && !BIAS ? 4 : 3) : 1;
+  if constexpr (GRP > 1) return 1;  // (its register ring is GRP blocks deep per round)
+  else if constexpr (DT == kF32) return D <= 64 ? (NW == 8 && !BIAS ? 4 : 3) : 1;
   else return D <= 64 && NW == 8 && !BIAS ? 4 : 1;
 }
 
-template <int DT, int D, bool BIAS, int NW, int CT>
+// GRP > 1: the waves form GRP groups of NW / GRP waves; every group holds
+// the tile's query rows (16 per wave) and computes every GRP-th block of the
+// split, so a split of n blocks takes ceil(n / GRP) staging rounds; the
+// groups' softmax states are merged in LDS at the end.  For tiles of few
+// query rows (short multi-token steps), whose waves would otherwise walk the
+// band one block after another with nothing to overlap.
+template <int DT, int D, bool BIAS, int NW, int CT, int GRP = 1>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(chunk_min_waves<DT, D, NW, BIAS>(), 8)))
+__attribute__((amdgpu_waves_per_eu(chunk_min_waves<DT, D, NW, BIAS, GRP>(), 8)))
 void attn_chunk_kernel(AttnArgs a) {
   constexpr bool Q8 = CT != 0;
   using Sh = ChunkShape<DT, D, NW>;
   constexpr int kThreads = Sh::kThreads;
-  constexpr int BQ = 16 * NW;  // query rows per workgroup
+  constexpr int NWQ = NW / GRP;  // waves per group
+  constexpr int BQ = 16 * NWQ;   // query rows per workgroup
+  static_assert(NW % GRP == 0, "whole groups of waves");
   using LT = typename LdsT<DT>::T;
   constexpr int e = Sh::e, KS = Sh::KS, VS = Sh::VS, CPT = Sh::CPT, DSTEPS = Sh::DSTEPS;
   constexpr int DT16 = Sh::DT16;
@@ -247,7 +256,8 @@ void attn_chunk_kernel(AttnArgs a) {
   // other holds the block being computed; 16-bit types stage every block in
   // one buffer between two barriers (measured faster for them)
   constexpr bool DB = chunk_double_buffer<DT>();
-  constexpr int NBUF = DB ? 2 : 1;
+  static_assert(GRP == 1 || !DB, "wave groups stage one buffer per group");
+  constexpr int NBUF = DB ? 2 : GRP;
   __shared__ __attribute__((aligned(16))) LT sK[NBUF * Sh::KELEMS];
   __shared__ __attribute__((aligned(16))) LT sV[NBUF * Sh::VELEMS];
 
@@ -263,6 +273,8 @@ void attn_chunk_kernel(AttnArgs a) {
   const int split = (int)t - tile * a.nsplit;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
+  const int wq = wave % NWQ;   // the wave's query rows: 16 wq .. 16 wq + 15 of the tile
+  const int grp = wave / NWQ;  // its group: blocks grp, grp + GRP, ...
   const int lane = tid % kWave;
   const int lq = lane % 16;   // query column of this lane
   const int lg = lane / 16;   // lane group (0..3)
@@ -281,7 +293,7 @@ void attn_chunk_kernel(AttnArgs a) {
 
   // This lane's query (column lq of wave's 16 rows), loaded before the
   // plan: its address does not depend on seqlens_k.
-  const int my_qi = q0 + wave * 16 + lq;
+  const int my_qi = q0 + wq * 16 + lq;
   const bool my_ok = my_qi < nq_item;
   const int my_qc = my_ok ? my_qi : nq_item - 1;
   // (divisions by invariants)
@@ -387,9 +399,11 @@ void attn_chunk_kernel(AttnArgs a) {
   // them where they are loaded would make every block wait for all loads in
   // flight.
   constexpr int BW = 8 * e / 4;  // words of the 8 bias entries
+  // (with wave groups each thread scores another block than most it
+  // stages: its bias words are loaded apart, see load_bias)
   struct BlockRegs {
     u32x4 k[CPT], v[CPT];
-    uint32_t bias[BW];
+    uint32_t bias[GRP == 1 ? BW : 1];
   };
   // Per-lane parts of the addresses: chunk u of a block is key kc + j0,
   // 16-byte part pc; blocks made only of cache rows (nearly all) add j0 rows
@@ -445,6 +459,32 @@ void attn_chunk_kernel(AttnArgs a) {
     }
   }
 
+  // The attention_bias entries this lane scores in the block at j0, as raw
+  // words.
+  auto load_bias = [&](int64_t j0, uint32_t* w) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      // the keys of this lane's scores (16-bit: j0 + 8 lg + [0, 8), one
+      // 8-element load; fp32: j0 + 16 kt + 4 lg + [0, 4), one 4-element
+      // load per tile) at element (not vector) alignment -- global memory
+      // takes unaligned vector loads on this target.  The start is clamped
+      // to total - (elements loaded) so the load stays inside the row (a
+      // valid item has total >= T >= S, and the host sends steps here only
+      // when total >= 8); entries of keys past the band's end are masked,
+      // and a group moved back by the clamp is shifted into place when the
+      // block is computed.  One path for every block, so no load waits on
+      // another.
+      if constexpr (DT == kF32) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int64_t g0 = min(j0 + kt * 16, (int64_t)a.total - 4 - 4 * lg);
+          load4_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), w + kt * BW / 2);
+        }
+      } else {
+        const int64_t g0 = min(j0, (int64_t)a.total - 8 - 8 * lg);
+        load8_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), w);
+      }
+    }
+  };
   auto load_block = [&](int64_t j0, BlockRegs& rg) __attribute__((always_inline)) {
     if (j0 + BN <= cache_end) {  // uniform
       const uint64_t boff = (uint64_t)(j0 * kRowB);
@@ -491,28 +531,7 @@ void attn_chunk_kernel(AttnArgs a) {
         }
       }
     }
-    if constexpr (BIAS) {
-      // the keys of this lane's scores (16-bit: j0 + 8 lg + [0, 8), one
-      // 8-element load; fp32: j0 + 16 kt + 4 lg + [0, 4), one 4-element
-      // load per tile) at element (not vector) alignment -- global memory
-      // takes unaligned vector loads on this target.  The start is clamped
-      // to total - (elements loaded) so the load stays inside the row (a
-      // valid item has total >= T >= S, and the host sends steps here only
-      // when total >= 8); entries of keys past the band's end are masked,
-      // and a group moved back by the clamp is shifted into place when the
-      // block is computed.  One path for every block, so no load waits on
-      // another.
-      if constexpr (DT == kF32) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int64_t g0 = min(j0 + kt * 16, (int64_t)a.total - 4 - 4 * lg);
-          load4_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), &rg.bias[kt * BW / 2]);
-        }
-      } else {
-        const int64_t g0 = min(j0, (int64_t)a.total - 8 - 8 * lg);
-        load8_raw_unaligned<DT>(bias_lane + (uint64_t)(g0 * e), rg.bias);
-      }
-    }
+    if constexpr (BIAS && GRP == 1) load_bias(j0, rg.bias);
   };
   auto store_block = [&](const BlockRegs& rg, int buf) __attribute__((always_inline)) {
     LT* const bK = sK + buf * Sh::KELEMS;
@@ -601,7 +620,7 @@ void attn_chunk_kernel(AttnArgs a) {
   int32_t w_vis_lo = INT32_MIN;
   int32_t w_vis_hi = INT32_MAX;
   {
-    const int qw0 = q0 + 16 * __builtin_amdgcn_readfirstlane(wave);
+    const int qw0 = q0 + 16 * __builtin_amdgcn_readfirstlane(wq);
     if (qw0 < nq_item) {
       const int qw1 = min(qw0 + 15, nq_item - 1);
       // largest position: the highest lower bound; smallest: the lowest upper bound
@@ -623,9 +642,9 @@ void attn_chunk_kernel(AttnArgs a) {
   const int32_t nk_band = ke > kb ? (int32_t)(ke - kb) : 0;  // keys of this split
   const float qk_scale = Q8 ? a.scale * a.k_scale : a.scale;
   // One block: scores, online softmax, PV, from the block staged in LDS.
-  auto compute_block = [&](int blk, const float* bias_blk) __attribute__((always_inline)) {
-    const LT* const bK = sK + (DB ? (blk & 1) : 0) * Sh::KELEMS;
-    const LT* const bV = sV + (DB ? (blk & 1) : 0) * Sh::VELEMS;
+  auto compute_block = [&](int blk, int buf, const float* bias_blk) __attribute__((always_inline)) {
+    const LT* const bK = sK + buf * Sh::KELEMS;
+    const LT* const bV = sV + buf * Sh::VELEMS;
     // the block's second score tile (fp32: keys 16 .. 31; 16-bit: keys
     // 8g + 4 .. 8g + 7) holds keys of the band (else its scores are masked
     // and its products are skipped: P = 0 there)
@@ -839,7 +858,7 @@ void attn_chunk_kernel(AttnArgs a) {
     }
   };
   // The attention_bias entries of block blk as floats, from its raw words.
-  auto block_bias = [&](int blk, const BlockRegs& rg, float* bias_blk) __attribute__((always_inline)) {
+  auto block_bias = [&](int blk, const uint32_t* braw, float* bias_blk) __attribute__((always_inline)) {
     if constexpr (BIAS) {
       const int64_t j0 = kb + (int64_t)blk * BN;
       float x[8];  // entry 4 kt + r: the bias of score r of tile kt
@@ -850,7 +869,7 @@ void attn_chunk_kernel(AttnArgs a) {
           // passes the end of the row)
           const int64_t g = j0 + kt * 16 + 4 * lg;
           const int sh = (int)min(g - min(g, (int64_t)a.total - 4), (int64_t)3);
-          const uint32_t* w = &rg.bias[kt * BW / 2];
+          const uint32_t* w = braw + kt * BW / 2;
           // (selects, not an index: a register array indexed at run time
           // would live in scratch memory)
 #pragma unroll
@@ -866,7 +885,7 @@ void attn_chunk_kernel(AttnArgs a) {
         // and masked)
         const int64_t g = j0 + 8 * lg;
         const int sh = (int)min(g - min(g, (int64_t)a.total - 8), (int64_t)7);
-        const uint32_t* w = rg.bias;
+        const uint32_t* w = braw;
         // the 8 entries as one 128-bit value, shifted right by sh entries
         const uint64_t lo = ((uint64_t)w[1] << 32) | w[0];
         const uint64_t hi = ((uint64_t)w[3] << 32) | w[2];
@@ -898,9 +917,9 @@ void attn_chunk_kernel(AttnArgs a) {
   // registers of their occupancy)
   constexpr int RING = (DT == kF32 || D * e >= 512) ? 2 : SWGQA_CHUNK_RING16;
   auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
-    compute_block(blk, bias_cur);
+    compute_block(blk, blk & 1, bias_cur);
     store_block(rg, (blk + 1) & 1);
-    block_bias(blk + 1, rg, bias_cur);  // compute_block(blk) is done with it
+    block_bias(blk + 1, rg.bias, bias_cur);  // compute_block(blk) is done with it
     load_block(block_start(blk + 1 + RING), rg);
     __syncthreads();
   };
@@ -909,14 +928,57 @@ void attn_chunk_kernel(AttnArgs a) {
   auto step1 = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
     __syncthreads();  // the previous block's LDS reads are done
     store_block(rg, 0);
-    block_bias(blk, rg, bias_cur);
+    block_bias(blk, rg.bias, bias_cur);
     __syncthreads();
     if constexpr (kCanMove)
       if (fmove) move_block(blk, rg);
     load_block(block_start(blk + RING), rg);
-    compute_block(blk, bias_cur);
+    compute_block(blk, 0, bias_cur);
   };
-  if constexpr (!DB) {
+  if constexpr (GRP > 1) {
+    // Staging round r: blocks r GRP + g into buffers g (those inside the
+    // split), bias of block r GRP + grp, a barrier, the surviving rows of
+    // the staged blocks moved, their registers reloaded with the blocks of
+    // round r + RG, then each group computes its block.  A barrier opens the
+    // next round once every group is done with the buffers.
+    constexpr int RG = 2;  // rounds of loads in flight
+    const int nrounds = (nblocks + GRP - 1) / GRP;
+    if (nblocks > 0) {
+      BlockRegs rg[RG][GRP];
+      uint32_t brg[RG][BW];
+#pragma unroll
+      for (int i = 0; i < RG; ++i) {
+#pragma unroll
+        for (int g = 0; g < GRP; ++g) load_block(block_start(i * GRP + g), rg[i][g]);
+        load_bias(block_start(i * GRP + grp), brg[i]);
+      }
+      for (int r = 0; r < nrounds;) {
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+          if (r >= nrounds) break;
+          const int b0 = r * GRP;
+          __syncthreads();  // the previous round's LDS reads are done
+#pragma unroll
+          for (int g = 0; g < GRP; ++g)
+            if (b0 + g < nblocks) store_block(rg[i][g], g);
+          block_bias(b0 + grp, brg[i], bias_cur);
+          __syncthreads();
+          if constexpr (kCanMove) {
+            if (fmove) {
+#pragma unroll
+              for (int g = 0; g < GRP; ++g)
+                if (b0 + g < nblocks) move_block(b0 + g, rg[i][g]);
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < GRP; ++g) load_block(block_start(b0 + RG * GRP + g), rg[i][g]);
+          load_bias(block_start(b0 + RG * GRP + grp), brg[i]);
+          if (b0 + grp < nblocks) compute_block(b0 + grp, grp, bias_cur);
+          ++r;
+        }
+      }
+    }
+  } else if constexpr (!DB) {
     if (nblocks > 0) {
       BlockRegs rg[RING];
 #pragma unroll
@@ -935,7 +997,7 @@ void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < RING; ++i) load_block(block_start(i), rg[i]);
     store_block(rg[0], 0);
-    block_bias(0, rg[0], bias_cur);
+    block_bias(0, rg[0].bias, bias_cur);
     load_block(block_start(RING), rg[0]);
     __syncthreads();
     for (int blk = 0; blk < nblocks;) {
@@ -948,10 +1010,51 @@ void attn_chunk_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (GRP > 1) {
+    // Groups 1 .. GRP - 1 hand their softmax states (per lane: O^T column
+    // parts, running maximum, partial sum) to group 0 through LDS; group 0
+    // merges them with its own, as the split merge does.
+    constexpr int SLOT = 4 * DT16 + 2;  // floats per lane
+    __shared__ float sG[GRP > 1 ? (GRP - 1) * NWQ * SLOT * kWave : 1];
+    auto at = [&](int g1, int f) { return ((g1 * NWQ + wq) * SLOT + f) * kWave + lane; };
+    if (grp > 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sG[at(grp - 1, 4 * dt + r)] = o[dt][r];
+      sG[at(grp - 1, 4 * DT16)] = m_run;
+      sG[at(grp - 1, 4 * DT16 + 1)] = l_run;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      float mg[GRP - 1 > 0 ? GRP - 1 : 1];
+      float M = m_run;
+#pragma unroll
+      for (int g1 = 0; g1 < GRP - 1; ++g1) {
+        mg[g1] = sG[at(g1, 4 * DT16)];
+        M = fmaxf(M, mg[g1]);
+      }
+      const float c0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+      l_run *= c0;
+#pragma unroll
+      for (int dt = 0; dt < DT16; ++dt) o[dt] *= c0;
+#pragma unroll
+      for (int g1 = 0; g1 < GRP - 1; ++g1) {
+        const float c = mg[g1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mg[g1] - M);
+        l_run += sG[at(g1, 4 * DT16 + 1)] * c;
+#pragma unroll
+        for (int dt = 0; dt < DT16; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[dt][r] += sG[at(g1, 4 * dt + r)] * c;
+      }
+      m_run = M;
+    }
+  }
+
   // Sum of P over the four lane groups; write O (or the split partial).
   l_run = reduce_xor16(l_run, add_f);
   l_run = reduce_xor32(l_run, add_f);
-  if (my_ok) {
+  if (my_ok && (GRP == 1 || grp == 0)) {
     const int64_t row = ((int64_t)b * a.S + my_i) * a.Hq + my_h;
     if (a.nsplit == 1) {
       float m_fin = m_run;
@@ -1024,9 +1127,23 @@ void attn_chunk_kernel(AttnArgs a) {
   slice_tail_rows<8>(a, pl, b, kvh, D, CE, nullptr, nullptr);
 }
 
+// Wave groups: 16-bit element-type caches with rows of at most 256 bytes.
+template <int DT, int D, int CT>
+constexpr bool chunk_groups_ok() { return DT != kF32 && CT == 0 && D * 2 <= 256 && !chunk_double_buffer<DT>(); }
+
 template <int DT, int D, int NW, int CT>
 hipError_t launch_w(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.ntiles * a.nsplit, a.Hkv, a.B);
+  if constexpr (NW == 8 && chunk_groups_ok<DT, D, CT>()) {
+    if (a.chunk_groups == 4) {
+      if (a.bias)
+        attn_chunk_kernel<DT, D, true, 8, CT, 4><<<grid, 8 * kWave, 0, st>>>(a);
+      else
+        attn_chunk_kernel<DT, D, false, 8, CT, 4><<<grid, 8 * kWave, 0, st>>>(a);
+      return hipGetLastError();
+    }
+  }
+  if (a.chunk_groups > 1) return hipErrorInvalidValue;
   if (a.bias)
     attn_chunk_kernel<DT, D, true, NW, CT><<<grid, NW * kWave, 0, st>>>(a);
   else

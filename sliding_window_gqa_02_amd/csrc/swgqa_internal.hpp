@@ -45,6 +45,7 @@ struct AttnArgs {
   int32_t smooth;
   int32_t fuse_writeback;  // shared buffer, one key split: write-back in the kernel
   int32_t waves;           // waves per workgroup of the staged kernel
+  int32_t chunk_groups;    // chunk kernel: groups of waves that share a tile's rows (1 or 4)
   // staged decode kernel, 8 waves, one workgroup per slice: the variant that
   // moves a compacting slice's surviving rows as it reads them
   int32_t fused_move;
@@ -116,7 +117,7 @@ hipError_t launch_attn_split(int dtype, int D, int nq, const AttnArgs& a,
 // MFMA kernel for multi-token steps (swgqa_attn_chunk.hip): 16 query rows
 // per wave, 4 or 8 waves per workgroup, keys in blocks of 32.
 bool chunk_kernel_supports(int dtype, int D);
-int chunk_rows_per_workgroup(int waves);  // 4 or 8 waves
+int chunk_rows_per_workgroup(int waves, int groups);  // 4 or 8 waves, 1 or 4 groups
 int chunk_keys_per_block();
 // Whether the kernel (cache in the element type) honours AttnArgs::stash.
 bool chunk_kernel_moves_rows(int dtype);
