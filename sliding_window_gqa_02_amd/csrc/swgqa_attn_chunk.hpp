@@ -904,7 +904,8 @@ void attn_chunk_kernel(AttnArgs a) {
   };
   // A block's K/V/bias loads are issued three steps before it is staged
   // (register ring of three), so two blocks of loads stay in flight while
-  // one is computed; blocks past the band's end reload its last block.  Step
+  // one is computed; no loads are issued for blocks past the split's end
+  // (they only took load-unit cycles from the blocks still wanted).  Step
   // blk computes block blk from LDS buffer blk & 1, then stages block blk + 1
   // (in the ring since step blk - 3) into the other buffer -- whose block,
   // blk - 1, every wave finished before the barrier that ended step blk - 1
@@ -920,7 +921,7 @@ void attn_chunk_kernel(AttnArgs a) {
     compute_block(blk, blk & 1, bias_cur);
     store_block(rg, (blk + 1) & 1);
     block_bias(blk + 1, rg.bias, bias_cur);  // compute_block(blk) is done with it
-    load_block(block_start(blk + 1 + RING), rg);
+    if (blk + 1 + RING < nblocks) load_block(block_start(blk + 1 + RING), rg);
     __syncthreads();
   };
   // single buffer: barrier, stage block blk, barrier, reload its registers
@@ -932,7 +933,7 @@ void attn_chunk_kernel(AttnArgs a) {
     __syncthreads();
     if constexpr (kCanMove)
       if (fmove) move_block(blk, rg);
-    load_block(block_start(blk + RING), rg);
+    if (blk + RING < nblocks) load_block(block_start(blk + RING), rg);
     compute_block(blk, 0, bias_cur);
   };
   if constexpr (GRP > 1) {
@@ -949,8 +950,9 @@ void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < RG; ++i) {
 #pragma unroll
-        for (int g = 0; g < GRP; ++g) load_block(block_start(i * GRP + g), rg[i][g]);
-        load_bias(block_start(i * GRP + grp), brg[i]);
+        for (int g = 0; g < GRP; ++g)
+          if (i * GRP + g < nblocks) load_block(block_start(i * GRP + g), rg[i][g]);
+        if (i * GRP + grp < nblocks) load_bias(block_start(i * GRP + grp), brg[i]);
       }
       for (int r = 0; r < nrounds;) {
 #pragma unroll
@@ -961,7 +963,7 @@ void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
           for (int g = 0; g < GRP; ++g)
             if (b0 + g < nblocks) store_block(rg[i][g], g);
-          block_bias(b0 + grp, brg[i], bias_cur);
+          if (b0 + grp < nblocks) block_bias(b0 + grp, brg[i], bias_cur);
           __syncthreads();
           if constexpr (kCanMove) {
             if (fmove) {
@@ -971,8 +973,9 @@ void attn_chunk_kernel(AttnArgs a) {
             }
           }
 #pragma unroll
-          for (int g = 0; g < GRP; ++g) load_block(block_start(b0 + RG * GRP + g), rg[i][g]);
-          load_bias(block_start(b0 + RG * GRP + grp), brg[i]);
+          for (int g = 0; g < GRP; ++g)
+            if (b0 + RG * GRP + g < nblocks) load_block(block_start(b0 + RG * GRP + g), rg[i][g]);
+          if (b0 + RG * GRP + grp < nblocks) load_bias(block_start(b0 + RG * GRP + grp), brg[i]);
           if (b0 + grp < nblocks) compute_block(b0 + grp, grp, bias_cur);
           ++r;
         }
@@ -982,7 +985,8 @@ void attn_chunk_kernel(AttnArgs a) {
     if (nblocks > 0) {
       BlockRegs rg[RING];
 #pragma unroll
-      for (int i = 0; i < RING; ++i) load_block(block_start(i), rg[i]);
+      for (int i = 0; i < RING; ++i)
+        if (i < nblocks) load_block(block_start(i), rg[i]);
       for (int blk = 0; blk < nblocks;) {
 #pragma unroll
         for (int i = 0; i < RING; ++i) {
@@ -995,10 +999,11 @@ void attn_chunk_kernel(AttnArgs a) {
   } else if (nblocks > 0) {
     BlockRegs rg[RING];
 #pragma unroll
-    for (int i = 0; i < RING; ++i) load_block(block_start(i), rg[i]);
+    for (int i = 0; i < RING; ++i)
+      if (i < nblocks) load_block(block_start(i), rg[i]);
     store_block(rg[0], 0);
     block_bias(0, rg[0].bias, bias_cur);
-    load_block(block_start(RING), rg[0]);
+    if (RING < nblocks) load_block(block_start(RING), rg[0]);
     __syncthreads();
     for (int blk = 0; blk < nblocks;) {
 #pragma unroll
