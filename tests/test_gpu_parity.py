@@ -456,6 +456,44 @@ def test_chunked_steps_ragged_bias(cfg, mode):
     say(f"  worst scaled error {run.worst:.3g}")
 
 
+# Wave groups of the chunk kernel (tiles of at most 32 query rows, 16-bit):
+# 256 slices, so one key split per slice and up to 10 blocks per split --
+# several staging rounds, the last with groups that have no block.  With 4
+# query heads per KV head, S = 8 takes the groups, S = 16 the 64-row tiles
+# and S = 4 the staged decode kernel; with one, S = 16 / 24 / 32 give tiles
+# of 16 / 24 / 32 rows (group waves without rows, or with some).
+GROUPS = [
+    (Cfg(B=16, Hq=64, Hkv=16, D=64, C=320, W=300, seed=36, dtype=synth.F16),
+     [(8, True), (8, False), (4, True), (16, False), (8, True), (4, False), (8, False), (8, True)]),
+    (Cfg(B=16, Hq=64, Hkv=16, D=128, C=310, W=290, seed=37, dtype=synth.BF16, softcap=25.0),
+     [(8, True), (16, False), (8, False), (8, True), (4, False), (8, True)]),
+    (Cfg(B=16, Hq=16, Hkv=16, D=64, C=300, W=280, seed=38, dtype=synth.F16),
+     [(16, True), (24, False), (32, True), (16, False), (24, True)]),
+]
+
+
+@pytest.mark.parametrize("mode", ["shared", "separate"])
+@pytest.mark.parametrize("cfg,steps", GROUPS,
+                         ids=lambda c: f"D{c.D}g{c.Hq // c.Hkv}t{c.dtype}" if isinstance(c, Cfg) else "")
+def test_chunk_wave_groups_many_rounds(cfg, steps, mode):
+    say(f"wave groups {cfg} mode={mode}")
+    syn = cfg.synth()
+    vers = Versions(cfg.B)
+    P0 = np.array([cfg.W - 40 + 7 * b for b in range(cfg.B)], dtype=np.int64)
+    K, V = seeded_cache(cfg, syn, P0, vers)
+    run = Lockstep(cfg, mode=mode, K=K, V=V, vers=vers)
+    P = P0.copy()
+    events = 0
+    for S, with_bias in steps:
+        total = int((P + S).max())
+        bias = _bias_nan_outside(cfg, syn, P, S, total) if with_bias else None
+        _, _, plan = run.step(P, S, bias=bias, total=total)
+        events += int((plan[:, 5] > 0).sum())
+        P = P + S
+    say(f"  {events} compaction events, worst scaled error {run.worst:.3g}")
+    assert events > 0
+
+
 def test_bias_rows_shorter_than_a_load_group():
     """Bias rows of 2, 9 and 13 entries: the chunk kernel reads bias in groups
     of 8 entries clamped to the row's end (shifted back when computed: by 7
