@@ -11,8 +11,9 @@
 // from the new rows, so a step that evicts history it still reads needs no
 // staging copy ("[CPU] Add windowed kv cache for GQA", staging).
 //
-// A workgroup (4 waves) owns 64 consecutive (position, head) query rows of
-// one KV head's group and walks the key band [p_first - W + 1, p_last] in
+// A workgroup (4 or 8 waves, 16 query rows each; or 8 waves in 4 groups of
+// 2 that share 32 rows, see GRP) owns consecutive (position, head) query rows
+// of one KV head's group and walks the key band [p_first - W + 1, p_last] in
 // blocks of 32 keys staged in LDS -- every K/V row staged is used by all the
 // heads of the group.  Per block each wave (16 query rows):
 //   S^T = K . Q^T   16 keys x 16 queries per MFMA (Q^T is the B operand, held
@@ -54,7 +55,8 @@ namespace swgqa {
 
 namespace {
 
-// A workgroup of NW waves (4 or 8) owns 16 NW query rows.
+// A workgroup of NW waves (4 or 8) owns 16 NW query rows (16 NW / GRP with
+// wave groups).
 constexpr int BN = 32;   // keys per block
 constexpr float kLog2e = 1.4426950408889634f;
 
