@@ -222,6 +222,16 @@ constexpr bool chunk_split_moves() { return !chunk_double_buffer<DT>() && CT == 
 // waves) and 3 otherwise (the bias path and 4-wave workgroups need a little
 // more); 16-bit rows of at most 128 bytes in 8-wave workgroups without bias,
 // 4 (two workgroups per CU); no floor for the other shapes.
+// Blocks of loads in flight in the register ring: three (16-bit rows under
+// 512 bytes, tunable; fp32 rows of at most 256 bytes, except 4-wave
+// workgroups with bias, which would spill), else two, which keeps the rest
+// within the registers of their occupancy.
+template <int DT, int D, int NW, bool BIAS>
+constexpr int chunk_ring() {
+  if constexpr (DT == kF32) return D <= 64 && !(BIAS && NW == 4) ? 3 : 2;
+  else return D * 2 >= 512 ? 2 : SWGQA_CHUNK_RING16;
+}
+
 template <int DT, int D, int NW, bool BIAS, int GRP = 1>
 constexpr int chunk_min_waves() {
   if constexpr (GRP > 1) return 1;  // (its register ring is GRP blocks deep per round)
@@ -916,9 +926,7 @@ void attn_chunk_kernel(AttnArgs a) {
   // barrier per block.
   auto block_start = [&](int blk) { return kb + (int64_t)min(blk, nblocks - 1) * BN; };
   float bias_cur[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  // (fp32, and 16-bit rows of 512 bytes: two, which keeps them within the
-  // registers of their occupancy)
-  constexpr int RING = (DT == kF32 || D * e >= 512) ? 2 : SWGQA_CHUNK_RING16;
+  constexpr int RING = chunk_ring<DT, D, NW, BIAS>();
   auto step = [&](int blk, BlockRegs& rg) __attribute__((always_inline)) {
     compute_block(blk, blk & 1, bias_cur);
     store_block(rg, (blk + 1) & 1);
