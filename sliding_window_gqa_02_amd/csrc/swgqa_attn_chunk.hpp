@@ -1029,25 +1029,24 @@ void attn_chunk_kernel(AttnArgs a) {
     // Groups 1 .. GRP - 1 hand their softmax states (per lane: O^T column
     // parts, running maximum, partial sum) to group 0 through LDS; group 0
     // merges them with its own, as the split merge does.
-    constexpr int SLOT = 4 * DT16 + 2;  // floats per lane
-    __shared__ float sG[GRP > 1 ? (GRP - 1) * NWQ * SLOT * kWave : 1];
-    auto at = [&](int g1, int f) { return ((g1 * NWQ + wq) * SLOT + f) * kWave + lane; };
+    // (16-byte slots per lane: the DT16 O^T words, then max and sum; slot k
+    // of every lane of a wave is one contiguous 1 KiB row)
+    constexpr int NS = DT16 + 1;
+    __shared__ f4 sG[GRP > 1 ? (GRP - 1) * NWQ * NS * kWave : 1];
+    auto at = [&](int g1, int k) { return ((g1 * NWQ + wq) * NS + k) * kWave + lane; };
     if (grp > 0) {
 #pragma unroll
-      for (int dt = 0; dt < DT16; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sG[at(grp - 1, 4 * dt + r)] = o[dt][r];
-      sG[at(grp - 1, 4 * DT16)] = m_run;
-      sG[at(grp - 1, 4 * DT16 + 1)] = l_run;
+      for (int dt = 0; dt < DT16; ++dt) sG[at(grp - 1, dt)] = o[dt];
+      sG[at(grp - 1, DT16)] = f4{m_run, l_run, 0.0f, 0.0f};
     }
     __syncthreads();
     if (grp == 0) {
-      float mg[GRP - 1 > 0 ? GRP - 1 : 1];
+      f4 ml[GRP - 1 > 0 ? GRP - 1 : 1];
       float M = m_run;
 #pragma unroll
       for (int g1 = 0; g1 < GRP - 1; ++g1) {
-        mg[g1] = sG[at(g1, 4 * DT16)];
-        M = fmaxf(M, mg[g1]);
+        ml[g1] = sG[at(g1, DT16)];
+        M = fmaxf(M, ml[g1][0]);
       }
       const float c0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
       l_run *= c0;
@@ -1055,12 +1054,10 @@ void attn_chunk_kernel(AttnArgs a) {
       for (int dt = 0; dt < DT16; ++dt) o[dt] *= c0;
 #pragma unroll
       for (int g1 = 0; g1 < GRP - 1; ++g1) {
-        const float c = mg[g1] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mg[g1] - M);
-        l_run += sG[at(g1, 4 * DT16 + 1)] * c;
+        const float c = ml[g1][0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[g1][0] - M);
+        l_run += ml[g1][1] * c;
 #pragma unroll
-        for (int dt = 0; dt < DT16; ++dt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[dt][r] += sG[at(g1, 4 * dt + r)] * c;
+        for (int dt = 0; dt < DT16; ++dt) o[dt] += sG[at(g1, dt)] * c;
       }
       m_run = M;
     }
